@@ -1,0 +1,160 @@
+/*
+ * smx.h — C ABI of the MI355X (gfx950) row-softmax library.
+ *
+ * Batched row-wise stable softmax computed by online normalization:
+ *   p_j = exp(x_j - m) / l,  m = max_j x_j,  l = sum_j exp(x_j - m)
+ * over the valid lanes of each row of a row-major [rows, cols] tensor.
+ *
+ * Sources (web pages; section names as on the pages):
+ *  - "Softmax numerics architecture", section "The max-subtraction identity,
+ *    and why it is exact": shifting by the row maximum keeps every
+ *    exponential in (0, 1] and the sum in [1, N].
+ *  - Same page, section "Why the accumulator is fp32 even when the inputs are
+ *    not": bf16/fp16 inputs keep an fp32 running max and accumulator.
+ *  - "Online stable softmax", sections "Derive the update for two blocks" and
+ *    "Reference summary": a block is summarized by (m, l); two summaries
+ *    merge as m' = max(m, m2), l' = exp(m - m') l + exp(m2 - m') l2.
+ *  - "Stable softmax: keep the normalizer consistent as tiles arrive", the
+ *    paragraphs on masks and on fused rows: the mask contract, and a row is
+ *    read once when it fits on chip, otherwise with a counted reread.
+ *
+ * Contract for every call
+ *  - All pointers except `mask` and the mask descriptor itself are DEVICE
+ *    pointers on the current HIP device, allocated and owned by the caller.
+ *    The mask descriptor struct is read on the host during the call.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL means
+ *    the default stream). Results are valid once the stream has synchronized.
+ *    The library never synchronizes the host and keeps no device memory
+ *    between calls.
+ *  - Return value: SMX_OK (0) or an SMX_E* code; smx_last_error() then
+ *    returns a message (thread-local, valid until the next call on the same
+ *    thread). Invalid arguments are rejected before anything is enqueued.
+ *  - rows == 0 or cols == 0 is a successful no-op.
+ *  - x == y (exact aliasing) is allowed; partial overlap is SMX_EINVAL.
+ *  - Any pointer alignment is accepted; 16-byte aligned x and y with
+ *    cols * element_size a multiple of 16 take the 128-bit vector path.
+ *  - Results are deterministic: the same inputs give bitwise the same output.
+ *
+ * Data policy (values are never errors)
+ *  - Masked lanes contribute nothing and are written as +0.0. A valid lane
+ *    holding -inf behaves like a masked lane.
+ *  - A row with no valid finite lane (cols == 0, valid length 0, every lane
+ *    masked, or every valid lane -inf) is written as all +0.0; no
+ *    -inf - (-inf) is ever formed.
+ *  - A row with +inf or NaN (any sign, quiet or signalling) in a VALID lane is
+ *    written as the canonical quiet NaN in every lane: f32 0x7FC00000,
+ *    f16 0x7E00, bf16 0x7FC0. +inf or NaN in a masked lane is ignored.
+ *  - Accumulation is fp32 for every element type; outputs are rounded to
+ *    nearest-even with gradual underflow (subnormals are kept).
+ */
+#ifndef SMX_H
+#define SMX_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define SMX_OK 0
+#define SMX_EINVAL 1 /* a bad argument; nothing was enqueued            */
+#define SMX_EHIP 2   /* the HIP runtime reported an error               */
+
+/* Element type of x and y (they share one); accumulation is always fp32. */
+typedef enum { SMX_F32 = 0, SMX_F16 = 1, SMX_BF16 = 2 } smx_dtype;
+
+/* Mask kinds. Lane j of row r is valid when:
+ *   SMX_MASK_NONE      : always;
+ *   SMX_MASK_VALID_LEN : j < clamp(valid_len[r], 0, cols);
+ *   SMX_MASK_CAUSAL    : j < clamp((r mod causal_period) + 1 + causal_offset,
+ *                                  0, cols)  (row i of each period keeps
+ *                                  columns 0..i+causal_offset);
+ *   SMX_MASK_KEEP_BYTES: keep[r * cols + j] != 0.
+ * An out-of-range valid length is clamped, not an error. */
+typedef enum {
+  SMX_MASK_NONE = 0,
+  SMX_MASK_VALID_LEN = 1,
+  SMX_MASK_CAUSAL = 2,
+  SMX_MASK_KEEP_BYTES = 3
+} smx_mask_kind;
+
+typedef struct {
+  smx_mask_kind kind;
+  const int32_t* valid_len; /* VALID_LEN: device [rows]                      */
+  int64_t causal_period;    /* CAUSAL: > 0                                   */
+  int64_t causal_offset;    /* CAUSAL: any value                             */
+  const uint8_t* keep;      /* KEEP_BYTES: device [rows, cols], row-major    */
+} smx_mask;                 /* a NULL descriptor pointer means SMX_MASK_NONE */
+
+/* A chunk summary: m is the chunk's maximum over valid finite lanes and
+ * l = sum exp(x_j - m) over them (l in [1, lanes]). An empty chunk is
+ * (-inf, 0); a chunk holding +inf or NaN in a valid lane is (NaN, NaN). */
+typedef struct {
+  float m;
+  float l;
+} smx_stat;
+
+/* Kernel paths. */
+typedef enum {
+  SMX_PATH_AUTO = 0,  /* chosen from the row size and the row count        */
+  SMX_PATH_WAVE = 1,  /* one wave64 per row, the row held in registers     */
+  SMX_PATH_LDS = 2,   /* one workgroup per row, the row staged in LDS      */
+  SMX_PATH_SPLIT = 3  /* chunk summaries, then merge + normalize (2 reads) */
+} smx_path;
+
+/* softmax_rows — y[r, :] = softmax of the valid lanes of x[r, :].
+ *   x, y  : device [rows, cols] row-major, element type dtype.
+ *   valid_len_or_mask : host pointer to a mask descriptor, or NULL.
+ *   stream: hipStream_t.
+ * Long rows go through the split path, which takes its summary workspace
+ * (rows * ceil(cols / chunk) * 8 bytes) with a stream-ordered allocation and
+ * frees it on the same stream. */
+int softmax_rows(const void* x, void* y, int64_t rows, int64_t cols,
+                 smx_dtype dtype, const smx_mask* valid_len_or_mask,
+                 void* stream);
+
+/* softmax_rows_path — softmax_rows with the kernel path forced (AUTO picks
+ * as softmax_rows does). chunk_cols applies to SMX_PATH_SPLIT (0 = the
+ * default). A path that cannot hold the row (WAVE above its register budget,
+ * LDS above its LDS budget) is SMX_EINVAL. */
+int softmax_rows_path(const void* x, void* y, int64_t rows, int64_t cols,
+                      smx_dtype dtype, const smx_mask* valid_len_or_mask,
+                      smx_path path, int64_t chunk_cols, void* stream);
+
+/* The path softmax_rows takes for a shape (no device access). */
+smx_path softmax_select_path(int64_t rows, int64_t cols, smx_dtype dtype);
+
+/* softmax_row_stats — per-chunk summaries ("Stable softmax: keep the
+ * normalizer consistent as tiles arrive", block-merge paragraph).
+ *   chunk_cols: > 0; chunk c covers columns [c*chunk_cols,
+ *               min((c+1)*chunk_cols, cols)).
+ *   stats: device [rows][n_chunks], n_chunks = ceil(cols / chunk_cols). */
+int softmax_row_stats(const void* x, int64_t rows, int64_t cols,
+                      smx_dtype dtype, const smx_mask* valid_len_or_mask,
+                      int64_t chunk_cols, smx_stat* stats, void* stream);
+
+/* softmax_merge_normalize — merges each row's n_chunks summaries with the
+ * (m, l) rule ("Online stable softmax", "Reference summary"; the side holding
+ * the maximum keeps factor 1, so (-inf, 0) is an exact identity), then
+ * rereads x and writes y = exp(x - M) / L over valid finite lanes.
+ * Any (NaN, NaN) summary makes a NaN row; all-empty summaries a zero row.
+ *   stats: device [rows][n_chunks], as written by softmax_row_stats or by the
+ *          caller (e.g. summaries exchanged between devices);
+ *   n_chunks must equal ceil(cols / chunk_cols). */
+int softmax_merge_normalize(const void* x, void* y, int64_t rows, int64_t cols,
+                            smx_dtype dtype, const smx_mask* valid_len_or_mask,
+                            int64_t chunk_cols, const smx_stat* stats,
+                            int64_t n_chunks, void* stream);
+
+/* The chunk width softmax_rows uses on the split path (a tuning hint). */
+int64_t softmax_default_chunk_cols(int64_t rows, int64_t cols,
+                                   smx_dtype dtype);
+
+/* Message for the last nonzero status on this thread ("" if none). */
+const char* smx_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SMX_H */

@@ -1,0 +1,203 @@
+"""Python binding of the gfx950 row-softmax library (libsmx.so).
+
+Argument marshalling only: every function passes device pointers, sizes and
+the current HIP stream to the C ABI declared in include/smx.h, and every step
+of the computation runs in the library's HIP kernels. PyTorch supplies device
+memory and streams. There is no CPU fallback: if the library is not built,
+importing this package raises.
+
+Functions keep the C names:
+  softmax_rows(x, ...)              -> y
+  softmax_row_stats(x, chunk_cols)  -> stats [rows, n_chunks, 2] (m, l)
+  softmax_merge_normalize(x, stats, chunk_cols) -> y
+  softmax_default_chunk_cols(rows, cols, dtype)
+  softmax_select_path(rows, cols, dtype)
+  smx_last_error()
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional
+
+import torch  # loads the HIP runtime this library then shares
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsmx.so")
+
+SMX_OK, SMX_EINVAL, SMX_EHIP = 0, 1, 2
+DTYPE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+DTYPE_NAME = {"f32": 0, "f16": 1, "bf16": 2}
+MASK = {"none": 0, "valid_len": 1, "causal": 2, "keep": 3}
+PATH = {"auto": 0, "wave": 1, "lds": 2, "split": 3}
+PATH_NAME = {v: k for k, v in PATH.items()}
+
+
+class SmxMask(C.Structure):
+    _fields_ = [
+        ("kind", C.c_int),
+        ("valid_len", C.c_void_p),
+        ("causal_period", C.c_int64),
+        ("causal_offset", C.c_int64),
+        ("keep", C.c_void_p),
+    ]
+
+
+class SmxError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"smx error {code}: {msg}")
+        self.code = code
+
+
+_lib = None
+
+
+def lib() -> C.CDLL:
+    """The loaded C library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is missing: build it with numerically_stable_online_amd/build.py "
+                "(or __graft_entry__.build()); there is no fallback implementation")
+        L = C.CDLL(LIB_PATH)
+        vp, i64, i32 = C.c_void_p, C.c_int64, C.c_int
+        mp = C.POINTER(SmxMask)
+        L.softmax_rows.argtypes = [vp, vp, i64, i64, i32, mp, vp]
+        L.softmax_rows.restype = i32
+        L.softmax_rows_path.argtypes = [vp, vp, i64, i64, i32, mp, i32, i64, vp]
+        L.softmax_rows_path.restype = i32
+        L.softmax_select_path.argtypes = [i64, i64, i32]
+        L.softmax_select_path.restype = i32
+        L.softmax_row_stats.argtypes = [vp, i64, i64, i32, mp, i64, vp, vp]
+        L.softmax_row_stats.restype = i32
+        L.softmax_merge_normalize.argtypes = [vp, vp, i64, i64, i32, mp, i64, vp, i64, vp]
+        L.softmax_merge_normalize.restype = i32
+        L.softmax_default_chunk_cols.argtypes = [i64, i64, i32]
+        L.softmax_default_chunk_cols.restype = i64
+        L.smx_last_error.argtypes = []
+        L.smx_last_error.restype = C.c_char_p
+        _lib = L
+    return _lib
+
+
+def smx_last_error() -> str:
+    return lib().smx_last_error().decode()
+
+
+def _check(rc: int) -> None:
+    if rc != SMX_OK:
+        raise SmxError(rc, smx_last_error())
+
+
+def _stream_handle(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    try:
+        return DTYPE[t.dtype]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {t.dtype}; use float32, float16 or bfloat16") from None
+
+
+def _rows_cols(x: torch.Tensor):
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [rows, cols]")
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous (row-major)")
+    if x.device.type != "cuda":
+        raise ValueError("x must be a device tensor")
+    return x.shape[0], x.shape[1]
+
+
+def make_mask(rows: int, cols: int, valid_len: Optional[torch.Tensor] = None,
+              causal_period: Optional[int] = None, causal_offset: int = 0,
+              keep: Optional[torch.Tensor] = None):
+    """Build the C mask descriptor; returns (struct or None, tensors to keep alive)."""
+    given = sum(v is not None for v in (valid_len, causal_period, keep))
+    if given > 1:
+        raise ValueError("give at most one of valid_len, causal_period, keep")
+    if given == 0:
+        return None, ()
+    m = SmxMask()
+    if valid_len is not None:
+        if valid_len.dtype != torch.int32 or valid_len.shape != (rows,) or not valid_len.is_contiguous():
+            raise ValueError("valid_len must be a contiguous int32 device tensor of shape [rows]")
+        m.kind = MASK["valid_len"]
+        m.valid_len = valid_len.data_ptr()
+        return m, (valid_len,)
+    if causal_period is not None:
+        m.kind = MASK["causal"]
+        m.causal_period = int(causal_period)
+        m.causal_offset = int(causal_offset)
+        return m, ()
+    if keep.dtype not in (torch.uint8, torch.bool) or keep.shape != (rows, cols) or not keep.is_contiguous():
+        raise ValueError("keep must be a contiguous uint8/bool device tensor of shape [rows, cols]")
+    m.kind = MASK["keep"]
+    m.keep = keep.data_ptr()
+    return m, (keep,)
+
+
+def _mask_arg(m):
+    return None if m is None else C.byref(m)
+
+
+def softmax_rows(x: torch.Tensor, out: Optional[torch.Tensor] = None, *, valid_len=None,
+                 causal_period=None, causal_offset: int = 0, keep=None, path: str = "auto",
+                 chunk_cols: int = 0, stream=None) -> torch.Tensor:
+    """Row-wise stable softmax of x [rows, cols] (float32, float16 or bfloat16)."""
+    rows, cols = _rows_cols(x)
+    y = torch.empty_like(x) if out is None else out
+    if y.shape != x.shape or y.dtype != x.dtype or not y.is_contiguous():
+        raise ValueError("out must be a contiguous tensor of x's shape and dtype")
+    m, keepalive = make_mask(rows, cols, valid_len, causal_period, causal_offset, keep)
+    rc = lib().softmax_rows_path(x.data_ptr(), y.data_ptr(), rows, cols, _dtype_code(x), _mask_arg(m),
+                                 PATH[path], int(chunk_cols), _stream_handle(stream))
+    _check(rc)
+    return y
+
+
+def softmax_row_stats(x: torch.Tensor, chunk_cols: int, out: Optional[torch.Tensor] = None, *,
+                      valid_len=None, causal_period=None, causal_offset: int = 0, keep=None,
+                      stream=None) -> torch.Tensor:
+    """Per-chunk (m, l) summaries, float32 [rows, n_chunks, 2]."""
+    rows, cols = _rows_cols(x)
+    nch = -(-cols // chunk_cols) if chunk_cols > 0 else 0
+    st = torch.empty((rows, nch, 2), dtype=torch.float32, device=x.device) if out is None else out
+    if st.shape != (rows, nch, 2) or st.dtype != torch.float32 or not st.is_contiguous():
+        raise ValueError("out must be a contiguous float32 tensor [rows, n_chunks, 2]")
+    m, keepalive = make_mask(rows, cols, valid_len, causal_period, causal_offset, keep)
+    rc = lib().softmax_row_stats(x.data_ptr(), rows, cols, _dtype_code(x), _mask_arg(m), int(chunk_cols),
+                                 st.data_ptr(), _stream_handle(stream))
+    _check(rc)
+    return st
+
+
+def softmax_merge_normalize(x: torch.Tensor, stats: torch.Tensor, chunk_cols: int,
+                            out: Optional[torch.Tensor] = None, *, valid_len=None, causal_period=None,
+                            causal_offset: int = 0, keep=None, stream=None) -> torch.Tensor:
+    """Merge each row's chunk summaries and write exp(x - M) / L."""
+    rows, cols = _rows_cols(x)
+    if stats.dim() != 3 or stats.shape[0] != rows or stats.shape[2] != 2 or stats.dtype != torch.float32 \
+            or not stats.is_contiguous():
+        raise ValueError("stats must be a contiguous float32 tensor [rows, n_chunks, 2]")
+    y = torch.empty_like(x) if out is None else out
+    m, keepalive = make_mask(rows, cols, valid_len, causal_period, causal_offset, keep)
+    rc = lib().softmax_merge_normalize(x.data_ptr(), y.data_ptr(), rows, cols, _dtype_code(x), _mask_arg(m),
+                                       int(chunk_cols), stats.data_ptr(), stats.shape[1],
+                                       _stream_handle(stream))
+    _check(rc)
+    return y
+
+
+def softmax_default_chunk_cols(rows: int, cols: int, dtype) -> int:
+    code = DTYPE[dtype] if isinstance(dtype, torch.dtype) else DTYPE_NAME[dtype]
+    return int(lib().softmax_default_chunk_cols(rows, cols, code))
+
+
+def softmax_select_path(rows: int, cols: int, dtype) -> str:
+    code = DTYPE[dtype] if isinstance(dtype, torch.dtype) else DTYPE_NAME[dtype]
+    return PATH_NAME[int(lib().softmax_select_path(rows, cols, code))]

@@ -1,0 +1,174 @@
+// k_lds.hip — one workgroup per row, the row staged in LDS.
+//
+// The row's valid prefix is copied from HBM straight into LDS with gfx950's
+// direct global->LDS 128-bit loads (global_load_lds_dwordx4): the copy needs
+// no VGPRs, so a workgroup can have the whole row in flight at once. The row
+// is read from HBM exactly once ("Stable softmax: keep the normalizer
+// consistent as tiles arrive", paragraph on fused rows); every thread then
+// takes its packs out of LDS into registers, and the max, the sum of
+// shifted exponentials and the normalized stores follow as in the wave
+// kernel, with workgroup-wide reductions.
+#include "smx_device.hpp"
+
+namespace smx {
+namespace {
+
+constexpr int kPiece = 64 * 16;  // bytes one wave's direct load moves
+
+template <int DT, int VPT, bool KEEP>
+__global__ __launch_bounds__(kThreads) void k_lds(RowArgs a) {
+  constexpr int S = Fmt<DT>::S;
+  constexpr int E = 16 / S;
+  constexpr bool ACC = DT == kF32;
+  extern __shared__ __attribute__((aligned(1024))) char row_lds[];
+  __shared__ RedScratch red;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t cols = a.cols;
+
+  for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
+    const int64_t prefix = valid_prefix(a.mask, row, cols);
+    const char* xr = a.x + row * cols * S;
+    char* yr = a.y + row * cols * S;
+
+    // stage the valid prefix: wave w copies pieces w, w + 4, ...
+    const int64_t nvec = (prefix + E - 1) / E;
+    const int64_t npieces = (nvec + 63) / 64;
+    for (int64_t pc = wid; pc < npieces; pc += kWaves) {
+      const int64_t vi = pc * 64 + lane;
+      const int64_t vsrc = vi < nvec ? vi : nvec - 1;  // stays inside the row
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(xr + vsrc * 16),
+          (__attribute__((address_space(3))) void*)(row_lds + pc * kPiece), 16, 0, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    float v[VPT][E];
+    float mx = -kInf;
+    bool bad = false;
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      const int64_t vi = (int64_t)k * kThreads + tid;
+      const int64_t j0 = vi * E;
+      Pack<DT, E> p;
+      p.fill(0);
+      uint64_t kb = ~0ull;
+      const bool ld = j0 < prefix;
+      if (ld) {
+        const uint4 w = *reinterpret_cast<const uint4*>(row_lds + vi * 16);
+        p.w[0] = w.x;
+        p.w[1] = w.y;
+        p.w[2] = w.z;
+        p.w[3] = w.w;
+        if constexpr (KEEP) kb = load_keep<E>(a.mask.keep + row * cols + j0);
+      }
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const bool ok = ld && (j0 + e < prefix) && (!KEEP || keep_lane(kb, e));
+        const float f = ok ? p.get(e) : -kInf;
+        bad |= !(f < kInf);
+        mx = fmaxf(mx, f);
+        v[k][e] = f;
+      }
+    }
+    // the reductions' barriers also release the LDS row for the next one
+    mx = block_max<kWaves>(mx, red);
+    const bool poisoned = block_any<kWaves>(bad, red);
+
+    if (poisoned || mx == -kInf) {
+      Pack<DT, E> p;
+      p.fill(poisoned ? Fmt<DT>::kNaN : 0u);
+#pragma unroll
+      for (int k = 0; k < VPT; ++k) {
+        const int64_t j0 = ((int64_t)k * kThreads + tid) * E;
+        if (j0 < cols) p.store(yr + j0 * S);
+      }
+      continue;
+    }
+
+    float total;
+    if constexpr (ACC) {
+      KahanSum ks;
+#pragma unroll
+      for (int k = 0; k < VPT; ++k)
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const float t = exp_acc_b64(v[k][e], mx);
+          v[k][e] = t;
+          ks.add(t);
+        }
+      total = block_sum_pair<kWaves>(ks.hi(), ks.lo(), red);
+    } else {
+      float s = 0.0f;
+#pragma unroll
+      for (int k = 0; k < VPT; ++k)
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const float t = exp_hw_b64(v[k][e], mx);
+          v[k][e] = t;
+          s += t;
+        }
+      total = block_sum<kWaves>(s, red);
+    }
+    const float inv = 1.0f / total;
+
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      const int64_t j0 = ((int64_t)k * kThreads + tid) * E;
+      if (j0 < cols) {
+        uint32_t h[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) h[e] = enc<DT>(v[k][e] * inv);
+        Pack<DT, E> p;
+        p.put(h);
+        p.store(yr + j0 * S);
+      }
+    }
+  }
+}
+
+// rows up to 8 packs per thread: 32 KiB of LDS, 32 (f32) or 64 (16-bit)
+// register-resident values per thread
+constexpr int64_t kMaxRowBytes = (int64_t)kThreads * 8 * 16;
+
+template <int DT, int VPT>
+hipError_t launch_vpt(const RowArgs& a, hipStream_t s) {
+  constexpr int S = Fmt<DT>::S;
+  const int64_t bytes = ((a.cols * S + kPiece - 1) / kPiece) * kPiece;
+  const unsigned grid = (unsigned)(a.rows < (1 << 20) ? a.rows : (1 << 20));
+  if (a.mask.kind == kMaskKeep) {
+    hipLaunchKernelGGL((k_lds<DT, VPT, true>), dim3(grid), dim3(kThreads), (size_t)bytes, s, a);
+  } else {
+    hipLaunchKernelGGL((k_lds<DT, VPT, false>), dim3(grid), dim3(kThreads), (size_t)bytes, s, a);
+  }
+  return hipGetLastError();
+}
+
+template <int DT>
+hipError_t launch_dt(const RowArgs& a, hipStream_t s) {
+  constexpr int E = 16 / Fmt<DT>::S;
+  const int64_t per_vpt = (int64_t)kThreads * E;
+  const int64_t need = (a.cols + per_vpt - 1) / per_vpt;
+  if (need <= 2) return launch_vpt<DT, 2>(a, s);
+  if (need <= 4) return launch_vpt<DT, 4>(a, s);
+  return launch_vpt<DT, 8>(a, s);
+}
+
+}  // namespace
+
+int64_t lds_max_cols(int dtype) { return kMaxRowBytes / elem_size(dtype); }
+
+hipError_t launch_lds(const RowArgs& a, int dtype, hipStream_t s) {
+  switch (dtype) {
+    case kF32:
+      return launch_dt<kF32>(a, s);
+    case kF16:
+      return launch_dt<kF16>(a, s);
+    default:
+      return launch_dt<kBF16>(a, s);
+  }
+}
+
+}  // namespace smx

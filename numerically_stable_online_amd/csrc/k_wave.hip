@@ -1,0 +1,152 @@
+// k_wave.hip — one wave64 per row, the whole row held in registers.
+//
+// The row is read from HBM once ("Stable softmax: keep the normalizer
+// consistent as tiles arrive", paragraph on fused rows: load the row, find
+// its maximum and sum, write the normalized values). Each lane keeps VPT
+// packs of E elements: pack k of lane t covers elements (k*64 + t)*E ..
+// +E-1, so every load and store of a wave is one contiguous 1 KiB (E*S = 16)
+// or 64 contiguous elements (E = 1). Lanes keep a lane-wise running maximum
+// and sum and reduce once per row ("Softmax numerics architecture", pitfall
+// of reducing horizontally inside the loop).
+#include "smx_device.hpp"
+
+namespace smx {
+namespace {
+
+template <int DT, int E, int VPT, bool KEEP>
+__global__ __launch_bounds__(kThreads) void k_wave(RowArgs a) {
+  constexpr int S = Fmt<DT>::S;
+  constexpr bool ACC = DT == kF32;
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (row >= a.rows) return;  // wave-uniform
+  const int64_t cols = a.cols;
+  const int64_t prefix = valid_prefix(a.mask, row, cols);
+  const char* xr = a.x + row * cols * S;
+  char* yr = a.y + row * cols * S;
+
+  // load, mask, lane-wise max and the policy flag
+  float v[VPT][E];
+  float mx = -kInf;
+  bool bad = false;
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    const int64_t j0 = (int64_t)(k * 64 + lane) * E;
+    Pack<DT, E> p;
+    p.fill(0);
+    uint64_t kb = ~0ull;
+    const bool ld = j0 < prefix;
+    if (ld) {
+      p.load(xr + j0 * S);
+      if constexpr (KEEP) kb = load_keep<E>(a.mask.keep + row * cols + j0);
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const bool ok = ld && (j0 + e < prefix) && (!KEEP || keep_lane(kb, e));
+      const float f = ok ? p.get(e) : -kInf;
+      bad |= !(f < kInf);  // NaN or +inf in a valid lane
+      mx = fmaxf(mx, f);
+      v[k][e] = f;
+    }
+  }
+  mx = wave_max(mx);
+  const bool poisoned = wave_any(bad);
+
+  if (poisoned || mx == -kInf) {
+    // declared policy rows: canonical NaN, or all +0.0 with no -inf - -inf
+    Pack<DT, E> p;
+    p.fill(poisoned ? Fmt<DT>::kNaN : 0u);
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      const int64_t j0 = (int64_t)(k * 64 + lane) * E;
+      if (j0 < cols) p.store(yr + j0 * S);
+    }
+    return;
+  }
+
+  // exp(x - m) * 2^64 and its sum; masked lanes give exactly 0
+  float total;
+  if constexpr (ACC) {
+    KahanSum ks;
+#pragma unroll
+    for (int k = 0; k < VPT; ++k)
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const float t = exp_acc_b64(v[k][e], mx);
+        v[k][e] = t;
+        ks.add(t);
+      }
+    total = wave_sum_pair(ks.hi(), ks.lo());
+  } else {
+    float s = 0.0f;
+#pragma unroll
+    for (int k = 0; k < VPT; ++k)
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const float t = exp_hw_b64(v[k][e], mx);
+        v[k][e] = t;
+        s += t;
+      }
+    total = wave_sum(s);
+  }
+  const float inv = 1.0f / total;  // 2^-64 / l
+
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    const int64_t j0 = (int64_t)(k * 64 + lane) * E;
+    if (j0 < cols) {
+      uint32_t h[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) h[e] = enc<DT>(v[k][e] * inv);
+      Pack<DT, E> p;
+      p.put(h);
+      p.store(yr + j0 * S);
+    }
+  }
+}
+
+template <int DT, int E, int VPT>
+hipError_t launch_vpt(const RowArgs& a, hipStream_t stream) {
+  const int64_t blocks = (a.rows + kWaves - 1) / kWaves;
+  if (a.mask.kind == kMaskKeep) {
+    hipLaunchKernelGGL((k_wave<DT, E, VPT, true>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((k_wave<DT, E, VPT, false>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+// the smallest register budget that holds the row
+template <int DT, int E>
+hipError_t launch_e(const RowArgs& a, hipStream_t stream) {
+  const int64_t per_vpt = 64 * E;
+  const int64_t need = (a.cols + per_vpt - 1) / per_vpt;
+  if constexpr (E == 1) {
+    if (need <= 2) return launch_vpt<DT, E, 2>(a, stream);
+    if (need <= 8) return launch_vpt<DT, E, 8>(a, stream);
+    return launch_vpt<DT, E, 32>(a, stream);
+  } else {
+    if (need <= 1) return launch_vpt<DT, E, 1>(a, stream);
+    if (need <= 2) return launch_vpt<DT, E, 2>(a, stream);
+    if (need <= 4) return launch_vpt<DT, E, 4>(a, stream);
+    return launch_vpt<DT, E, 8>(a, stream);
+  }
+}
+
+}  // namespace
+
+int64_t wave_max_cols(int dtype, bool vec) { return vec ? 64 * 8 * vec_elems(dtype) : 64 * 32; }
+
+hipError_t launch_wave(const RowArgs& a, int dtype, bool vec, hipStream_t stream) {
+  if (a.rows / kWaves >= (int64_t)INT32_MAX) return hipErrorInvalidValue;
+  switch (dtype) {
+    case kF32:
+      return vec ? launch_e<kF32, 4>(a, stream) : launch_e<kF32, 1>(a, stream);
+    case kF16:
+      return vec ? launch_e<kF16, 8>(a, stream) : launch_e<kF16, 1>(a, stream);
+    default:
+      return vec ? launch_e<kBF16, 8>(a, stream) : launch_e<kBF16, 1>(a, stream);
+  }
+}
+
+}  // namespace smx

@@ -1,0 +1,225 @@
+// smx_api.hip — the C ABI: argument checks, path choice and launches.
+//
+// Nothing here touches the device before every argument has been checked;
+// an invalid call returns SMX_EINVAL with a message and enqueues nothing.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "smx_internal.hpp"
+
+namespace smx {
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return SMX_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(SMX_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Row geometry and mask, checked.
+struct Call {
+  RowArgs a{};
+  int dtype = 0;
+  bool vec = false;  // 128-bit accesses allowed
+};
+
+int check_common(const void* x, const void* y, int64_t rows, int64_t cols, int dtype, const smx_mask* mk,
+                 bool need_y, Call& c) {
+  if (dtype != SMX_F32 && dtype != SMX_F16 && dtype != SMX_BF16)
+    return fail(SMX_EINVAL, "dtype %d is not SMX_F32, SMX_F16 or SMX_BF16", dtype);
+  if (rows < 0 || cols < 0) return fail(SMX_EINVAL, "rows (%lld) and cols (%lld) must be >= 0", (long long)rows,
+                                        (long long)cols);
+  const int64_t s = elem_size(dtype);
+  if (cols > 0 && rows > INT64_MAX / cols / s) return fail(SMX_EINVAL, "rows * cols * element size overflows int64");
+  const int64_t n = rows * cols;
+  if (n > 0 && x == nullptr) return fail(SMX_EINVAL, "x is NULL");
+  if (need_y && n > 0 && y == nullptr) return fail(SMX_EINVAL, "y is NULL");
+  if (need_y && n > 0 && x != y) {
+    const uintptr_t xa = (uintptr_t)x, ya = (uintptr_t)y, bytes = (uintptr_t)(n * s);
+    if (xa < ya + bytes && ya < xa + bytes) return fail(SMX_EINVAL, "x and y overlap without being equal");
+  }
+  MaskArgs m{};
+  m.kind = mk ? (int)mk->kind : SMX_MASK_NONE;
+  switch (m.kind) {
+    case SMX_MASK_NONE:
+      break;
+    case SMX_MASK_VALID_LEN:
+      if (rows > 0 && mk->valid_len == nullptr) return fail(SMX_EINVAL, "SMX_MASK_VALID_LEN needs valid_len");
+      m.valid_len = mk->valid_len;
+      break;
+    case SMX_MASK_CAUSAL:
+      if (mk->causal_period <= 0) return fail(SMX_EINVAL, "SMX_MASK_CAUSAL needs causal_period > 0");
+      if (mk->causal_offset > ((int64_t)1 << 62) || mk->causal_offset < -((int64_t)1 << 62))
+        return fail(SMX_EINVAL, "causal_offset out of range (|offset| <= 2^62)");
+      m.period = mk->causal_period;
+      m.offset = mk->causal_offset;
+      break;
+    case SMX_MASK_KEEP_BYTES:
+      if (n > 0 && mk->keep == nullptr) return fail(SMX_EINVAL, "SMX_MASK_KEEP_BYTES needs keep");
+      m.keep = mk->keep;
+      break;
+    default:
+      return fail(SMX_EINVAL, "mask kind %d is not a smx_mask_kind", m.kind);
+  }
+  c.dtype = dtype;
+  c.a.x = (const char*)x;
+  c.a.y = (char*)y;
+  c.a.rows = rows;
+  c.a.cols = cols;
+  c.a.mask = m;
+  const int e = vec_elems(dtype);
+  c.vec = ((uintptr_t)x % 16 == 0) && (!need_y || (uintptr_t)y % 16 == 0) && ((cols * s) % 16 == 0) &&
+          (m.kind != SMX_MASK_KEEP_BYTES || (uintptr_t)m.keep % e == 0);
+  return SMX_OK;
+}
+
+// rows at least this many to fill the chip one workgroup per row
+constexpr int64_t kLdsMinRows = 1024;
+
+smx_path choose(int64_t rows, int64_t cols, int dtype, bool vec) {
+  const int64_t bytes = cols * elem_size(dtype);
+  if (cols <= wave_max_cols(dtype, vec) && bytes <= 4096) return SMX_PATH_WAVE;
+  if (vec && cols <= lds_max_cols(dtype) && rows >= kLdsMinRows) return SMX_PATH_LDS;
+  if (cols <= wave_max_cols(dtype, vec) && rows >= kLdsMinRows) return SMX_PATH_WAVE;
+  return SMX_PATH_SPLIT;
+}
+
+int64_t default_chunk(int64_t rows, int64_t cols, int dtype, bool vec) {
+  // one register round per workgroup, halved while the grid has fewer than
+  // 2048 workgroups (8 per CU), never below 64 packs
+  const int64_t e = vec ? vec_elems(dtype) : 1;
+  int64_t chunk = split_round_cols(dtype, vec);
+  const int64_t floor_chunk = 64 * e;
+  while (chunk > floor_chunk && rows * ((cols + chunk - 1) / chunk) < 2048) chunk /= 2;
+  return chunk;
+}
+
+int run_split(const Call& c, int64_t chunk, hipStream_t stream) {
+  const int64_t e = vec_elems(c.dtype);
+  const bool vec = c.vec && chunk % e == 0;
+  const int64_t nch = (c.a.cols + chunk - 1) / chunk;
+  void* ws = nullptr;
+  const size_t bytes = (size_t)(c.a.rows * nch) * sizeof(smx_stat);
+  hipError_t err = hipMallocAsync(&ws, bytes, stream);
+  if (err != hipSuccess) return hip_fail(err, "hipMallocAsync of the summary workspace");
+  err = launch_stats(c.a, c.dtype, vec, chunk, nch, (smx_stat*)ws, stream);
+  if (err == hipSuccess) err = launch_merge_normalize(c.a, c.dtype, vec, chunk, nch, (const smx_stat*)ws, stream);
+  const hipError_t ferr = hipFreeAsync(ws, stream);
+  if (err != hipSuccess) return hip_fail(err, "split-path launch");
+  if (ferr != hipSuccess) return hip_fail(ferr, "hipFreeAsync of the summary workspace");
+  return ok();
+}
+
+int run_rows(const Call& c, smx_path path, int64_t chunk_cols, hipStream_t stream) {
+  const int64_t rows = c.a.rows, cols = c.a.cols;
+  if (path == SMX_PATH_AUTO) path = choose(rows, cols, c.dtype, c.vec);
+  hipError_t err = hipSuccess;
+  switch (path) {
+    case SMX_PATH_WAVE:
+      if (cols > wave_max_cols(c.dtype, c.vec))
+        return fail(SMX_EINVAL, "the wave path holds at most %lld cols for this dtype/alignment",
+                    (long long)wave_max_cols(c.dtype, c.vec));
+      err = launch_wave(c.a, c.dtype, c.vec, stream);
+      break;
+    case SMX_PATH_LDS:
+      if (!c.vec)
+        return fail(SMX_EINVAL, "the LDS path needs 16-byte aligned x, y and rows of a multiple of 16 bytes");
+      if (cols > lds_max_cols(c.dtype))
+        return fail(SMX_EINVAL, "the LDS path holds at most %lld cols for this dtype",
+                    (long long)lds_max_cols(c.dtype));
+      err = launch_lds(c.a, c.dtype, stream);
+      break;
+    case SMX_PATH_SPLIT: {
+      if (chunk_cols < 0) return fail(SMX_EINVAL, "chunk_cols must be >= 0");
+      const int64_t chunk = chunk_cols > 0 ? chunk_cols : default_chunk(rows, cols, c.dtype, c.vec);
+      return run_split(c, chunk, stream);
+    }
+    default:
+      return fail(SMX_EINVAL, "path %d is not a smx_path", (int)path);
+  }
+  if (err != hipSuccess) return hip_fail(err, "kernel launch");
+  return ok();
+}
+
+}  // namespace
+}  // namespace smx
+
+using namespace smx;
+
+extern "C" {
+
+int softmax_rows_path(const void* x, void* y, int64_t rows, int64_t cols, smx_dtype dtype, const smx_mask* mask,
+                      smx_path path, int64_t chunk_cols, void* stream) {
+  Call c;
+  if (int rc = check_common(x, y, rows, cols, (int)dtype, mask, true, c)) return rc;
+  if ((int)path < SMX_PATH_AUTO || (int)path > SMX_PATH_SPLIT) return fail(SMX_EINVAL, "path %d is not a smx_path", (int)path);
+  if (chunk_cols < 0) return fail(SMX_EINVAL, "chunk_cols must be >= 0");
+  if (rows == 0 || cols == 0) return ok();
+  return run_rows(c, path, chunk_cols, (hipStream_t)stream);
+}
+
+int softmax_rows(const void* x, void* y, int64_t rows, int64_t cols, smx_dtype dtype, const smx_mask* mask,
+                 void* stream) {
+  return softmax_rows_path(x, y, rows, cols, dtype, mask, SMX_PATH_AUTO, 0, stream);
+}
+
+smx_path softmax_select_path(int64_t rows, int64_t cols, smx_dtype dtype) {
+  if ((int)dtype < 0 || (int)dtype > 2 || rows < 0 || cols < 0) return SMX_PATH_AUTO;
+  // the path for 16-byte aligned buffers
+  return choose(rows, cols, (int)dtype, (cols * elem_size((int)dtype)) % 16 == 0);
+}
+
+int64_t softmax_default_chunk_cols(int64_t rows, int64_t cols, smx_dtype dtype) {
+  if ((int)dtype < 0 || (int)dtype > 2 || rows < 0 || cols < 0) return 0;
+  return default_chunk(rows, cols, (int)dtype, (cols * elem_size((int)dtype)) % 16 == 0);
+}
+
+int softmax_row_stats(const void* x, int64_t rows, int64_t cols, smx_dtype dtype, const smx_mask* mask,
+                      int64_t chunk_cols, smx_stat* stats, void* stream) {
+  Call c;
+  if (int rc = check_common(x, nullptr, rows, cols, (int)dtype, mask, false, c)) return rc;
+  if (chunk_cols <= 0) return fail(SMX_EINVAL, "chunk_cols must be > 0");
+  const int64_t nch = (cols + chunk_cols - 1) / chunk_cols;
+  if (rows > 0 && nch > 0 && stats == nullptr) return fail(SMX_EINVAL, "stats is NULL");
+  if (rows == 0 || cols == 0) return ok();
+  const bool vec = c.vec && chunk_cols % vec_elems(c.dtype) == 0;
+  hipError_t err = launch_stats(c.a, c.dtype, vec, chunk_cols, nch, stats, (hipStream_t)stream);
+  if (err != hipSuccess) return hip_fail(err, "stats launch");
+  return ok();
+}
+
+int softmax_merge_normalize(const void* x, void* y, int64_t rows, int64_t cols, smx_dtype dtype,
+                            const smx_mask* mask, int64_t chunk_cols, const smx_stat* stats, int64_t n_chunks,
+                            void* stream) {
+  Call c;
+  if (int rc = check_common(x, y, rows, cols, (int)dtype, mask, true, c)) return rc;
+  if (chunk_cols <= 0) return fail(SMX_EINVAL, "chunk_cols must be > 0");
+  const int64_t nch = (cols + chunk_cols - 1) / chunk_cols;
+  if (n_chunks != nch)
+    return fail(SMX_EINVAL, "n_chunks is %lld but ceil(cols / chunk_cols) is %lld", (long long)n_chunks,
+                (long long)nch);
+  if (rows > 0 && nch > 0 && stats == nullptr) return fail(SMX_EINVAL, "stats is NULL");
+  if (rows == 0 || cols == 0) return ok();
+  const bool vec = c.vec && chunk_cols % vec_elems(c.dtype) == 0;
+  hipError_t err = launch_merge_normalize(c.a, c.dtype, vec, chunk_cols, nch, stats, (hipStream_t)stream);
+  if (err != hipSuccess) return hip_fail(err, "merge/normalize launch");
+  return ok();
+}
+
+const char* smx_last_error(void) { return g_err; }
+
+}  // extern "C"

@@ -1,0 +1,362 @@
+// smx_device.hpp — gfx950 building blocks of the row-softmax kernels:
+// element formats, 128-bit row access, wave64 DPP reductions, workgroup
+// reductions and the (m, l) summary merge.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "smx_internal.hpp"
+#include "smx_math.hpp"
+
+namespace smx {
+
+constexpr float kInf = __builtin_huge_valf();
+constexpr float kLog2e = 1.44269502162933349609375f;
+
+// ---------------------------------------------------------------------------
+// Element formats. DT: 0 = f32, 1 = f16, 2 = bf16.
+// ---------------------------------------------------------------------------
+
+template <int DT>
+struct Fmt {
+  static constexpr int S = DT == kF32 ? 4 : 2;  // bytes per element
+  static constexpr uint32_t kNaN = DT == kF32 ? 0x7FC00000u : (DT == kF16 ? 0x7E00u : 0x7FC0u);
+};
+
+// Exact widening of one element's bits to fp32.
+template <int DT>
+__device__ __forceinline__ float dec(uint32_t h) {
+  if constexpr (DT == kF32) {
+    return u2f(h);
+  } else if constexpr (DT == kF16) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+  } else {
+    return u2f(h << 16);
+  }
+}
+
+// Nearest-even rounding of a finite non-negative fp32 value to the element
+// format, gradual underflow kept.
+template <int DT>
+__device__ __forceinline__ uint32_t enc(float f) {
+  if constexpr (DT == kF32) {
+    return f2u(f);
+  } else if constexpr (DT == kF16) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
+  } else {
+    return bf16_rne(f);
+  }
+}
+
+// E consecutive elements: one 128-bit access (E * S == 16) or one element.
+template <int DT, int E>
+struct Pack {
+  static constexpr int S = Fmt<DT>::S;
+  static_assert(E == 1 || E * S == 16, "a pack is 16 bytes or one element");
+  static constexpr int W = E == 1 ? 1 : 4;
+  uint32_t w[W];
+
+  __device__ __forceinline__ void load(const char* p) {
+    if constexpr (E * S == 16) {
+      const uint4 v = *reinterpret_cast<const uint4*>(p);
+      w[0] = v.x;
+      w[1] = v.y;
+      w[2] = v.z;
+      w[3] = v.w;
+    } else if constexpr (S == 4) {
+      w[0] = *reinterpret_cast<const uint32_t*>(p);
+    } else {
+      w[0] = *reinterpret_cast<const uint16_t*>(p);
+    }
+  }
+  __device__ __forceinline__ void store(char* p) const {
+    if constexpr (E * S == 16) {
+      *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+    } else if constexpr (S == 4) {
+      *reinterpret_cast<uint32_t*>(p) = w[0];
+    } else {
+      *reinterpret_cast<uint16_t*>(p) = (uint16_t)w[0];
+    }
+  }
+  __device__ __forceinline__ float get(int e) const {
+    if constexpr (S == 4) {
+      return dec<DT>(w[e]);
+    } else if constexpr (DT == kBF16) {
+      const uint32_t word = w[e >> 1];
+      return u2f((e & 1) ? (word & 0xFFFF0000u) : (word << 16));
+    } else {
+      return dec<DT>((w[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu);
+    }
+  }
+  // fill from E element bit patterns
+  __device__ __forceinline__ void put(const uint32_t (&h)[E]) {
+    if constexpr (S == 4 || E == 1) {
+#pragma unroll
+      for (int i = 0; i < E; ++i) w[i] = h[i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < E / 2; ++i) w[i] = h[2 * i] | (h[2 * i + 1] << 16);
+    }
+  }
+  __device__ __forceinline__ void fill(uint32_t h) {
+    const uint32_t word = S == 4 || E == 1 ? h : (h | (h << 16));
+#pragma unroll
+    for (int i = 0; i < W; ++i) w[i] = word;
+  }
+};
+
+// E keep bytes of a KEEP_BYTES mask, as one integer (byte e = lane e).
+template <int E>
+__device__ __forceinline__ uint64_t load_keep(const uint8_t* p) {
+  if constexpr (E == 8) {
+    return *reinterpret_cast<const uint64_t*>(p);
+  } else if constexpr (E == 4) {
+    return *reinterpret_cast<const uint32_t*>(p);
+  } else {
+    return *p;
+  }
+}
+
+__device__ __forceinline__ bool keep_lane(uint64_t k, int e) { return ((k >> (8 * e)) & 0xFFu) != 0; }
+
+// Valid-prefix length of row r (the whole row for NONE and KEEP_BYTES).
+__device__ __forceinline__ int64_t valid_prefix(const MaskArgs& mk, int64_t r, int64_t cols) {
+  int64_t v = cols;
+  if (mk.kind == kMaskValidLen) {
+    v = mk.valid_len[r];
+  } else if (mk.kind == kMaskCausal) {
+    v = r % mk.period + 1 + mk.offset;
+  }
+  return v < 0 ? 0 : (v > cols ? cols : v);
+}
+
+// ---------------------------------------------------------------------------
+// Exponentials, scaled by 2^64 (a normal fp32 number down to exp(-131)).
+// ---------------------------------------------------------------------------
+
+// fp32 I/O: x - m carried exactly as hi + lo, then the polynomial exp.
+__device__ __forceinline__ float exp_acc_b64(float x, float m) {
+  float hi, lo;
+  two_diff(x, m, hi, lo);
+  return exp_biased64(hi, lo);
+}
+
+// 16-bit I/O: the hardware base-2 exponential, v_exp_f32. Its argument
+// carries a relative error of about 2^-23 |x - m|, far below half an ulp of
+// bf16 or fp16 wherever the result is not rounded to zero.
+__device__ __forceinline__ float exp_hw_b64(float x, float m) {
+  return __builtin_amdgcn_exp2f(__builtin_fmaf(x - m, kLog2e, 64.0f));
+}
+
+template <bool ACC>
+__device__ __forceinline__ float exp_b64(float x, float m) {
+  if constexpr (ACC) {
+    return exp_acc_b64(x, m);
+  } else {
+    return exp_hw_b64(x, m);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// The summary merge ("Online stable softmax", "Derive the update for two
+// blocks"): m' = max(m, m2), l' = exp(m - m') l + exp(m2 - m') l2, the side
+// holding m' with factor exactly 1. The sum is formed as a rounded product
+// plus a rounded product, so merge(a, b) == merge(b, a) bit for bit (the DPP
+// butterflies below rely on that to leave every lane with the same value).
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ void merge_ml(float& m, float& l, float m2, float l2) {
+  const float mm = fmaxf(m, m2);
+  const float fa = exp_diff(m, mm);
+  const float fb = exp_diff(m2, mm);
+  const float pa = l * fa;
+  const float pb = l2 * fb;
+  l = pa + pb;
+  m = mm;
+}
+
+// ---------------------------------------------------------------------------
+// Wave64 reductions: DPP within each 16-lane row (quad_perm xor 1, xor 2,
+// half-row mirror, row mirror), then the four row results read into scalars
+// and combined in a fixed order. Every lane returns the same value, and the
+// grouping never changes, so results are bitwise reproducible.
+// ---------------------------------------------------------------------------
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141;  // lane i <- lane 7 - i within 8
+constexpr int kDppMirror = 0x140;      // lane i <- lane 15 - i within 16
+
+__device__ __forceinline__ float lane_read(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp<kDppXor1>(v));
+  v = fmaxf(v, dpp<kDppXor2>(v));
+  v = fmaxf(v, dpp<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp<kDppMirror>(v));
+  return fmaxf(fmaxf(lane_read(v, 0), lane_read(v, 16)), fmaxf(lane_read(v, 32), lane_read(v, 48)));
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+  v = v + dpp<kDppXor1>(v);
+  v = v + dpp<kDppXor2>(v);
+  v = v + dpp<kDppHalfMirror>(v);
+  v = v + dpp<kDppMirror>(v);
+  return (lane_read(v, 0) + lane_read(v, 16)) + (lane_read(v, 32) + lane_read(v, 48));
+}
+
+// compensated pair sum: (hi, lo) + (hi2, lo2) with the rounding error of the
+// high parts carried into the low part
+__device__ __forceinline__ void pair_add(float& hi, float& lo, float hi2, float lo2) {
+  float s, e;
+  two_sum(hi, hi2, s, e);
+  hi = s;
+  lo = (lo + lo2) + e;
+}
+
+template <int CTRL>
+__device__ __forceinline__ void pair_step(float& hi, float& lo) {
+  const float h2 = dpp<CTRL>(hi);
+  const float l2 = dpp<CTRL>(lo);
+  pair_add(hi, lo, h2, l2);
+}
+
+__device__ __forceinline__ float wave_sum_pair(float hi, float lo) {
+  pair_step<kDppXor1>(hi, lo);
+  pair_step<kDppXor2>(hi, lo);
+  pair_step<kDppHalfMirror>(hi, lo);
+  pair_step<kDppMirror>(hi, lo);
+  float h0 = lane_read(hi, 0), l0 = lane_read(lo, 0);
+  float h1 = lane_read(hi, 16), l1 = lane_read(lo, 16);
+  float h2 = lane_read(hi, 32), l2 = lane_read(lo, 32);
+  float h3 = lane_read(hi, 48), l3 = lane_read(lo, 48);
+  pair_add(h0, l0, h1, l1);
+  pair_add(h2, l2, h3, l3);
+  pair_add(h0, l0, h2, l2);
+  return h0 + l0;
+}
+
+template <int CTRL>
+__device__ __forceinline__ void ml_step(float& m, float& l) {
+  const float m2 = dpp<CTRL>(m);
+  const float l2 = dpp<CTRL>(l);
+  merge_ml(m, l, m2, l2);
+}
+
+__device__ __forceinline__ void wave_merge(float& m, float& l) {
+  ml_step<kDppXor1>(m, l);
+  ml_step<kDppXor2>(m, l);
+  ml_step<kDppHalfMirror>(m, l);
+  ml_step<kDppMirror>(m, l);
+  float m0 = lane_read(m, 0), l0 = lane_read(l, 0);
+  float m1 = lane_read(m, 16), l1 = lane_read(l, 16);
+  float m2 = lane_read(m, 32), l2 = lane_read(l, 32);
+  float m3 = lane_read(m, 48), l3 = lane_read(l, 48);
+  merge_ml(m0, l0, m1, l1);
+  merge_ml(m2, l2, m3, l3);
+  merge_ml(m0, l0, m2, l2);
+  m = m0;
+  l = l0;
+}
+
+__device__ __forceinline__ bool wave_any(bool b) { return __ballot(b) != 0; }
+
+// ---------------------------------------------------------------------------
+// Workgroup reductions over NW waves through a small LDS scratch. Every
+// thread combines the NW wave results in the same order; the trailing
+// barrier lets the scratch be reused at once.
+// ---------------------------------------------------------------------------
+
+struct RedScratch {
+  float a[16];
+  float b[16];
+  int flag[16];
+};
+
+template <int NW>
+__device__ __forceinline__ float block_max(float v, RedScratch& s) {
+  v = wave_max(v);
+  if ((threadIdx.x & 63) == 0) s.a[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float r = s.a[0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) r = fmaxf(r, s.a[i]);
+  __syncthreads();
+  return r;
+}
+
+template <int NW>
+__device__ __forceinline__ bool block_any(bool b, RedScratch& s) {
+  const bool w = wave_any(b);
+  if ((threadIdx.x & 63) == 0) s.flag[threadIdx.x >> 6] = w ? 1 : 0;
+  __syncthreads();
+  int r = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) r |= s.flag[i];
+  __syncthreads();
+  return r != 0;
+}
+
+template <int NW>
+__device__ __forceinline__ float block_sum(float v, RedScratch& s) {
+  v = wave_sum(v);
+  if ((threadIdx.x & 63) == 0) s.a[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float r = s.a[0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) r = r + s.a[i];
+  __syncthreads();
+  return r;
+}
+
+template <int NW>
+__device__ __forceinline__ float block_sum_pair(float hi, float lo, RedScratch& s) {
+  // wave result as an exact-ish pair, then pairs across waves
+  pair_step<kDppXor1>(hi, lo);
+  pair_step<kDppXor2>(hi, lo);
+  pair_step<kDppHalfMirror>(hi, lo);
+  pair_step<kDppMirror>(hi, lo);
+  float h0 = lane_read(hi, 0), l0 = lane_read(lo, 0);
+  float h1 = lane_read(hi, 16), l1 = lane_read(lo, 16);
+  float h2 = lane_read(hi, 32), l2 = lane_read(lo, 32);
+  float h3 = lane_read(hi, 48), l3 = lane_read(lo, 48);
+  pair_add(h0, l0, h1, l1);
+  pair_add(h2, l2, h3, l3);
+  pair_add(h0, l0, h2, l2);
+  if ((threadIdx.x & 63) == 0) {
+    s.a[threadIdx.x >> 6] = h0;
+    s.b[threadIdx.x >> 6] = l0;
+  }
+  __syncthreads();
+  float rh = s.a[0], rl = s.b[0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) pair_add(rh, rl, s.a[i], s.b[i]);
+  __syncthreads();
+  return rh + rl;
+}
+
+template <int NW>
+__device__ __forceinline__ void block_merge(float& m, float& l, RedScratch& s) {
+  wave_merge(m, l);
+  if ((threadIdx.x & 63) == 0) {
+    s.a[threadIdx.x >> 6] = m;
+    s.b[threadIdx.x >> 6] = l;
+  }
+  __syncthreads();
+  float rm = s.a[0], rl = s.b[0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) merge_ml(rm, rl, s.a[i], s.b[i]);
+  __syncthreads();
+  m = rm;
+  l = rl;
+}
+
+}  // namespace smx

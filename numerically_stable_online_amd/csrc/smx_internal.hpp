@@ -1,0 +1,62 @@
+// smx_internal.hpp — what the host dispatcher and the kernel files share:
+// argument bundles, constants and the launchers each kernel file defines.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "smx.h"
+
+namespace smx {
+
+constexpr int kF32 = SMX_F32;
+constexpr int kF16 = SMX_F16;
+constexpr int kBF16 = SMX_BF16;
+
+constexpr int kMaskNone = SMX_MASK_NONE;
+constexpr int kMaskValidLen = SMX_MASK_VALID_LEN;
+constexpr int kMaskCausal = SMX_MASK_CAUSAL;
+constexpr int kMaskKeep = SMX_MASK_KEEP_BYTES;
+
+// Workgroup size of every kernel: four wave64s.
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+
+struct MaskArgs {
+  int kind;
+  const int32_t* valid_len;
+  int64_t period;
+  int64_t offset;
+  const uint8_t* keep;
+};
+
+struct RowArgs {
+  const char* x;
+  char* y;
+  int64_t rows;
+  int64_t cols;
+  MaskArgs mask;
+};
+
+inline int elem_size(int dtype) { return dtype == kF32 ? 4 : 2; }
+// elements per 128-bit access
+inline int vec_elems(int dtype) { return 16 / elem_size(dtype); }
+
+// --- wave-per-row kernel (k_wave.hip) ---
+// Largest cols the wave path holds in registers.
+int64_t wave_max_cols(int dtype, bool vec);
+hipError_t launch_wave(const RowArgs& a, int dtype, bool vec, hipStream_t stream);
+
+// --- workgroup-per-row, LDS-staged kernel (k_lds.hip) ---
+int64_t lds_max_cols(int dtype);
+hipError_t launch_lds(const RowArgs& a, int dtype, hipStream_t stream);
+
+// --- split path (k_split.hip) ---
+// Elements one workgroup holds per round of a chunk.
+int64_t split_round_cols(int dtype, bool vec);
+hipError_t launch_stats(const RowArgs& a, int dtype, bool vec, int64_t chunk_cols, int64_t n_chunks,
+                        smx_stat* stats, hipStream_t stream);
+hipError_t launch_merge_normalize(const RowArgs& a, int dtype, bool vec, int64_t chunk_cols,
+                                  int64_t n_chunks, const smx_stat* stats, hipStream_t stream);
+
+}  // namespace smx

@@ -1,0 +1,134 @@
+"""CPU-only checks of the C ABI boundary: the library loads, exports every
+symbol include/smx.h declares, rejects bad arguments before touching a device,
+and its scalar arithmetic (built for the host) meets its accuracy claims.
+No kernel is launched here.
+"""
+import ctypes as C
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "smx.h")
+
+
+@pytest.fixture(scope="module")
+def smx():
+    import numerically_stable_online_amd as m
+
+    if not os.path.exists(m.LIB_PATH):
+        from numerically_stable_online_amd import build
+
+        build.build()
+    return m
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_][a-z_0-9]*)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("softmax_rows", "softmax_rows_path", "softmax_row_stats", "softmax_merge_normalize",
+              "softmax_default_chunk_cols", "softmax_select_path", "smx_last_error"):
+        assert n in names, names
+
+
+def test_library_exports_every_declared_symbol(smx):
+    out = subprocess.run(["nm", "-D", "--defined-only", smx.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    missing = [n for n in declared_functions() if n not in exported]
+    assert not missing, missing
+    lib = smx.lib()
+    for n in declared_functions():
+        assert getattr(lib, n) is not None
+
+
+def test_header_is_plain_c(tmp_path):
+    src = tmp_path / "use.c"
+    src.write_text('#include "smx.h"\nint main(void){ smx_stat s; s.m = 0; s.l = 1; return (int)s.l - 1; }\n')
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only", f"-I{ROOT}/include", str(src)],
+                   check=True)
+
+
+def _call(smx, *args):
+    return smx.lib().softmax_rows(*args)
+
+
+def test_argument_checks_need_no_device(smx):
+    L = smx.lib()
+    EINVAL = smx.SMX_EINVAL
+    m = smx.SmxMask()
+    cases = [
+        ((None, None, -1, 4, 0, None, None), "rows"),
+        ((None, None, 4, -1, 0, None, None), "cols"),
+        ((None, None, 4, 4, 3, None, None), "dtype"),
+        ((None, None, 4, 4, 0, None, None), "x is NULL"),
+        ((16, None, 4, 4, 0, None, None), "y is NULL"),
+        ((4096, 4096 + 8, 4, 4, 0, None, None), "overlap"),
+        ((16, 4096, 1 << 40, 1 << 40, 0, None, None), "overflow"),
+    ]
+    for args, word in cases:
+        assert L.softmax_rows(*args) == EINVAL, word
+        assert word.split()[0] in smx.smx_last_error(), (word, smx.smx_last_error())
+    m.kind = 1  # VALID_LEN without the array
+    assert L.softmax_rows(16, 4096, 4, 4, 0, C.byref(m), None) == EINVAL
+    m.kind = 2  # CAUSAL with a bad period
+    m.causal_period = 0
+    assert L.softmax_rows(16, 4096, 4, 4, 0, C.byref(m), None) == EINVAL
+    m.kind = 3  # KEEP without bytes
+    assert L.softmax_rows(16, 4096, 4, 4, 0, C.byref(m), None) == EINVAL
+    m.kind = 9
+    assert L.softmax_rows(16, 4096, 4, 4, 0, C.byref(m), None) == EINVAL
+    # forced paths that cannot hold the shape are rejected before any launch
+    assert L.softmax_rows_path(16, 1 << 20, 4, 100000, 0, None, 1, 0, None) == EINVAL
+    assert L.softmax_rows_path(17, 1 << 20, 4, 64, 0, None, 2, 0, None) == EINVAL
+    assert L.softmax_rows_path(16, 1 << 20, 4, 64, 0, None, 7, 0, None) == EINVAL
+    assert L.softmax_rows_path(16, 1 << 20, 4, 64, 0, None, 3, -5, None) == EINVAL
+    # the summary calls
+    assert L.softmax_row_stats(16, 4, 64, 0, None, 0, 64, None) == EINVAL
+    assert L.softmax_row_stats(16, 4, 64, 0, None, 16, None, None) == EINVAL
+    assert L.softmax_merge_normalize(16, 1 << 20, 4, 64, 0, None, 16, 4096, 3, None) == EINVAL
+    assert "n_chunks" in smx.smx_last_error()
+
+
+def test_empty_shapes_are_noops(smx):
+    L = smx.lib()
+    assert L.softmax_rows(None, None, 0, 5, 0, None, None) == 0
+    assert L.softmax_rows(None, None, 7, 0, 2, None, None) == 0
+    assert L.softmax_row_stats(None, 0, 10, 1, None, 4, None, None) == 0
+    assert smx.smx_last_error() == ""
+
+
+def test_path_choice_and_default_chunk(smx):
+    assert smx.softmax_select_path(64, 1024, "f32") == "wave"
+    assert smx.softmax_select_path(8192, 4096, "bf16") == "lds"
+    assert smx.softmax_select_path(32768, 512, "f16") == "wave"
+    assert smx.softmax_select_path(64, 1 << 20, "f32") == "split"
+    assert smx.softmax_select_path(524288, 2048, "bf16") == "wave"
+    c = smx.softmax_default_chunk_cols(64, 1 << 20, "f32")
+    assert c > 0 and c % 4 == 0 and 64 * (-(-(1 << 20) // c)) >= 2048
+    for rows, cols, dt in ((1, 10, "bf16"), (3, 100000, "f16"), (1000, 5000, "f32")):
+        c = smx.softmax_default_chunk_cols(rows, cols, dt)
+        assert c >= 64 and c % (4 if dt == "f32" else 8) == 0
+
+
+def test_kernel_arithmetic_on_host(tmp_path):
+    """The kernels' scalar arithmetic built for the CPU: the fp32 exponential
+    is within one ulp of libm's double exp over [-120, 0] (every 8th float,
+    and exact differences x - m with a low part), merge identities are exact,
+    and bf16 rounding is nearest-even."""
+    exe = tmp_path / "check_smx_math"
+    subprocess.run(["g++", "-std=c++20", "-O2", "-ffp-contract=off",
+                    f"-I{ROOT}/numerically_stable_online_amd/csrc",
+                    f"{ROOT}/tests/csrc/check_smx_math.cpp", "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe), "8"], capture_output=True, text=True, check=True).stdout
+    vals = dict(kv.split("=") for kv in out.split() if "=" in kv)
+    assert float(vals["max_ulp"]) < 1.0 and float(vals["max_ulp_pair"]) < 1.0, out
+    assert vals["bad_identity"] == "0" and vals["bad_bf16"] == "0", out

@@ -1,0 +1,348 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Every comparison is element by element, to the bars in smx_compare: f32 within
+1e-6 relative and rows summing to 1 within 1e-5, f16/bf16 within 1 ulp of the
+correctly rounded oracle value, policy lanes bit-exact. The five workloads run
+at their full sizes, with the launch configuration the benchmark times (the
+automatic path), and again on every other path that can hold them.
+"""
+import numpy as np
+import pytest
+import torch
+
+import numerically_stable_online_amd as smx
+import oracle
+import workloads as W
+from smx_compare import TORCH_DTYPE, check, to_device, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def banner(msg: str) -> None:
+    print(f"[gpu] {msg}", flush=True)
+
+
+def mask_kwargs(mask: W.MaskSpec):
+    if mask is None or mask.kind == "none":
+        return {}
+    if mask.kind == "valid_len":
+        return {"valid_len": torch.from_numpy(np.ascontiguousarray(mask.valid_len, dtype=np.int32)).cuda()}
+    if mask.kind == "causal":
+        return {"causal_period": mask.causal_period, "causal_offset": mask.causal_offset}
+    return {"keep": torch.from_numpy(np.ascontiguousarray(mask.keep, dtype=np.uint8)).cuda()}
+
+
+def run_rows(x_raw, dtype, mask=None, path="auto", chunk_cols=0, misalign=False):
+    rows, cols = x_raw.shape
+    if misalign:  # shift x and y one element off any 16-byte boundary
+        buf = torch.empty(rows * cols + 1, dtype=TORCH_DTYPE[dtype], device="cuda")
+        x = buf[1:].view(rows, cols)
+        x.copy_(to_device(x_raw, dtype))
+        ybuf = torch.empty(rows * cols + 1, dtype=TORCH_DTYPE[dtype], device="cuda")
+        y = ybuf[1:].view(rows, cols)
+    else:
+        x = to_device(x_raw, dtype)
+        y = torch.empty_like(x)
+    smx.softmax_rows(x, y, path=path, chunk_cols=chunk_cols, **mask_kwargs(mask))
+    torch.cuda.synchronize()
+    return to_host(y, dtype)
+
+
+def check_full(x_raw, dtype, mask, y_raw, what):
+    p, cls, st = oracle.softmax_rows(x_raw, dtype, mask)
+    return check(y_raw, dtype, p, cls, st, what)
+
+
+# ---------------------------------------------------------------------------
+# The five workloads at full size
+# ---------------------------------------------------------------------------
+
+def test_select_path_for_workloads():
+    assert smx.softmax_select_path(64, 1024, "f32") == "wave"
+    assert smx.softmax_select_path(8192, 4096, "bf16") == "lds"
+    assert smx.softmax_select_path(32768, 512, "f16") == "wave"
+    assert smx.softmax_select_path(64, 1 << 20, "f32") == "split"
+    assert smx.softmax_select_path(524288, 2048, "bf16") == "wave"
+
+
+@pytest.mark.parametrize("path", ["auto", "wave", "lds", "split"])
+def test_config1(path):
+    w = W.config1()
+    banner(f"config1 {path}")
+    y = run_rows(w.x, "f32", w.mask, path=path, chunk_cols=256 if path == "split" else 0)
+    r = check_full(w.x, "f32", w.mask, y, f"config1/{path}")
+    banner(f"config1 {path}: {r}")
+
+
+@pytest.mark.parametrize("dtype", W.DTYPES)
+def test_fixed_rows(dtype):
+    for w in W.fixed_rows():
+        x = W.to_format(W.to_float(w.x, "f32").astype(np.float64), dtype)
+        for path in ("auto", "split"):
+            banner(f"{w.name} {dtype} {path}")
+            y = run_rows(x, dtype, None, path=path, chunk_cols=2 if path == "split" else 0)
+            check_full(x, dtype, None, y, f"{w.name}/{dtype}/{path}")
+            assert np.isfinite(W.to_float(y, dtype)).all()
+
+
+def test_worked_example_printed_values():
+    """[20, 18, 17, -5] on the GPU reproduces the printed probabilities."""
+    x = np.array([[20.0, 18.0, 17.0, -5.0]], dtype=np.float32)
+    y = run_rows(x, "f32")
+    assert np.allclose(y[0, :3], [0.84380, 0.11420, 0.04201], atol=1e-5)
+    assert abs(y[0, 3] - 1.17e-11) <= 5e-14
+
+
+@pytest.mark.parametrize("path", ["auto", "wave", "split"])
+def test_config2_full(path):
+    w = W.config2()
+    banner(f"config2 {path}")
+    y = run_rows(w.x, "bf16", w.mask, path=path)
+    r = check_full(w.x, "bf16", w.mask, y, f"config2/{path}")
+    banner(f"config2 {path}: {r}")
+
+
+@pytest.mark.parametrize("path", ["auto", "lds", "split"])
+def test_config3_full(path):
+    w = W.config3()
+    banner(f"config3 {path}")
+    y = run_rows(w.x, "f16", w.mask, path=path)
+    r = check_full(w.x, "f16", w.mask, y, f"config3/{path}")
+    banner(f"config3 {path}: {r}")
+
+
+@pytest.mark.parametrize("chunk", [0, 4096, 100000])
+def test_config4_full(chunk):
+    w = W.config4()
+    banner(f"config4 split chunk={chunk}")
+    y = run_rows(w.x, "f32", w.mask, path="auto" if chunk == 0 else "split", chunk_cols=chunk)
+    r = check_full(w.x, "f32", w.mask, y, f"config4/chunk{chunk}")
+    banner(f"config4 chunk={chunk}: {r}")
+
+
+@pytest.mark.timeout(600)
+def test_config5_full():
+    banner("config5 generate")
+    w = W.config5()
+    x = to_device(w.x, "bf16")
+    banner("config5 run")
+    y = smx.softmax_rows(x, causal_period=w.mask.causal_period)
+    torch.cuda.synchronize()
+    del x
+    y_raw = to_host(y, "bf16")
+    del y
+    banner("config5 compare")
+    n = 2048
+    worst = 0
+    for g in range(w.rows // n):
+        r0, r1 = g * n, (g + 1) * n
+        p, cls, st = oracle.softmax_rows(w.x, "bf16", w.mask, r0, r1)
+        r = check(y_raw[r0:r1], "bf16", p, cls, st, f"config5/group{g}")
+        worst = max(worst, r["max_ulp"])
+    # the injected rows follow the declared policy
+    nanrows = np.concatenate([w.special_rows["pos_inf_valid"], w.special_rows["nan_valid"]])
+    assert (y_raw[nanrows] == 0x7FC0).all()
+    assert (y_raw[w.special_rows["all_neg_inf"]] == 0).all()
+    banner(f"config5: max ulp {worst}")
+
+
+# ---------------------------------------------------------------------------
+# Shapes, alignments, masks and paths
+# ---------------------------------------------------------------------------
+
+ODD_COLS = [1, 3, 7, 8, 63, 64, 65, 255, 511, 513, 1000, 2047, 2048, 2049, 4095, 4096, 4104, 8191, 16385, 33000]
+
+
+def _masks(rows, cols, rng):
+    valid = rng.integers(-2, cols + 3, rows).astype(np.int32)
+    keep = (rng.random((rows, cols)) < 0.7).astype(np.uint8)
+    return [W.MaskSpec(), W.MaskSpec("valid_len", valid_len=valid),
+            W.MaskSpec("causal", causal_period=max(1, rows // 3), causal_offset=1),
+            W.MaskSpec("keep", keep=keep)]
+
+
+def _paths(dtype, cols, misalign):
+    paths = ["auto", "split"]
+    vec = not misalign and (cols * (4 if dtype == "f32" else 2)) % 16 == 0
+    wave_max = 64 * 8 * (4 if dtype == "f32" else 8) if vec else 64 * 32
+    if cols <= wave_max:
+        paths.append("wave")
+    if vec and cols <= 256 * 8 * (4 if dtype == "f32" else 8):
+        paths.append("lds")
+    return paths
+
+
+@pytest.mark.parametrize("dtype", W.DTYPES)
+def test_odd_shapes_masks_paths(dtype):
+    rng = np.random.default_rng(100)
+    for cols in ODD_COLS:
+        rows = 13
+        x = W.random_rows(rows, cols, dtype, seed=cols, scale=12.0)
+        for mask in _masks(rows, cols, rng):
+            p, cls, st = oracle.softmax_rows(x, dtype, mask)
+            for misalign in (False, True):
+                for path in _paths(dtype, cols, misalign):
+                    options = [c for c in (1, 5, 64, 200, 4096) if -(-cols // c) <= 512]
+                    chunk = 0 if path != "split" else int(rng.choice(options))
+                    what = f"{dtype} cols={cols} mask={mask.kind} misalign={misalign} path={path} chunk={chunk}"
+                    banner(what)
+                    y = run_rows(x, dtype, mask, path=path, chunk_cols=chunk, misalign=misalign)
+                    check(y, dtype, p, cls, st, what)
+
+
+@pytest.mark.parametrize("dtype", W.DTYPES)
+def test_policy_rows_bit_exact(dtype):
+    cols = 40
+    rows = 10
+    base = W.to_format(np.linspace(-5, 5, cols)[None, :].repeat(rows, 0), dtype)
+    x = base.copy()
+    pinf = W.POS_INF[dtype].view(np.uint32) if dtype == "f32" else W.POS_INF[dtype]
+    ninf = W.NEG_INF[dtype].view(np.uint32) if dtype == "f32" else W.NEG_INF[dtype]
+    W.set_bits(x, 0, 3, dtype, pinf)                 # +inf valid -> NaN row
+    W.set_bits(x, 1, 39, dtype, W.QNAN[dtype])        # NaN valid (last lane)
+    W.set_bits(x, 2, 0, dtype, W.NEG_SNAN[dtype])     # -sNaN valid
+    W.set_bits(x, 3, 30, dtype, W.QNAN[dtype])        # NaN masked -> ignored
+    W.set_bits(x, 4, 35, dtype, pinf)                 # +inf masked -> ignored
+    for j in range(cols):
+        W.set_bits(x, 5, j, dtype, ninf)              # all -inf -> zero row
+    for j in range(0, cols, 2):
+        W.set_bits(x, 6, j, dtype, ninf)              # half -inf
+    valid = np.array([40, 40, 40, 20, 20, 40, 40, 0, 1, 40], dtype=np.int32)  # row 7 empty
+    mask = W.MaskSpec("valid_len", valid_len=valid)
+    p, cls, st = oracle.softmax_rows(x, dtype, mask)
+    assert list(st[:3]) == [oracle.ROW_POISON] * 3 and st[5] == st[7] == oracle.ROW_EMPTY
+    for path in ("auto", "wave", "lds", "split"):
+        if path == "lds" and (cols * (4 if dtype == "f32" else 2)) % 16:
+            continue
+        banner(f"policy {dtype} {path}")
+        y = run_rows(x, dtype, mask, path=path, chunk_cols=7 if path == "split" else 0)
+        check(y, dtype, p, cls, st, f"policy/{dtype}/{path}")
+        assert float(W.to_float(y, dtype)[8, 0]) == 1.0  # one valid lane -> exactly 1
+
+
+@pytest.mark.parametrize("dtype", W.DTYPES)
+def test_exact_special_cases(dtype):
+    for k in (0, 5, 10, 12):
+        n = 1 << k
+        x = W.to_format(np.full((3, n), 2.5), dtype)
+        for path in ("auto", "split"):
+            y = W.to_float(run_rows(x, dtype, path=path), dtype)
+            assert (y == np.float32(2.0 ** -k)).all(), (dtype, k, path)
+    x = W.to_format(np.array([[-np.inf, 7.0, -np.inf, 7.0]]), dtype)
+    y = W.to_float(run_rows(x, dtype), dtype)
+    assert list(y[0]) == [0.0, 0.5, 0.0, 0.5]
+
+
+# ---------------------------------------------------------------------------
+# The summary calls on their own
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", W.DTYPES)
+def test_row_stats_against_oracle(dtype):
+    rng = np.random.default_rng(7)
+    rows, cols = 19, 5000
+    x = W.random_rows(rows, cols, dtype, seed=3, scale=20.0)
+    valid = rng.integers(0, cols + 1, rows).astype(np.int32)
+    valid[0] = 0
+    mask = W.MaskSpec("valid_len", valid_len=valid)
+    W.set_bits(x, 1, 10, dtype, W.QNAN[dtype])
+    tol = 2e-6 if dtype == "f32" else 2e-5
+    for chunk in (1, 100, 1024, 4096, 5000, 9999):
+        banner(f"stats {dtype} chunk={chunk}")
+        st = smx.softmax_row_stats(to_device(x, dtype), chunk, **mask_kwargs(mask)).cpu().numpy()
+        m, l = oracle.chunk_stats(x, dtype, chunk, mask)
+        nan = np.isnan(m)
+        assert np.array_equal(np.isnan(st[..., 0]), nan) and np.array_equal(np.isnan(st[..., 1]), nan)
+        fin = ~nan
+        assert np.array_equal(st[..., 0][fin], m[fin].astype(np.float32))  # the max is exact
+        empty = fin & (m == -np.inf)
+        assert (st[..., 1][empty] == 0).all()
+        live = fin & ~empty
+        rel = np.abs(st[..., 1][live] - l[live]) / l[live]
+        assert rel.max() <= tol, rel.max()
+
+
+@pytest.mark.parametrize("dtype", W.DTYPES)
+def test_merge_normalize_with_oracle_summaries(dtype):
+    """Summaries computed by the oracle (then rounded to fp32) go into the
+    library's merge/normalize; the oracle merges the same rounded summaries."""
+    rng = np.random.default_rng(8)
+    rows, cols, chunk = 11, 3000, 256
+    x = W.random_rows(rows, cols, dtype, seed=4, scale=30.0)
+    keep = (rng.random((rows, cols)) < 0.5).astype(np.uint8)
+    keep[2] = 0
+    mask = W.MaskSpec("keep", keep=keep)
+    m, l = oracle.chunk_stats(x, dtype, chunk, mask)
+    m32, l32 = m.astype(np.float32), l.astype(np.float32)
+    st = torch.from_numpy(np.stack([m32, l32], axis=-1)).cuda()
+    banner(f"merge_normalize {dtype}")
+    y = smx.softmax_merge_normalize(to_device(x, dtype), st, chunk, **mask_kwargs(mask))
+    torch.cuda.synchronize()
+    p, cls, s = oracle.merge_normalize(x, dtype, m32.astype(np.float64), l32.astype(np.float64), mask)
+    check(to_host(y, dtype), dtype, p, cls, s, f"merge_normalize/{dtype}")
+
+
+def test_merge_normalize_external_summaries_policy():
+    """Caller-made summaries: a NaN summary poisons its row, all-empty
+    summaries give a zero row, (-inf, 0) is an identity."""
+    x = W.to_format(np.zeros((3, 8)), "f32")
+    st = np.array([[[0.0, 4.0], [-np.inf, 0.0]],
+                   [[np.nan, np.nan], [0.0, 4.0]],
+                   [[-np.inf, 0.0], [-np.inf, 0.0]]], dtype=np.float32)
+    y = smx.softmax_merge_normalize(to_device(x, "f32"), torch.from_numpy(st).cuda(), 4)
+    y = to_host(y, "f32")
+    assert (y[0] == 0.25).all()
+    assert (y[1].view(np.uint32) == 0x7FC00000).all()
+    assert (y[2].view(np.uint32) == 0).all()
+
+
+# ---------------------------------------------------------------------------
+# Determinism, aliasing, streams and stray writes
+# ---------------------------------------------------------------------------
+
+def test_determinism_and_aliasing():
+    w = W.config2(rows=512)
+    x = to_device(w.x, "bf16")
+    for path in ("auto", "wave", "split"):
+        y1 = smx.softmax_rows(x, path=path)
+        y2 = smx.softmax_rows(x, path=path)
+        torch.cuda.synchronize()
+        assert torch.equal(y1.view(torch.int16), y2.view(torch.int16)), path
+        z = x.clone()
+        smx.softmax_rows(z, z, path=path)  # in place
+        torch.cuda.synchronize()
+        assert torch.equal(z.view(torch.int16), y1.view(torch.int16)), path
+
+
+def test_no_stray_writes():
+    rows, cols = 37, 2000
+    x_raw = W.random_rows(rows, cols, "f32", seed=9)
+    for path in ("auto", "wave", "lds", "split"):
+        guard = 4096
+        buf = torch.full((rows * cols + 2 * guard,), 123.0, device="cuda")
+        y = buf[guard:guard + rows * cols].view(rows, cols)
+        smx.softmax_rows(to_device(x_raw, "f32"), y, path=path)
+        torch.cuda.synchronize()
+        assert (buf[:guard] == 123.0).all() and (buf[-guard:] == 123.0).all(), path
+
+
+def test_nondefault_stream():
+    w = W.config3(rows=1024)
+    x = to_device(w.x, "f16")
+    vl = torch.from_numpy(w.mask.valid_len).cuda()
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        y = smx.softmax_rows(x, valid_len=vl)
+    s.synchronize()
+    check_full(w.x, "f16", w.mask, to_host(y, "f16"), "stream")
+
+
+def test_invalid_arguments_raise():
+    x = torch.zeros(4, 8, device="cuda")
+    with pytest.raises(smx.SmxError):
+        smx.softmax_rows(x.view(-1)[1:29].view(4, 7), path="lds")  # misaligned rows
+    with pytest.raises(smx.SmxError):
+        smx.softmax_rows(torch.zeros(2, 5000, device="cuda"), path="wave")  # too long for registers
+    with pytest.raises(smx.SmxError):
+        smx.softmax_merge_normalize(x, torch.zeros(4, 3, 2, device="cuda"), 4)  # wrong n_chunks
