@@ -1,0 +1,249 @@
+"""Benchmark: row-softmax effective HBM bandwidth on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--configs 1,2,3,4,5]
+
+One step is one softmax_rows call over one batch of the headline workload,
+8192 x 4096 bf16 rows (logits 8*N(0,1) plus a +30 spike per row), which the
+library runs on its LDS-staged workgroup-per-row kernel. The batch rotates
+through enough resident copies of x and y (>= 1 GiB in all) that every step
+streams from HBM instead of hitting the 256 MB Infinity Cache left warm by
+the previous step.
+
+value  = algorithmic bytes per step / mean step time, in GB/s (1e9 B/s);
+         algorithmic bytes = valid input lanes read (twice on the split path),
+         every output lane written, plus mask and chunk-summary bytes.
+roofline.achieved = the same bytes / the dominant kernel's mean launch time,
+         from HIP events recorded on the stream the kernel runs on.
+cpu_baseline = the CPU oracle (three-pass, double precision) on the same
+         input, on the host cores, writing the element format.
+
+Prints one JSON line. Other workloads (--configs) are reported inside it
+under "per_config".
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
+MALL_BYTES = 256 * 2 ** 20
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+KERNEL_SOURCES = {
+    "lds": ["k_lds.hip", "smx_device.hpp", "smx_math.hpp"],
+    "wave": ["k_wave.hip", "smx_device.hpp", "smx_math.hpp"],
+    "split": ["k_split.hip", "smx_device.hpp", "smx_math.hpp"],
+}
+KERNEL_NAME = {"lds": "k_lds", "wave": "k_wave", "split": "k_merge_normalize+k_stats"}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--configs", default="2,1,3,4,5",
+                    help="workloads to time; the first is the headline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain device copy of the headline x (counter calibration)")
+    return ap.parse_args()
+
+
+def kernel_source_sha(path: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[path]:
+        with open(os.path.join(ROOT, "numerically_stable_online_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(w, path: str, n_chunks: int = 0) -> int:
+    """Bytes the method must move for one pass over workload w."""
+    from workloads import ITEMSIZE
+
+    s = ITEMSIZE[w.dtype]
+    rows, cols, m = w.rows, w.cols, w.mask
+    if m.kind == "none":
+        valid, mask_bytes = rows * cols, 0
+    elif m.kind == "valid_len":
+        valid, mask_bytes = int(np.clip(m.valid_len.astype(np.int64), 0, cols).sum()), 4 * rows
+    elif m.kind == "causal":
+        r = np.arange(rows, dtype=np.int64)
+        valid, mask_bytes = int(np.clip(r % m.causal_period + 1 + m.causal_offset, 0, cols).sum()), 0
+    else:
+        valid, mask_bytes = int(np.count_nonzero(m.keep)), rows * cols
+    reads = 2 if path == "split" else 1
+    summaries = 2 * rows * n_chunks * 8 if path == "split" else 0
+    return reads * valid * s + rows * cols * s + mask_bytes + summaries
+
+
+def make_workload(k: int):
+    import workloads as W
+
+    return W.CONFIGS[k]()
+
+
+def time_workload(w, steps: int, warmup: int, calibrate_copy: bool = False):
+    import torch
+
+    import numerically_stable_online_amd as smx
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from smx_compare import to_device
+
+    x0 = to_device(w.x, w.dtype)
+    kw = {}
+    if w.mask.kind == "valid_len":
+        kw["valid_len"] = torch.from_numpy(w.mask.valid_len).cuda()
+    elif w.mask.kind == "causal":
+        kw["causal_period"] = w.mask.causal_period
+        kw["causal_offset"] = w.mask.causal_offset
+    pair_bytes = 2 * x0.numel() * x0.element_size()
+    free = torch.cuda.mem_get_info()[0]
+    copies = max(1, min(64, math.ceil(2 ** 30 / pair_bytes), int(0.5 * free // pair_bytes)))
+    if pair_bytes > 4 * MALL_BYTES:
+        copies = 1
+    xs = [x0] + [x0.clone() for _ in range(copies - 1)]
+    ys = [torch.empty_like(x0) for _ in range(copies)]
+    path = smx.softmax_select_path(w.rows, w.cols, x0.dtype)
+    n_chunks = 0
+    if path == "split":
+        chunk = smx.softmax_default_chunk_cols(w.rows, w.cols, x0.dtype)
+        n_chunks = -(-w.cols // chunk)
+    nbytes = algorithmic_bytes(w, path, n_chunks)
+
+    if calibrate_copy:
+        c = torch.empty_like(x0)
+        c.copy_(x0)
+        torch.cuda.synchronize()
+
+    for i in range(warmup):
+        smx.softmax_rows(xs[i % copies], ys[i % copies], **kw)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()  # the library launches on this stream
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        smx.softmax_rows(xs[i % copies], ys[i % copies], **kw)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+    return {
+        "path": path,
+        "bytes": nbytes,
+        "copies": copies,
+        "n_chunks": n_chunks,
+        "ms_per_step": wall * 1e3 / steps,
+        "launch_ms_mean": float(launch_ms.mean()),
+        "launch_ms_median": float(np.median(launch_ms)),
+        "launch_ms_p10": float(np.percentile(launch_ms, 10)),
+        "launch_ms_p90": float(np.percentile(launch_ms, 90)),
+    }
+
+
+def cpu_baseline(w, nbytes: int):
+    import oracle
+
+    threads = max(1, min(16, os.cpu_count() or 1))
+    times = []
+    t_end = time.perf_counter() + 12.0
+    while len(times) < 3 or (time.perf_counter() < t_end and len(times) < 10):
+        _, dt = oracle.softmax_rows_encode_mt(w.x, w.dtype, w.mask, threads)
+        times.append(dt)
+    med = float(np.median(times))
+    return {"value": nbytes / med / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"the whole {w.name} input ({w.rows}x{w.cols} {w.dtype}), {len(times)} runs, median "
+                      f"{med:.3f} s, three-pass double-precision oracle writing {w.dtype}",
+            "seconds": med}
+
+
+def load_traffic(path: str, kernel_sha: str, launch_bytes_key: str):
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    rec = t.get(launch_bytes_key)
+    if not rec or rec.get("source_sha") != kernel_sha:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(rows are independent: a multi-GPU run would split rows across devices)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    import numerically_stable_online_amd as smx
+
+    smx.lib()
+    cfgs = [int(c) for c in args.configs.split(",") if c]
+    per = {}
+    head = None
+    for k in cfgs:
+        w = make_workload(k)
+        r = time_workload(w, args.steps, args.warmup, calibrate_copy=args.calibrate_copy and head is None)
+        gbs = r["bytes"] / (r["ms_per_step"] * 1e-3) / 1e9
+        kgbs = r["bytes"] / (r["launch_ms_mean"] * 1e-3) / 1e9
+        entry = {"workload": w.name, "path": r["path"], "algorithmic_bytes": r["bytes"],
+                 "step_ms": round(r["ms_per_step"], 5), "launch_ms_mean": round(r["launch_ms_mean"], 5),
+                 "launch_ms_p10": round(r["launch_ms_p10"], 5), "launch_ms_p90": round(r["launch_ms_p90"], 5),
+                 "GBps_step": round(gbs, 1), "GBps_launch": round(kgbs, 1),
+                 "frac_of_peak": round(kgbs / HBM_PEAK_GBS, 4), "buffer_copies": r["copies"]}
+        per[f"config{k}"] = entry
+        print(f"# config{k} {w.name}: path={r['path']} {kgbs:.0f} GB/s per launch "
+              f"({r['launch_ms_mean'] * 1e3:.1f} us), {gbs:.0f} GB/s per step", file=sys.stderr, flush=True)
+        if head is None:
+            head = (k, w, r, gbs, kgbs)
+        else:
+            del w
+
+    k, w, r, gbs, kgbs = head
+    sha = kernel_source_sha(r["path"])
+    traffic = load_traffic(r["path"], sha, f"config{k}")
+    out = {
+        "metric": "row-softmax effective HBM GB/s (read+write bytes/time) and % of MI355X peak",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "rows": w.rows, "cols": w.cols, "mask": w.mask.kind,
+                   "path": r["path"], "seed": w.seed, "algorithmic_bytes_per_step": r["bytes"],
+                   "buffer_copies": r["copies"]},
+        "roofline": {"bound": "hbm", "kernel": KERNEL_NAME[r["path"]], "achieved": round(kgbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(kgbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel_source_sha": sha},
+        "per_config": per,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, r["bytes"])
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
