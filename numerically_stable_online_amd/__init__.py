@@ -90,9 +90,16 @@ def _check(rc: int) -> None:
         raise SmxError(rc, smx_last_error())
 
 
-def _stream_handle(stream) -> int:
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _stream_handle(stream, device) -> int:
+    """The hipStream_t to launch on: the given stream, else torch's current
+    stream on x's device."""
     if stream is None:
-        stream = torch.cuda.current_stream()
+        if _raw_stream is not None:
+            return _raw_stream(device.index if device.index is not None else torch.cuda.current_device())
+        stream = torch.cuda.current_stream(device)
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
@@ -113,9 +120,14 @@ def _rows_cols(x: torch.Tensor):
     return x.shape[0], x.shape[1]
 
 
+def _on(t: torch.Tensor, device, what: str) -> None:
+    if t.device != device:
+        raise ValueError(f"{what} must be on {device} (the library reads it on the device), got {t.device}")
+
+
 def make_mask(rows: int, cols: int, valid_len: Optional[torch.Tensor] = None,
               causal_period: Optional[int] = None, causal_offset: int = 0,
-              keep: Optional[torch.Tensor] = None):
+              keep: Optional[torch.Tensor] = None, device=None):
     """Build the C mask descriptor; returns (struct or None, tensors to keep alive)."""
     given = sum(v is not None for v in (valid_len, causal_period, keep))
     if given > 1:
@@ -126,6 +138,8 @@ def make_mask(rows: int, cols: int, valid_len: Optional[torch.Tensor] = None,
     if valid_len is not None:
         if valid_len.dtype != torch.int32 or valid_len.shape != (rows,) or not valid_len.is_contiguous():
             raise ValueError("valid_len must be a contiguous int32 device tensor of shape [rows]")
+        if device is not None:
+            _on(valid_len, device, "valid_len")
         m.kind = MASK["valid_len"]
         m.valid_len = valid_len.data_ptr()
         return m, (valid_len,)
@@ -136,6 +150,8 @@ def make_mask(rows: int, cols: int, valid_len: Optional[torch.Tensor] = None,
         return m, ()
     if keep.dtype not in (torch.uint8, torch.bool) or keep.shape != (rows, cols) or not keep.is_contiguous():
         raise ValueError("keep must be a contiguous uint8/bool device tensor of shape [rows, cols]")
+    if device is not None:
+        _on(keep, device, "keep")
     m.kind = MASK["keep"]
     m.keep = keep.data_ptr()
     return m, (keep,)
@@ -153,9 +169,10 @@ def softmax_rows(x: torch.Tensor, out: Optional[torch.Tensor] = None, *, valid_l
     y = torch.empty_like(x) if out is None else out
     if y.shape != x.shape or y.dtype != x.dtype or not y.is_contiguous():
         raise ValueError("out must be a contiguous tensor of x's shape and dtype")
-    m, keepalive = make_mask(rows, cols, valid_len, causal_period, causal_offset, keep)
+    _on(y, x.device, "out")
+    m, keepalive = make_mask(rows, cols, valid_len, causal_period, causal_offset, keep, x.device)
     rc = lib().softmax_rows_path(x.data_ptr(), y.data_ptr(), rows, cols, _dtype_code(x), _mask_arg(m),
-                                 PATH[path], int(chunk_cols), _stream_handle(stream))
+                                 PATH[path], int(chunk_cols), _stream_handle(stream, x.device))
     _check(rc)
     return y
 
@@ -169,9 +186,10 @@ def softmax_row_stats(x: torch.Tensor, chunk_cols: int, out: Optional[torch.Tens
     st = torch.empty((rows, nch, 2), dtype=torch.float32, device=x.device) if out is None else out
     if st.shape != (rows, nch, 2) or st.dtype != torch.float32 or not st.is_contiguous():
         raise ValueError("out must be a contiguous float32 tensor [rows, n_chunks, 2]")
-    m, keepalive = make_mask(rows, cols, valid_len, causal_period, causal_offset, keep)
+    _on(st, x.device, "out")
+    m, keepalive = make_mask(rows, cols, valid_len, causal_period, causal_offset, keep, x.device)
     rc = lib().softmax_row_stats(x.data_ptr(), rows, cols, _dtype_code(x), _mask_arg(m), int(chunk_cols),
-                                 st.data_ptr(), _stream_handle(stream))
+                                 st.data_ptr(), _stream_handle(stream, x.device))
     _check(rc)
     return st
 
@@ -184,11 +202,15 @@ def softmax_merge_normalize(x: torch.Tensor, stats: torch.Tensor, chunk_cols: in
     if stats.dim() != 3 or stats.shape[0] != rows or stats.shape[2] != 2 or stats.dtype != torch.float32 \
             or not stats.is_contiguous():
         raise ValueError("stats must be a contiguous float32 tensor [rows, n_chunks, 2]")
+    _on(stats, x.device, "stats")
     y = torch.empty_like(x) if out is None else out
-    m, keepalive = make_mask(rows, cols, valid_len, causal_period, causal_offset, keep)
+    if y.shape != x.shape or y.dtype != x.dtype or not y.is_contiguous():
+        raise ValueError("out must be a contiguous tensor of x's shape and dtype")
+    _on(y, x.device, "out")
+    m, keepalive = make_mask(rows, cols, valid_len, causal_period, causal_offset, keep, x.device)
     rc = lib().softmax_merge_normalize(x.data_ptr(), y.data_ptr(), rows, cols, _dtype_code(x), _mask_arg(m),
                                        int(chunk_cols), stats.data_ptr(), stats.shape[1],
-                                       _stream_handle(stream))
+                                       _stream_handle(stream, x.device))
     _check(rc)
     return y
 

@@ -2,7 +2,8 @@
 //
 // The row's valid prefix is copied from HBM straight into LDS with gfx950's
 // direct global->LDS 128-bit loads (global_load_lds_dwordx4): the copy needs
-// no VGPRs, so a workgroup can have the whole row in flight at once. The row
+// no VGPRs, so a workgroup can have the whole row in flight at once. Input
+// and output stream through the caches with the nontemporal bit set. The row
 // is read from HBM exactly once ("Stable softmax: keep the normalizer
 // consistent as tiles arrive", paragraph on fused rows); every thread then
 // takes its packs out of LDS into registers, and the max, the sum of
@@ -14,6 +15,7 @@ namespace smx {
 namespace {
 
 constexpr int kPiece = 64 * 16;  // bytes one wave's direct load moves
+constexpr int kAuxNT = 2;        // cache-policy operand: the nontemporal bit
 
 template <int DT, int VPT, bool KEEP>
 __global__ __launch_bounds__(kThreads) void k_lds(RowArgs a) {
@@ -40,7 +42,7 @@ __global__ __launch_bounds__(kThreads) void k_lds(RowArgs a) {
       const int64_t vsrc = vi < nvec ? vi : nvec - 1;  // stays inside the row
       __builtin_amdgcn_global_load_lds(
           (const void*)(xr + vsrc * 16),
-          (__attribute__((address_space(3))) void*)(row_lds + pc * kPiece), 16, 0, 0);
+          (__attribute__((address_space(3))) void*)(row_lds + pc * kPiece), 16, 0, kAuxNT);
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -83,7 +85,7 @@ __global__ __launch_bounds__(kThreads) void k_lds(RowArgs a) {
 #pragma unroll
       for (int k = 0; k < VPT; ++k) {
         const int64_t j0 = ((int64_t)k * kThreads + tid) * E;
-        if (j0 < cols) p.store(yr + j0 * S);
+        if (j0 < cols) p.template store<true>(yr + j0 * S);
       }
       continue;
     }
@@ -123,7 +125,7 @@ __global__ __launch_bounds__(kThreads) void k_lds(RowArgs a) {
         for (int e = 0; e < E; ++e) h[e] = enc<DT>(v[k][e] * inv);
         Pack<DT, E> p;
         p.put(h);
-        p.store(yr + j0 * S);
+        p.template store<true>(yr + j0 * S);
       }
     }
   }

@@ -24,14 +24,20 @@ constexpr int kVptScalar = 16;  // packs per thread per round for single-element
 
 template <int DT, int E>
 constexpr int vpt() {
-  return E == 1 ? kVptScalar : (DT == kF32 ? 16 : 8);
+  return E == 1 ? kVptScalar : 8;
 }
 
-template <int DT, int E, bool KEEP>
+// the stats pass keeps two rounds in registers (the one being reduced and
+// the one in flight)
+template <int DT, int E>
+constexpr int vpt_stats() {
+  return E == 1 ? 8 : 4;
+}
+
+template <int DT, int E, int VPT, bool KEEP>
 __global__ __launch_bounds__(kThreads) void k_stats(RowArgs a, int64_t chunk, int64_t nch, smx_stat* stats) {
   constexpr int S = Fmt<DT>::S;
   constexpr bool ACC = DT == kF32;
-  constexpr int VPT = vpt<DT, E>();
   constexpr int64_t kRound = (int64_t)kThreads * VPT * E;
   __shared__ RedScratch red;
   const int tid = threadIdx.x;
@@ -44,59 +50,75 @@ __global__ __launch_bounds__(kThreads) void k_stats(RowArgs a, int64_t chunk, in
     const int64_t prefix = valid_prefix(a.mask, row, a.cols);
     const int64_t lim = j_hi < prefix ? j_hi : prefix;
     const char* xr = a.x + row * a.cols * S;
+    const uint8_t* kr = KEEP ? a.mask.keep + row * a.cols : nullptr;
 
-    float m_t = -kInf, l_t = 0.0f;  // l_t scaled by 2^64
+    // issue one round's loads into registers
+    auto fetch = [&](int64_t base, Pack<DT, E>(&p)[VPT], uint64_t(&kb)[VPT]) {
+#pragma unroll
+      for (int k = 0; k < VPT; ++k) {
+        const int64_t j0 = base + (int64_t)(k * kThreads + tid) * E;
+        p[k].fill(0);
+        kb[k] = ~0ull;
+        if (j0 < lim) {
+          p[k].load(xr + j0 * S);
+          if constexpr (KEEP) kb[k] = load_keep<E>(kr + j0);
+        }
+      }
+    };
+
+    float m_t = -kInf, l_t = 0.0f;
     bool bad = false;
+    Pack<DT, E> cur[VPT];
+    uint64_t kcur[VPT];
+    if (j_lo < lim) fetch(j_lo, cur, kcur);
     for (int64_t base = j_lo; base < lim; base += kRound) {
-      float v[VPT][E];
+      // the next round's loads are in flight while this one is reduced
+      Pack<DT, E> nxt[VPT];
+      uint64_t knxt[VPT];
+      const bool more = base + kRound < lim;
+      if (more) fetch(base + kRound, nxt, knxt);
+
+      float v[VPT * E];
       float mr = -kInf;
 #pragma unroll
       for (int k = 0; k < VPT; ++k) {
         const int64_t j0 = base + (int64_t)(k * kThreads + tid) * E;
-        Pack<DT, E> p;
-        p.fill(0);
-        uint64_t kb = ~0ull;
-        const bool ld = j0 < lim;
-        if (ld) {
-          p.load(xr + j0 * S);
-          if constexpr (KEEP) kb = load_keep<E>(a.mask.keep + row * a.cols + j0);
-        }
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-          const bool ok = ld && (j0 + e < lim) && (!KEEP || keep_lane(kb, e));
-          const float f = ok ? p.get(e) : -kInf;
+          const bool ok = (j0 + e < lim) && (!KEEP || keep_lane(kcur[k], e));
+          const float f = ok ? cur[k].get(e) : -kInf;
           bad |= !(f < kInf);
           mr = fmaxf(mr, f);
-          v[k][e] = f;
+          v[k * E + e] = f;
         }
       }
       const float m_new = fmaxf(m_t, mr);
       if (m_new != -kInf) {
-        // correct the running sum, then add this round against m_new
-        float add;
-        if constexpr (ACC) {
-          KahanSum ks;
+        // correct the running sum, then add this round against m_new; the
+        // round's terms are summed as a tree in registers
 #pragma unroll
-          for (int k = 0; k < VPT; ++k)
-#pragma unroll
-            for (int e = 0; e < E; ++e) ks.add(exp_acc_b64(v[k][e], m_new));
-          add = ks.hi() + ks.lo();
-        } else {
-          float s = 0.0f;
-#pragma unroll
-          for (int k = 0; k < VPT; ++k)
-#pragma unroll
-            for (int e = 0; e < E; ++e) s += exp_hw_b64(v[k][e], m_new);
-          add = s;
+        for (int i = 0; i < VPT * E; ++i) {
+          if constexpr (ACC) {
+            v[i] = exp_acc_sum(v[i], m_new);
+          } else {
+            v[i] = __builtin_amdgcn_exp2f((v[i] - m_new) * kLog2e);
+          }
         }
-        l_t = l_t * exp_diff(m_t, m_new) + add;
+        l_t = l_t * exp_diff(m_t, m_new) + tree_sum<VPT * E>(v);
         m_t = m_new;
+      }
+      if (more) {
+#pragma unroll
+        for (int k = 0; k < VPT; ++k) {
+          cur[k] = nxt[k];
+          kcur[k] = knxt[k];
+        }
       }
     }
     // thread summaries -> chunk summary; NaN/inf poisons the chunk
     const bool poisoned = block_any<kWaves>(bad, red);
     float m = m_t, l = l_t;
-    block_merge<kWaves>(m, l, red);
+    block_merge_max_sum<kWaves>(m, l, red);
     if (tid == 0) {
       smx_stat s;
       if (poisoned) {
@@ -107,7 +129,7 @@ __global__ __launch_bounds__(kThreads) void k_stats(RowArgs a, int64_t chunk, in
         s.l = 0.0f;
       } else {
         s.m = m;
-        s.l = l * 5.42101086242752217e-20f;  // remove the 2^64 scale (exact)
+        s.l = l;
       }
       stats[b] = s;
     }
@@ -146,12 +168,12 @@ __global__ __launch_bounds__(kThreads) void k_merge_normalize(RowArgs a, int64_t
       }
     }
     const bool poisoned = block_any<kWaves>(bad, red);
-    block_merge<kWaves>(m, l, red);
+    block_merge_max_sum<kWaves>(m, l, red);
 
     if (poisoned || m == -kInf) {
       Pack<DT, E> p;
       p.fill(poisoned ? Fmt<DT>::kNaN : 0u);
-      for (int64_t j0 = j_lo + (int64_t)tid * E; j0 < j_hi; j0 += (int64_t)kThreads * E) p.store(yr + j0 * S);
+      for (int64_t j0 = j_lo + (int64_t)tid * E; j0 < j_hi; j0 += (int64_t)kThreads * E) p.template store<true>(yr + j0 * S);
       continue;
     }
     const float inv = 1.0f / (l * 18446744073709551616.0f);  // 2^-64 / L
@@ -165,7 +187,7 @@ __global__ __launch_bounds__(kThreads) void k_merge_normalize(RowArgs a, int64_t
         in[k].fill(0);
         kb[k] = ~0ull;
         if (j0 < lim) {
-          in[k].load(xr + j0 * S);
+          in[k].template load<true>(xr + j0 * S);
           if constexpr (KEEP) kb[k] = load_keep<E>(a.mask.keep + row * a.cols + j0);
         }
       }
@@ -182,7 +204,7 @@ __global__ __launch_bounds__(kThreads) void k_merge_normalize(RowArgs a, int64_t
           }
           Pack<DT, E> out;
           out.put(h);
-          out.store(yr + j0 * S);
+          out.template store<true>(yr + j0 * S);
         }
       }
     }
@@ -193,12 +215,13 @@ constexpr int64_t kMaxGrid = 1 << 20;
 
 template <int DT, int E>
 hipError_t launch_stats_t(const RowArgs& a, int64_t chunk, int64_t nch, smx_stat* stats, hipStream_t s) {
+  constexpr int VPT = vpt_stats<DT, E>();
   const int64_t total = a.rows * nch;
   const unsigned grid = (unsigned)(total < kMaxGrid ? total : kMaxGrid);
   if (a.mask.kind == kMaskKeep) {
-    hipLaunchKernelGGL((k_stats<DT, E, true>), dim3(grid), dim3(kThreads), 0, s, a, chunk, nch, stats);
+    hipLaunchKernelGGL((k_stats<DT, E, VPT, true>), dim3(grid), dim3(kThreads), 0, s, a, chunk, nch, stats);
   } else {
-    hipLaunchKernelGGL((k_stats<DT, E, false>), dim3(grid), dim3(kThreads), 0, s, a, chunk, nch, stats);
+    hipLaunchKernelGGL((k_stats<DT, E, VPT, false>), dim3(grid), dim3(kThreads), 0, s, a, chunk, nch, stats);
   }
   return hipGetLastError();
 }
@@ -219,7 +242,7 @@ hipError_t launch_mn_t(const RowArgs& a, int64_t chunk, int64_t nch, const smx_s
 
 int64_t split_round_cols(int dtype, bool vec) {
   if (!vec) return (int64_t)kThreads * kVptScalar;
-  return dtype == kF32 ? (int64_t)kThreads * 16 * 4 : (int64_t)kThreads * 8 * 8;
+  return (int64_t)kThreads * 8 * vec_elems(dtype);
 }
 
 hipError_t launch_stats(const RowArgs& a, int dtype, bool vec, int64_t chunk, int64_t nch, smx_stat* stats,

@@ -8,128 +8,150 @@
 // or 64 contiguous elements (E = 1). Lanes keep a lane-wise running maximum
 // and sum and reduce once per row ("Softmax numerics architecture", pitfall
 // of reducing horizontally inside the loop).
+//
+// Short rows leave a wave with little to do between its load and its store,
+// so a wave takes RPW rows at once: all their loads are in flight together
+// and their reductions interleave.
 #include "smx_device.hpp"
 
 namespace smx {
 namespace {
 
-template <int DT, int E, int VPT, bool KEEP>
+template <int DT, int E, int VPT, int RPW, bool KEEP>
 __global__ __launch_bounds__(kThreads) void k_wave(RowArgs a) {
   constexpr int S = Fmt<DT>::S;
   constexpr bool ACC = DT == kF32;
   const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (row >= a.rows) return;  // wave-uniform
+  const int64_t row0 = ((int64_t)blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) * RPW;
+  if (row0 >= a.rows) return;  // wave-uniform
   const int64_t cols = a.cols;
-  const int64_t prefix = valid_prefix(a.mask, row, cols);
-  const char* xr = a.x + row * cols * S;
-  char* yr = a.y + row * cols * S;
 
-  // load, mask, lane-wise max and the policy flag
-  float v[VPT][E];
-  float mx = -kInf;
-  bool bad = false;
+  // load, mask, lane-wise max and the policy flag, for every row of the wave
+  float v[RPW][VPT][E];
+  float mx[RPW];
+  bool bad[RPW];
+  int64_t prefix[RPW];
 #pragma unroll
-  for (int k = 0; k < VPT; ++k) {
-    const int64_t j0 = (int64_t)(k * 64 + lane) * E;
-    Pack<DT, E> p;
-    p.fill(0);
-    uint64_t kb = ~0ull;
-    const bool ld = j0 < prefix;
-    if (ld) {
-      p.load(xr + j0 * S);
-      if constexpr (KEEP) kb = load_keep<E>(a.mask.keep + row * cols + j0);
-    }
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const bool ok = ld && (j0 + e < prefix) && (!KEEP || keep_lane(kb, e));
-      const float f = ok ? p.get(e) : -kInf;
-      bad |= !(f < kInf);  // NaN or +inf in a valid lane
-      mx = fmaxf(mx, f);
-      v[k][e] = f;
-    }
+  for (int r = 0; r < RPW; ++r) {
+    const int64_t row = row0 + r;
+    prefix[r] = row < a.rows ? valid_prefix(a.mask, row, cols) : 0;
+    mx[r] = -kInf;
+    bad[r] = false;
   }
-  mx = wave_max(mx);
-  const bool poisoned = wave_any(bad);
-
-  if (poisoned || mx == -kInf) {
-    // declared policy rows: canonical NaN, or all +0.0 with no -inf - -inf
-    Pack<DT, E> p;
-    p.fill(poisoned ? Fmt<DT>::kNaN : 0u);
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    const char* xr = a.x + (row0 + r) * cols * S;
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
       const int64_t j0 = (int64_t)(k * 64 + lane) * E;
-      if (j0 < cols) p.store(yr + j0 * S);
-    }
-    return;
-  }
-
-  // exp(x - m) * 2^64 and its sum; masked lanes give exactly 0
-  float total;
-  if constexpr (ACC) {
-    KahanSum ks;
-#pragma unroll
-    for (int k = 0; k < VPT; ++k)
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const float t = exp_acc_b64(v[k][e], mx);
-        v[k][e] = t;
-        ks.add(t);
-      }
-    total = wave_sum_pair(ks.hi(), ks.lo());
-  } else {
-    float s = 0.0f;
-#pragma unroll
-    for (int k = 0; k < VPT; ++k)
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const float t = exp_hw_b64(v[k][e], mx);
-        v[k][e] = t;
-        s += t;
-      }
-    total = wave_sum(s);
-  }
-  const float inv = 1.0f / total;  // 2^-64 / l
-
-#pragma unroll
-  for (int k = 0; k < VPT; ++k) {
-    const int64_t j0 = (int64_t)(k * 64 + lane) * E;
-    if (j0 < cols) {
-      uint32_t h[E];
-#pragma unroll
-      for (int e = 0; e < E; ++e) h[e] = enc<DT>(v[k][e] * inv);
       Pack<DT, E> p;
-      p.put(h);
-      p.store(yr + j0 * S);
+      p.fill(0);
+      uint64_t kb = ~0ull;
+      const bool ld = j0 < prefix[r];
+      if (ld) {
+        p.template load<true>(xr + j0 * S);
+        if constexpr (KEEP) kb = load_keep<E>(a.mask.keep + (row0 + r) * cols + j0);
+      }
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const bool ok = ld && (j0 + e < prefix[r]) && (!KEEP || keep_lane(kb, e));
+        const float f = ok ? p.get(e) : -kInf;
+        bad[r] |= !(f < kInf);  // NaN or +inf in a valid lane
+        mx[r] = fmaxf(mx[r], f);
+        v[r][k][e] = f;
+      }
+    }
+  }
+
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    const int64_t row = row0 + r;
+    if (row >= a.rows) break;  // wave-uniform
+    char* yr = a.y + row * cols * S;
+    const float m = wave_max(mx[r]);
+    const bool poisoned = wave_any(bad[r]);
+    if (poisoned || m == -kInf) {
+      // declared policy rows: canonical NaN, or all +0.0 with no -inf - -inf
+      Pack<DT, E> p;
+      p.fill(poisoned ? Fmt<DT>::kNaN : 0u);
+#pragma unroll
+      for (int k = 0; k < VPT; ++k) {
+        const int64_t j0 = (int64_t)(k * 64 + lane) * E;
+        if (j0 < cols) p.template store<true>(yr + j0 * S);
+      }
+      continue;
+    }
+
+    // exp(x - m) * 2^64 and its sum; masked lanes give exactly 0
+    float total;
+    if constexpr (ACC) {
+      KahanSum ks;
+#pragma unroll
+      for (int k = 0; k < VPT; ++k)
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const float t = exp_acc_b64(v[r][k][e], m);
+          v[r][k][e] = t;
+          ks.add(t);
+        }
+      total = wave_sum_pair(ks.hi(), ks.lo());
+    } else {
+      float s = 0.0f;
+#pragma unroll
+      for (int k = 0; k < VPT; ++k)
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const float t = exp_hw_b64(v[r][k][e], m);
+          v[r][k][e] = t;
+          s += t;
+        }
+      total = wave_sum(s);
+    }
+    const float inv = 1.0f / total;  // 2^-64 / l
+
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      const int64_t j0 = (int64_t)(k * 64 + lane) * E;
+      if (j0 < cols) {
+        uint32_t h[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) h[e] = enc<DT>(v[r][k][e] * inv);
+        Pack<DT, E> p;
+        p.put(h);
+        p.template store<true>(yr + j0 * S);
+      }
     }
   }
 }
 
-template <int DT, int E, int VPT>
+template <int DT, int E, int VPT, int RPW>
 hipError_t launch_vpt(const RowArgs& a, hipStream_t stream) {
-  const int64_t blocks = (a.rows + kWaves - 1) / kWaves;
+  const int64_t rows_per_block = (int64_t)kWaves * RPW;
+  const int64_t blocks = (a.rows + rows_per_block - 1) / rows_per_block;
+  if (blocks > (int64_t)INT32_MAX) return hipErrorInvalidValue;
   if (a.mask.kind == kMaskKeep) {
-    hipLaunchKernelGGL((k_wave<DT, E, VPT, true>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((k_wave<DT, E, VPT, RPW, true>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
   } else {
-    hipLaunchKernelGGL((k_wave<DT, E, VPT, false>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((k_wave<DT, E, VPT, RPW, false>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
   }
   return hipGetLastError();
 }
 
-// the smallest register budget that holds the row
+// the smallest register budget that holds the row; short rows go several to
+// a wave
 template <int DT, int E>
 hipError_t launch_e(const RowArgs& a, hipStream_t stream) {
   const int64_t per_vpt = 64 * E;
   const int64_t need = (a.cols + per_vpt - 1) / per_vpt;
   if constexpr (E == 1) {
-    if (need <= 2) return launch_vpt<DT, E, 2>(a, stream);
-    if (need <= 8) return launch_vpt<DT, E, 8>(a, stream);
-    return launch_vpt<DT, E, 32>(a, stream);
+    if (need <= 2) return launch_vpt<DT, E, 2, 4>(a, stream);
+    if (need <= 8) return launch_vpt<DT, E, 8, 2>(a, stream);
+    return launch_vpt<DT, E, 32, 1>(a, stream);
   } else {
-    if (need <= 1) return launch_vpt<DT, E, 1>(a, stream);
-    if (need <= 2) return launch_vpt<DT, E, 2>(a, stream);
-    if (need <= 4) return launch_vpt<DT, E, 4>(a, stream);
-    return launch_vpt<DT, E, 8>(a, stream);
+    if (need <= 1) return launch_vpt<DT, E, 1, 4>(a, stream);
+    if (need <= 2) return launch_vpt<DT, E, 2, 2>(a, stream);
+    if (need <= 4) return launch_vpt<DT, E, 4, 1>(a, stream);
+    return launch_vpt<DT, E, 8, 1>(a, stream);
   }
 }
 
@@ -138,7 +160,6 @@ hipError_t launch_e(const RowArgs& a, hipStream_t stream) {
 int64_t wave_max_cols(int dtype, bool vec) { return vec ? 64 * 8 * vec_elems(dtype) : 64 * 32; }
 
 hipError_t launch_wave(const RowArgs& a, int dtype, bool vec, hipStream_t stream) {
-  if (a.rows / kWaves >= (int64_t)INT32_MAX) return hipErrorInvalidValue;
   switch (dtype) {
     case kF32:
       return vec ? launch_e<kF32, 4>(a, stream) : launch_e<kF32, 1>(a, stream);

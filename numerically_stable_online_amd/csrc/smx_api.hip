@@ -99,10 +99,11 @@ smx_path choose(int64_t rows, int64_t cols, int dtype, bool vec) {
 }
 
 int64_t default_chunk(int64_t rows, int64_t cols, int dtype, bool vec) {
-  // one register round per workgroup, halved while the grid has fewer than
-  // 2048 workgroups (8 per CU), never below 64 packs
+  // 64 KiB chunks (several register rounds per workgroup, so the stats pass
+  // overlaps its loads with its arithmetic), halved while the grid has fewer
+  // than 2048 workgroups (8 per CU), never below 64 packs
   const int64_t e = vec ? vec_elems(dtype) : 1;
-  int64_t chunk = split_round_cols(dtype, vec);
+  int64_t chunk = 65536 / elem_size(dtype);
   const int64_t floor_chunk = 64 * e;
   while (chunk > floor_chunk && rows * ((cols + chunk - 1) / chunk) < 2048) chunk /= 2;
   return chunk;

@@ -179,13 +179,13 @@ def test_odd_shapes_masks_paths(dtype):
         rows = 13
         x = W.random_rows(rows, cols, dtype, seed=cols, scale=12.0)
         for mask in _masks(rows, cols, rng):
+            banner(f"{dtype} cols={cols} mask={mask.kind}")
             p, cls, st = oracle.softmax_rows(x, dtype, mask)
             for misalign in (False, True):
                 for path in _paths(dtype, cols, misalign):
                     options = [c for c in (1, 5, 64, 200, 4096) if -(-cols // c) <= 512]
                     chunk = 0 if path != "split" else int(rng.choice(options))
                     what = f"{dtype} cols={cols} mask={mask.kind} misalign={misalign} path={path} chunk={chunk}"
-                    banner(what)
                     y = run_rows(x, dtype, mask, path=path, chunk_cols=chunk, misalign=misalign)
                     check(y, dtype, p, cls, st, what)
 
@@ -231,6 +231,24 @@ def test_exact_special_cases(dtype):
     x = W.to_format(np.array([[-np.inf, 7.0, -np.inf, 7.0]]), dtype)
     y = W.to_float(run_rows(x, dtype), dtype)
     assert list(y[0]) == [0.0, 0.5, 0.0, 0.5]
+
+
+def test_f32_exponential_sweep():
+    """Rows [c, c + d, c + d/2, c - 7] with random offsets c (so x - m has a
+    low-order part) and d swept over [-110, 0]: every output probes the fp32
+    exponential, including results that are fp32 subnormals."""
+    rng = np.random.default_rng(5)
+    d = np.concatenate([-rng.uniform(0, 110, 30000), -np.linspace(0, 110, 2001)])
+    c = rng.uniform(-50, 50, d.size)
+    x = np.stack([c, c + d, c + d / 2, c - 7], 1).astype(np.float32)
+    p, cls, st = oracle.softmax_rows(x, "f32")
+    for path, chunk in (("wave", 0), ("lds", 0), ("split", 1), ("split", 2), ("split", 4)):
+        banner(f"exp sweep {path} {chunk}")
+        y = run_rows(x, "f32", path=path, chunk_cols=chunk)
+        r = check(y, "f32", p, cls, st, f"exp sweep/{path}/{chunk}")
+        banner(f"exp sweep {path} {chunk}: {r}")
+    tiny = p[p > 0].min()
+    assert tiny < 2.0 ** -126  # subnormal outputs are exercised
 
 
 # ---------------------------------------------------------------------------
