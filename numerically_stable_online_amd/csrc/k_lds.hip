@@ -17,11 +17,12 @@ namespace {
 constexpr int kPiece = 64 * 16;  // bytes one wave's direct load moves
 constexpr int kAuxNT = 2;        // cache-policy operand: the nontemporal bit
 
-template <int DT, int VPT, bool KEEP>
-__global__ __launch_bounds__(kThreads) void k_lds(RowArgs a) {
+template <int DT, int NT, int VPT, bool KEEP>
+__global__ __launch_bounds__(NT) void k_lds(RowArgs a) {
   constexpr int S = Fmt<DT>::S;
   constexpr int E = 16 / S;
   constexpr bool ACC = DT == kF32;
+  constexpr int NW = NT / 64;
   extern __shared__ __attribute__((aligned(1024))) char row_lds[];
   __shared__ RedScratch red;
   const int tid = threadIdx.x;
@@ -37,7 +38,7 @@ __global__ __launch_bounds__(kThreads) void k_lds(RowArgs a) {
     // stage the valid prefix: wave w copies pieces w, w + 4, ...
     const int64_t nvec = (prefix + E - 1) / E;
     const int64_t npieces = (nvec + 63) / 64;
-    for (int64_t pc = wid; pc < npieces; pc += kWaves) {
+    for (int64_t pc = wid; pc < npieces; pc += NW) {
       const int64_t vi = pc * 64 + lane;
       const int64_t vsrc = vi < nvec ? vi : nvec - 1;  // stays inside the row
       __builtin_amdgcn_global_load_lds(
@@ -52,7 +53,7 @@ __global__ __launch_bounds__(kThreads) void k_lds(RowArgs a) {
     bool bad = false;
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
-      const int64_t vi = (int64_t)k * kThreads + tid;
+      const int64_t vi = (int64_t)k * NT + tid;
       const int64_t j0 = vi * E;
       Pack<DT, E> p;
       p.fill(0);
@@ -75,16 +76,18 @@ __global__ __launch_bounds__(kThreads) void k_lds(RowArgs a) {
         v[k][e] = f;
       }
     }
-    // the reductions' barriers also release the LDS row for the next one
-    mx = block_max<kWaves>(mx, red);
-    const bool poisoned = block_any<kWaves>(bad, red);
+    // the reductions' barriers also release the LDS row for the next one; a
+    // thread that saw NaN or +inf contributes +inf, so the row is poisoned
+    // exactly when its maximum is +inf
+    mx = block_max<NW>(bad ? kInf : mx, red);
+    const bool poisoned = mx == kInf;
 
     if (poisoned || mx == -kInf) {
       Pack<DT, E> p;
       p.fill(poisoned ? Fmt<DT>::kNaN : 0u);
 #pragma unroll
       for (int k = 0; k < VPT; ++k) {
-        const int64_t j0 = ((int64_t)k * kThreads + tid) * E;
+        const int64_t j0 = ((int64_t)k * NT + tid) * E;
         if (j0 < cols) p.template store<true>(yr + j0 * S);
       }
       continue;
@@ -101,7 +104,7 @@ __global__ __launch_bounds__(kThreads) void k_lds(RowArgs a) {
           v[k][e] = t;
           ks.add(t);
         }
-      total = block_sum_pair<kWaves>(ks.hi(), ks.lo(), red);
+      total = block_sum_pair<NW>(ks.hi(), ks.lo(), red);
     } else {
       float s = 0.0f;
 #pragma unroll
@@ -112,13 +115,13 @@ __global__ __launch_bounds__(kThreads) void k_lds(RowArgs a) {
           v[k][e] = t;
           s += t;
         }
-      total = block_sum<kWaves>(s, red);
+      total = block_sum<NW>(s, red);
     }
     const float inv = 1.0f / total;
 
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
-      const int64_t j0 = ((int64_t)k * kThreads + tid) * E;
+      const int64_t j0 = ((int64_t)k * NT + tid) * E;
       if (j0 < cols) {
         uint32_t h[E];
 #pragma unroll
@@ -131,31 +134,32 @@ __global__ __launch_bounds__(kThreads) void k_lds(RowArgs a) {
   }
 }
 
-// rows up to 8 packs per thread: 32 KiB of LDS, 32 (f32) or 64 (16-bit)
-// register-resident values per thread
-constexpr int64_t kMaxRowBytes = (int64_t)kThreads * 8 * 16;
+// rows up to 8 packs per thread of a 256-thread workgroup: 32 KiB of LDS,
+// 32 (f32) or 64 (16-bit) register-resident values per thread
+constexpr int64_t kMaxRowBytes = 256 * 8 * 16;
 
-template <int DT, int VPT>
+template <int DT, int NT, int VPT>
 hipError_t launch_vpt(const RowArgs& a, hipStream_t s) {
   constexpr int S = Fmt<DT>::S;
   const int64_t bytes = ((a.cols * S + kPiece - 1) / kPiece) * kPiece;
   const unsigned grid = (unsigned)(a.rows < (1 << 20) ? a.rows : (1 << 20));
   if (a.mask.kind == kMaskKeep) {
-    hipLaunchKernelGGL((k_lds<DT, VPT, true>), dim3(grid), dim3(kThreads), (size_t)bytes, s, a);
+    hipLaunchKernelGGL((k_lds<DT, NT, VPT, true>), dim3(grid), dim3(NT), (size_t)bytes, s, a);
   } else {
-    hipLaunchKernelGGL((k_lds<DT, VPT, false>), dim3(grid), dim3(kThreads), (size_t)bytes, s, a);
+    hipLaunchKernelGGL((k_lds<DT, NT, VPT, false>), dim3(grid), dim3(NT), (size_t)bytes, s, a);
   }
   return hipGetLastError();
 }
 
+// Four-wave workgroups hold the row in 2, 4 or 8 packs per thread (two-wave
+// and eight-wave shapes measured slower on the 8192 x 4096 bf16 workload).
 template <int DT>
 hipError_t launch_dt(const RowArgs& a, hipStream_t s) {
   constexpr int E = 16 / Fmt<DT>::S;
-  const int64_t per_vpt = (int64_t)kThreads * E;
-  const int64_t need = (a.cols + per_vpt - 1) / per_vpt;
-  if (need <= 2) return launch_vpt<DT, 2>(a, s);
-  if (need <= 4) return launch_vpt<DT, 4>(a, s);
-  return launch_vpt<DT, 8>(a, s);
+  const int64_t packs = (a.cols + E - 1) / E;
+  if (packs <= 256 * 2) return launch_vpt<DT, 256, 2>(a, s);
+  if (packs <= 256 * 4) return launch_vpt<DT, 256, 4>(a, s);
+  return launch_vpt<DT, 256, 8>(a, s);
 }
 
 }  // namespace

@@ -116,9 +116,8 @@ __global__ __launch_bounds__(kThreads) void k_stats(RowArgs a, int64_t chunk, in
       }
     }
     // thread summaries -> chunk summary; NaN/inf poisons the chunk
-    const bool poisoned = block_any<kWaves>(bad, red);
     float m = m_t, l = l_t;
-    block_merge_max_sum<kWaves>(m, l, red);
+    const bool poisoned = block_merge_flagged<kWaves>(m, l, bad, red);
     if (tid == 0) {
       smx_stat s;
       if (poisoned) {
@@ -167,8 +166,7 @@ __global__ __launch_bounds__(kThreads) void k_merge_normalize(RowArgs a, int64_t
         merge_ml(m, l, s.m, s.l);
       }
     }
-    const bool poisoned = block_any<kWaves>(bad, red);
-    block_merge_max_sum<kWaves>(m, l, red);
+    const bool poisoned = block_merge_flagged<kWaves>(m, l, bad, red);
 
     if (poisoned || m == -kInf) {
       Pack<DT, E> p;

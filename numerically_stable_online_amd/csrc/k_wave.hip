@@ -68,8 +68,10 @@ __global__ __launch_bounds__(kThreads) void k_wave(RowArgs a) {
     const int64_t row = row0 + r;
     if (row >= a.rows) break;  // wave-uniform
     char* yr = a.y + row * cols * S;
-    const float m = wave_max(mx[r]);
-    const bool poisoned = wave_any(bad[r]);
+    // a lane that saw NaN or +inf contributes +inf: the row is poisoned
+    // exactly when its maximum is +inf, so one reduction carries both
+    const float m = wave_max(bad[r] ? kInf : mx[r]);
+    const bool poisoned = m == kInf;
     if (poisoned || m == -kInf) {
       // declared policy rows: canonical NaN, or all +0.0 with no -inf - -inf
       Pack<DT, E> p;

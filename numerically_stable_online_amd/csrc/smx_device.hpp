@@ -425,6 +425,18 @@ __device__ __forceinline__ void block_merge_max_sum(float& m, float& l, RedScrat
   m = mm;
 }
 
+// The same merge with the policy flag folded in: a thread that saw NaN or
+// +inf contributes the maximum +inf, so the group is poisoned exactly when M
+// is +inf (and the sum is skipped). Returns whether it is poisoned.
+template <int NW>
+__device__ __forceinline__ bool block_merge_flagged(float& m, float& l, bool bad, RedScratch& s) {
+  const float mm = block_max<NW>(bad ? kInf : m, s);
+  if (mm == kInf) return true;  // uniform across the workgroup
+  l = block_sum_pair<NW>(l * exp_diff(m, mm), 0.0f, s);
+  m = mm;
+  return false;
+}
+
 template <int NW>
 __device__ __forceinline__ void block_merge(float& m, float& l, RedScratch& s) {
   wave_merge(m, l);
