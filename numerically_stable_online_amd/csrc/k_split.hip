@@ -11,10 +11,11 @@
 //
 // Pass 2 (k_merge_normalize): every workgroup of a row merges that row's
 // summaries (the same rule; (-inf, 0) is an identity and a NaN summary
-// poisons the row), then rereads its chunk and writes exp(x - M) / L. The
-// reread is the second HBM read that online softmax does not remove
-// ("Kernel visualization: online softmax", section "Online softmax: two
-// passes").
+// poisons the row), then rereads its chunk and writes exp(x - M) / L. For a
+// row that cannot stay on chip this second read of x is inherent to the
+// online method: no output can be written before the row's sum is final
+// ("Kernel visualization: online softmax", sections "Tiled version" and
+// "Online softmax: two passes").
 #include "smx_device.hpp"
 
 namespace smx {
