@@ -56,6 +56,13 @@
 extern "C" {
 #endif
 
+/* The library exports exactly the functions declared here. */
+#if defined(__GNUC__) || defined(__clang__)
+#define SMX_API __attribute__((visibility("default")))
+#else
+#define SMX_API
+#endif
+
 /* Status codes. */
 #define SMX_OK 0
 #define SMX_EINVAL 1 /* a bad argument; nothing was enqueued            */
@@ -110,7 +117,7 @@ typedef enum {
  * Long rows go through the split path, which takes its summary workspace
  * (rows * ceil(cols / chunk) * 8 bytes) with a stream-ordered allocation and
  * frees it on the same stream. */
-int softmax_rows(const void* x, void* y, int64_t rows, int64_t cols,
+SMX_API int softmax_rows(const void* x, void* y, int64_t rows, int64_t cols,
                  smx_dtype dtype, const smx_mask* valid_len_or_mask,
                  void* stream);
 
@@ -118,19 +125,19 @@ int softmax_rows(const void* x, void* y, int64_t rows, int64_t cols,
  * as softmax_rows does). chunk_cols applies to SMX_PATH_SPLIT (0 = the
  * default). A path that cannot hold the row (WAVE above its register budget,
  * LDS above its LDS budget) is SMX_EINVAL. */
-int softmax_rows_path(const void* x, void* y, int64_t rows, int64_t cols,
+SMX_API int softmax_rows_path(const void* x, void* y, int64_t rows, int64_t cols,
                       smx_dtype dtype, const smx_mask* valid_len_or_mask,
                       smx_path path, int64_t chunk_cols, void* stream);
 
 /* The path softmax_rows takes for a shape (no device access). */
-smx_path softmax_select_path(int64_t rows, int64_t cols, smx_dtype dtype);
+SMX_API smx_path softmax_select_path(int64_t rows, int64_t cols, smx_dtype dtype);
 
 /* softmax_row_stats — per-chunk summaries ("Stable softmax: keep the
  * normalizer consistent as tiles arrive", block-merge paragraph).
  *   chunk_cols: > 0; chunk c covers columns [c*chunk_cols,
  *               min((c+1)*chunk_cols, cols)).
  *   stats: device [rows][n_chunks], n_chunks = ceil(cols / chunk_cols). */
-int softmax_row_stats(const void* x, int64_t rows, int64_t cols,
+SMX_API int softmax_row_stats(const void* x, int64_t rows, int64_t cols,
                       smx_dtype dtype, const smx_mask* valid_len_or_mask,
                       int64_t chunk_cols, smx_stat* stats, void* stream);
 
@@ -142,17 +149,36 @@ int softmax_row_stats(const void* x, int64_t rows, int64_t cols,
  *   stats: device [rows][n_chunks], as written by softmax_row_stats or by the
  *          caller (e.g. summaries exchanged between devices);
  *   n_chunks must equal ceil(cols / chunk_cols). */
-int softmax_merge_normalize(const void* x, void* y, int64_t rows, int64_t cols,
+SMX_API int softmax_merge_normalize(const void* x, void* y, int64_t rows, int64_t cols,
                             smx_dtype dtype, const smx_mask* valid_len_or_mask,
                             int64_t chunk_cols, const smx_stat* stats,
                             int64_t n_chunks, void* stream);
 
+/* log_softmax_rows — log-probabilities and the per-row log-sum-exp
+ * ("Softmax numerics architecture", section on log-sum-exp: LSE = m +
+ * log(sum exp(x - m)), log_softmax = x - LSE; going to log space directly
+ * avoids log(0) of an underflowed probability).
+ *   y  : device [rows, cols] in dtype, y[r, j] = x[r, j] - LSE_r over valid
+ *        finite lanes, -inf on masked and -inf lanes; may be NULL when only
+ *        the LSE is wanted.
+ *   lse: device float [rows], LSE_r in fp32; may be NULL (not both NULL).
+ * Policy: an empty or fully masked row gives LSE = -inf and y = -inf in
+ * every lane; a poisoned row (+inf/NaN in a valid lane) gives the canonical
+ * NaN in lse and in every lane of y. Same paths, alignment rules, errors and
+ * stream semantics as softmax_rows; lse must not overlap x or y. */
+SMX_API int log_softmax_rows(const void* x, void* y, float* lse, int64_t rows, int64_t cols, smx_dtype dtype,
+                     const smx_mask* valid_len_or_mask, void* stream);
+
+/* log_softmax_rows with the kernel path forced, as softmax_rows_path. */
+SMX_API int log_softmax_rows_path(const void* x, void* y, float* lse, int64_t rows, int64_t cols, smx_dtype dtype,
+                          const smx_mask* valid_len_or_mask, smx_path path, int64_t chunk_cols, void* stream);
+
 /* The chunk width softmax_rows uses on the split path (a tuning hint). */
-int64_t softmax_default_chunk_cols(int64_t rows, int64_t cols,
+SMX_API int64_t softmax_default_chunk_cols(int64_t rows, int64_t cols,
                                    smx_dtype dtype);
 
 /* Message for the last nonzero status on this thread ("" if none). */
-const char* smx_last_error(void);
+SMX_API const char* smx_last_error(void);
 
 #ifdef __cplusplus
 }

@@ -10,6 +10,7 @@ Functions keep the C names:
   softmax_rows(x, ...)              -> y
   softmax_row_stats(x, chunk_cols)  -> stats [rows, n_chunks, 2] (m, l)
   softmax_merge_normalize(x, stats, chunk_cols) -> y
+  log_softmax_rows(x, ...)          -> (y, lse)
   softmax_default_chunk_cols(rows, cols, dtype)
   softmax_select_path(rows, cols, dtype)
   smx_last_error()
@@ -73,6 +74,10 @@ def lib() -> C.CDLL:
         L.softmax_row_stats.restype = i32
         L.softmax_merge_normalize.argtypes = [vp, vp, i64, i64, i32, mp, i64, vp, i64, vp]
         L.softmax_merge_normalize.restype = i32
+        L.log_softmax_rows.argtypes = [vp, vp, vp, i64, i64, i32, mp, vp]
+        L.log_softmax_rows.restype = i32
+        L.log_softmax_rows_path.argtypes = [vp, vp, vp, i64, i64, i32, mp, i32, i64, vp]
+        L.log_softmax_rows_path.restype = i32
         L.softmax_default_chunk_cols.argtypes = [i64, i64, i32]
         L.softmax_default_chunk_cols.restype = i64
         L.smx_last_error.argtypes = []
@@ -175,6 +180,34 @@ def softmax_rows(x: torch.Tensor, out: Optional[torch.Tensor] = None, *, valid_l
                                  PATH[path], int(chunk_cols), _stream_handle(stream, x.device))
     _check(rc)
     return y
+
+
+def log_softmax_rows(x: torch.Tensor, out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                     *, want_y: bool = True, want_lse: bool = True, valid_len=None, causal_period=None,
+                     causal_offset: int = 0, keep=None, path: str = "auto", chunk_cols: int = 0, stream=None):
+    """Log-probabilities y = x - LSE and the per-row log-sum-exp (float32 [rows]).
+    Returns (y or None, lse or None)."""
+    rows, cols = _rows_cols(x)
+    if not (want_y or want_lse):
+        raise ValueError("ask for y, lse or both")
+    y = None
+    if want_y:
+        y = torch.empty_like(x) if out is None else out
+        if y.shape != x.shape or y.dtype != x.dtype or not y.is_contiguous():
+            raise ValueError("out must be a contiguous tensor of x's shape and dtype")
+        _on(y, x.device, "out")
+    ls = None
+    if want_lse:
+        ls = torch.empty(rows, dtype=torch.float32, device=x.device) if lse is None else lse
+        if ls.shape != (rows,) or ls.dtype != torch.float32 or not ls.is_contiguous():
+            raise ValueError("lse must be a contiguous float32 tensor [rows]")
+        _on(ls, x.device, "lse")
+    m, keepalive = make_mask(rows, cols, valid_len, causal_period, causal_offset, keep, x.device)
+    rc = lib().log_softmax_rows_path(x.data_ptr(), None if y is None else y.data_ptr(),
+                                     None if ls is None else ls.data_ptr(), rows, cols, _dtype_code(x),
+                                     _mask_arg(m), PATH[path], int(chunk_cols), _stream_handle(stream, x.device))
+    _check(rc)
+    return y, ls
 
 
 def softmax_row_stats(x: torch.Tensor, chunk_cols: int, out: Optional[torch.Tensor] = None, *,

@@ -17,7 +17,7 @@ namespace {
 constexpr int kPiece = 64 * 16;  // bytes one wave's direct load moves
 constexpr int kAuxNT = 2;        // cache-policy operand: the nontemporal bit
 
-template <int DT, int NT, int VPT, bool KEEP>
+template <int DT, int NT, int VPT, bool KEEP, int EPI>
 __global__ __launch_bounds__(NT) void k_lds(RowArgs a) {
   constexpr int S = Fmt<DT>::S;
   constexpr int E = 16 / S;
@@ -83,12 +83,17 @@ __global__ __launch_bounds__(NT) void k_lds(RowArgs a) {
     const bool poisoned = mx == kInf;
 
     if (poisoned || mx == -kInf) {
-      Pack<DT, E> p;
-      p.fill(poisoned ? Fmt<DT>::kNaN : 0u);
+      if constexpr (EPI == kEpiLogSoftmax) {
+        if (tid == 0) write_lse(a.lse, row, poisoned, mx, 0.0f);
+      }
+      if (a.y != nullptr) {
+        Pack<DT, E> p;
+        p.fill(poisoned ? Fmt<DT>::kNaN : (EPI == kEpiSoftmax ? 0u : Fmt<DT>::kNegInf));
 #pragma unroll
-      for (int k = 0; k < VPT; ++k) {
-        const int64_t j0 = ((int64_t)k * NT + tid) * E;
-        if (j0 < cols) p.template store<true>(yr + j0 * S);
+        for (int k = 0; k < VPT; ++k) {
+          const int64_t j0 = ((int64_t)k * NT + tid) * E;
+          if (j0 < cols) p.template store<true>(yr + j0 * S);
+        }
       }
       continue;
     }
@@ -101,7 +106,7 @@ __global__ __launch_bounds__(NT) void k_lds(RowArgs a) {
 #pragma unroll
         for (int e = 0; e < E; ++e) {
           const float t = exp_acc_b64(v[k][e], mx);
-          v[k][e] = t;
+          if constexpr (EPI == kEpiSoftmax) v[k][e] = t;
           ks.add(t);
         }
       total = block_sum_pair<NW>(ks.hi(), ks.lo(), red);
@@ -112,20 +117,28 @@ __global__ __launch_bounds__(NT) void k_lds(RowArgs a) {
 #pragma unroll
         for (int e = 0; e < E; ++e) {
           const float t = exp_hw_b64(v[k][e], mx);
-          v[k][e] = t;
+          if constexpr (EPI == kEpiSoftmax) v[k][e] = t;
           s += t;
         }
       total = block_sum<NW>(s, red);
     }
-    const float inv = 1.0f / total;
 
+    float shift;  // softmax: the reciprocal 2^-64 / l; log-softmax: m + log l
+    if constexpr (EPI == kEpiSoftmax) {
+      shift = 1.0f / total;
+    } else {
+      const float lsum = total * 5.42101086242752217e-20f;  // remove 2^64 (exact)
+      shift = mx + log_l(lsum);
+      if (tid == 0) write_lse(a.lse, row, false, mx, lsum);
+      if (a.y == nullptr) continue;
+    }
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
       const int64_t j0 = ((int64_t)k * NT + tid) * E;
       if (j0 < cols) {
         uint32_t h[E];
 #pragma unroll
-        for (int e = 0; e < E; ++e) h[e] = enc<DT>(v[k][e] * inv);
+        for (int e = 0; e < E; ++e) h[e] = enc<DT>(EPI == kEpiSoftmax ? v[k][e] * shift : v[k][e] - shift);
         Pack<DT, E> p;
         p.put(h);
         p.template store<true>(yr + j0 * S);
@@ -138,43 +151,48 @@ __global__ __launch_bounds__(NT) void k_lds(RowArgs a) {
 // 32 (f32) or 64 (16-bit) register-resident values per thread
 constexpr int64_t kMaxRowBytes = 256 * 8 * 16;
 
-template <int DT, int NT, int VPT>
+template <int DT, int NT, int VPT, int EPI>
 hipError_t launch_vpt(const RowArgs& a, hipStream_t s) {
   constexpr int S = Fmt<DT>::S;
   const int64_t bytes = ((a.cols * S + kPiece - 1) / kPiece) * kPiece;
   const unsigned grid = (unsigned)(a.rows < (1 << 20) ? a.rows : (1 << 20));
   if (a.mask.kind == kMaskKeep) {
-    hipLaunchKernelGGL((k_lds<DT, NT, VPT, true>), dim3(grid), dim3(NT), (size_t)bytes, s, a);
+    hipLaunchKernelGGL((k_lds<DT, NT, VPT, true, EPI>), dim3(grid), dim3(NT), (size_t)bytes, s, a);
   } else {
-    hipLaunchKernelGGL((k_lds<DT, NT, VPT, false>), dim3(grid), dim3(NT), (size_t)bytes, s, a);
+    hipLaunchKernelGGL((k_lds<DT, NT, VPT, false, EPI>), dim3(grid), dim3(NT), (size_t)bytes, s, a);
   }
   return hipGetLastError();
 }
 
 // Four-wave workgroups hold the row in 2, 4 or 8 packs per thread (two-wave
 // and eight-wave shapes measured slower on the 8192 x 4096 bf16 workload).
-template <int DT>
+template <int DT, int EPI>
 hipError_t launch_dt(const RowArgs& a, hipStream_t s) {
   constexpr int E = 16 / Fmt<DT>::S;
   const int64_t packs = (a.cols + E - 1) / E;
-  if (packs <= 256 * 2) return launch_vpt<DT, 256, 2>(a, s);
-  if (packs <= 256 * 4) return launch_vpt<DT, 256, 4>(a, s);
-  return launch_vpt<DT, 256, 8>(a, s);
+  if (packs <= 256 * 2) return launch_vpt<DT, 256, 2, EPI>(a, s);
+  if (packs <= 256 * 4) return launch_vpt<DT, 256, 4, EPI>(a, s);
+  return launch_vpt<DT, 256, 8, EPI>(a, s);
+}
+
+template <int EPI>
+hipError_t launch_epi(const RowArgs& a, int dtype, hipStream_t s) {
+  switch (dtype) {
+    case kF32:
+      return launch_dt<kF32, EPI>(a, s);
+    case kF16:
+      return launch_dt<kF16, EPI>(a, s);
+    default:
+      return launch_dt<kBF16, EPI>(a, s);
+  }
 }
 
 }  // namespace
 
 int64_t lds_max_cols(int dtype) { return kMaxRowBytes / elem_size(dtype); }
 
-hipError_t launch_lds(const RowArgs& a, int dtype, hipStream_t s) {
-  switch (dtype) {
-    case kF32:
-      return launch_dt<kF32>(a, s);
-    case kF16:
-      return launch_dt<kF16>(a, s);
-    default:
-      return launch_dt<kBF16>(a, s);
-  }
+hipError_t launch_lds(const RowArgs& a, int dtype, int epi, hipStream_t s) {
+  return epi == kEpiSoftmax ? launch_epi<kEpiSoftmax>(a, dtype, s) : launch_epi<kEpiLogSoftmax>(a, dtype, s);
 }
 
 }  // namespace smx

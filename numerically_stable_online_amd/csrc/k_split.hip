@@ -136,7 +136,7 @@ __global__ __launch_bounds__(kThreads) void k_stats(RowArgs a, int64_t chunk, in
   }
 }
 
-template <int DT, int E, bool KEEP>
+template <int DT, int E, bool KEEP, int EPI>
 __global__ __launch_bounds__(kThreads) void k_merge_normalize(RowArgs a, int64_t chunk, int64_t nch,
                                                               const smx_stat* stats) {
   constexpr int S = Fmt<DT>::S;
@@ -149,6 +149,8 @@ __global__ __launch_bounds__(kThreads) void k_merge_normalize(RowArgs a, int64_t
   for (int64_t b = blockIdx.x; b < total; b += gridDim.x) {
     const int64_t row = b / nch;
     const int64_t c = b - row * nch;
+    // with no y, only the log-sum-exp is wanted: one workgroup per row
+    if (a.y == nullptr && c != 0) continue;
     const int64_t j_lo = c * chunk;
     const int64_t j_hi = j_lo + chunk < a.cols ? j_lo + chunk : a.cols;
     const int64_t prefix = valid_prefix(a.mask, row, a.cols);
@@ -168,14 +170,19 @@ __global__ __launch_bounds__(kThreads) void k_merge_normalize(RowArgs a, int64_t
       }
     }
     const bool poisoned = block_merge_flagged<kWaves>(m, l, bad, red);
+    if constexpr (EPI == kEpiLogSoftmax) {
+      if (c == 0 && tid == 0) write_lse(a.lse, row, poisoned, poisoned ? kInf : m, l);
+      if (a.y == nullptr) continue;
+    }
 
     if (poisoned || m == -kInf) {
       Pack<DT, E> p;
-      p.fill(poisoned ? Fmt<DT>::kNaN : 0u);
+      p.fill(poisoned ? Fmt<DT>::kNaN : (EPI == kEpiSoftmax ? 0u : Fmt<DT>::kNegInf));
       for (int64_t j0 = j_lo + (int64_t)tid * E; j0 < j_hi; j0 += (int64_t)kThreads * E) p.template store<true>(yr + j0 * S);
       continue;
     }
-    const float inv = 1.0f / (l * 18446744073709551616.0f);  // 2^-64 / L
+    // softmax: the reciprocal 2^-64 / L; log-softmax: M + log L
+    const float shift = EPI == kEpiSoftmax ? 1.0f / (l * 18446744073709551616.0f) : m + log_l(l);
 
     for (int64_t base = j_lo; base < j_hi; base += kRound) {
       Pack<DT, E> in[VPT];
@@ -199,7 +206,7 @@ __global__ __launch_bounds__(kThreads) void k_merge_normalize(RowArgs a, int64_t
           for (int e = 0; e < E; ++e) {
             const bool ok = (j0 + e < lim) && (!KEEP || keep_lane(kb[k], e));
             const float f = ok ? in[k].get(e) : -kInf;
-            h[e] = enc<DT>(exp_b64<ACC>(f, m) * inv);
+            h[e] = enc<DT>(EPI == kEpiSoftmax ? exp_b64<ACC>(f, m) * shift : f - shift);
           }
           Pack<DT, E> out;
           out.put(h);
@@ -225,16 +232,30 @@ hipError_t launch_stats_t(const RowArgs& a, int64_t chunk, int64_t nch, smx_stat
   return hipGetLastError();
 }
 
-template <int DT, int E>
+template <int DT, int E, int EPI>
 hipError_t launch_mn_t(const RowArgs& a, int64_t chunk, int64_t nch, const smx_stat* stats, hipStream_t s) {
   const int64_t total = a.rows * nch;
   const unsigned grid = (unsigned)(total < kMaxGrid ? total : kMaxGrid);
   if (a.mask.kind == kMaskKeep) {
-    hipLaunchKernelGGL((k_merge_normalize<DT, E, true>), dim3(grid), dim3(kThreads), 0, s, a, chunk, nch, stats);
+    hipLaunchKernelGGL((k_merge_normalize<DT, E, true, EPI>), dim3(grid), dim3(kThreads), 0, s, a, chunk, nch, stats);
   } else {
-    hipLaunchKernelGGL((k_merge_normalize<DT, E, false>), dim3(grid), dim3(kThreads), 0, s, a, chunk, nch, stats);
+    hipLaunchKernelGGL((k_merge_normalize<DT, E, false, EPI>), dim3(grid), dim3(kThreads), 0, s, a, chunk, nch, stats);
   }
   return hipGetLastError();
+}
+
+template <int EPI>
+hipError_t launch_mn_epi(const RowArgs& a, int dtype, bool vec, int64_t chunk, int64_t nch, const smx_stat* stats,
+                         hipStream_t s) {
+  switch (dtype) {
+    case kF32:
+      return vec ? launch_mn_t<kF32, 4, EPI>(a, chunk, nch, stats, s) : launch_mn_t<kF32, 1, EPI>(a, chunk, nch, stats, s);
+    case kF16:
+      return vec ? launch_mn_t<kF16, 8, EPI>(a, chunk, nch, stats, s) : launch_mn_t<kF16, 1, EPI>(a, chunk, nch, stats, s);
+    default:
+      return vec ? launch_mn_t<kBF16, 8, EPI>(a, chunk, nch, stats, s)
+                 : launch_mn_t<kBF16, 1, EPI>(a, chunk, nch, stats, s);
+  }
 }
 
 }  // namespace
@@ -257,16 +278,10 @@ hipError_t launch_stats(const RowArgs& a, int dtype, bool vec, int64_t chunk, in
   }
 }
 
-hipError_t launch_merge_normalize(const RowArgs& a, int dtype, bool vec, int64_t chunk, int64_t nch,
+hipError_t launch_merge_normalize(const RowArgs& a, int dtype, bool vec, int epi, int64_t chunk, int64_t nch,
                                   const smx_stat* stats, hipStream_t s) {
-  switch (dtype) {
-    case kF32:
-      return vec ? launch_mn_t<kF32, 4>(a, chunk, nch, stats, s) : launch_mn_t<kF32, 1>(a, chunk, nch, stats, s);
-    case kF16:
-      return vec ? launch_mn_t<kF16, 8>(a, chunk, nch, stats, s) : launch_mn_t<kF16, 1>(a, chunk, nch, stats, s);
-    default:
-      return vec ? launch_mn_t<kBF16, 8>(a, chunk, nch, stats, s) : launch_mn_t<kBF16, 1>(a, chunk, nch, stats, s);
-  }
+  return epi == kEpiSoftmax ? launch_mn_epi<kEpiSoftmax>(a, dtype, vec, chunk, nch, stats, s)
+                            : launch_mn_epi<kEpiLogSoftmax>(a, dtype, vec, chunk, nch, stats, s);
 }
 
 }  // namespace smx

@@ -17,7 +17,7 @@
 namespace smx {
 namespace {
 
-template <int DT, int E, int VPT, int RPW, bool KEEP>
+template <int DT, int E, int VPT, int RPW, bool KEEP, int EPI>
 __global__ __launch_bounds__(kThreads) void k_wave(RowArgs a) {
   constexpr int S = Fmt<DT>::S;
   constexpr bool ACC = DT == kF32;
@@ -73,18 +73,25 @@ __global__ __launch_bounds__(kThreads) void k_wave(RowArgs a) {
     const float m = wave_max(bad[r] ? kInf : mx[r]);
     const bool poisoned = m == kInf;
     if (poisoned || m == -kInf) {
-      // declared policy rows: canonical NaN, or all +0.0 with no -inf - -inf
-      Pack<DT, E> p;
-      p.fill(poisoned ? Fmt<DT>::kNaN : 0u);
+      // declared policy rows: canonical NaN, or the empty row (all +0.0, or
+      // all -inf for log-probabilities) with no -inf - -inf
+      if constexpr (EPI == kEpiLogSoftmax) {
+        if (lane == 0) write_lse(a.lse, row, poisoned, m, 0.0f);
+      }
+      if (a.y != nullptr) {
+        Pack<DT, E> p;
+        p.fill(poisoned ? Fmt<DT>::kNaN : (EPI == kEpiSoftmax ? 0u : Fmt<DT>::kNegInf));
 #pragma unroll
-      for (int k = 0; k < VPT; ++k) {
-        const int64_t j0 = (int64_t)(k * 64 + lane) * E;
-        if (j0 < cols) p.template store<true>(yr + j0 * S);
+        for (int k = 0; k < VPT; ++k) {
+          const int64_t j0 = (int64_t)(k * 64 + lane) * E;
+          if (j0 < cols) p.template store<true>(yr + j0 * S);
+        }
       }
       continue;
     }
 
-    // exp(x - m) * 2^64 and its sum; masked lanes give exactly 0
+    // exp(x - m) * 2^64 and its sum; masked lanes give exactly 0. The
+    // softmax keeps the exponentials for its stores; log-softmax only sums.
     float total;
     if constexpr (ACC) {
       KahanSum ks;
@@ -93,7 +100,7 @@ __global__ __launch_bounds__(kThreads) void k_wave(RowArgs a) {
 #pragma unroll
         for (int e = 0; e < E; ++e) {
           const float t = exp_acc_b64(v[r][k][e], m);
-          v[r][k][e] = t;
+          if constexpr (EPI == kEpiSoftmax) v[r][k][e] = t;
           ks.add(t);
         }
       total = wave_sum_pair(ks.hi(), ks.lo());
@@ -104,56 +111,89 @@ __global__ __launch_bounds__(kThreads) void k_wave(RowArgs a) {
 #pragma unroll
         for (int e = 0; e < E; ++e) {
           const float t = exp_hw_b64(v[r][k][e], m);
-          v[r][k][e] = t;
+          if constexpr (EPI == kEpiSoftmax) v[r][k][e] = t;
           s += t;
         }
       total = wave_sum(s);
     }
-    const float inv = 1.0f / total;  // 2^-64 / l
 
+    if constexpr (EPI == kEpiSoftmax) {
+      const float inv = 1.0f / total;  // 2^-64 / l
 #pragma unroll
-    for (int k = 0; k < VPT; ++k) {
-      const int64_t j0 = (int64_t)(k * 64 + lane) * E;
-      if (j0 < cols) {
-        uint32_t h[E];
+      for (int k = 0; k < VPT; ++k) {
+        const int64_t j0 = (int64_t)(k * 64 + lane) * E;
+        if (j0 < cols) {
+          uint32_t h[E];
 #pragma unroll
-        for (int e = 0; e < E; ++e) h[e] = enc<DT>(v[r][k][e] * inv);
-        Pack<DT, E> p;
-        p.put(h);
-        p.template store<true>(yr + j0 * S);
+          for (int e = 0; e < E; ++e) h[e] = enc<DT>(v[r][k][e] * inv);
+          Pack<DT, E> p;
+          p.put(h);
+          p.template store<true>(yr + j0 * S);
+        }
+      }
+    } else {
+      // log-softmax: y = x - (m + log l); masked and -inf lanes stay -inf
+      const float lsum = total * 5.42101086242752217e-20f;  // remove 2^64 (exact)
+      const float lse = m + log_l(lsum);
+      if (lane == 0) write_lse(a.lse, row, false, m, lsum);
+      if (a.y != nullptr) {
+#pragma unroll
+        for (int k = 0; k < VPT; ++k) {
+          const int64_t j0 = (int64_t)(k * 64 + lane) * E;
+          if (j0 < cols) {
+            uint32_t h[E];
+#pragma unroll
+            for (int e = 0; e < E; ++e) h[e] = enc<DT>(v[r][k][e] - lse);
+            Pack<DT, E> p;
+            p.put(h);
+            p.template store<true>(yr + j0 * S);
+          }
+        }
       }
     }
   }
 }
 
-template <int DT, int E, int VPT, int RPW>
+template <int DT, int E, int VPT, int RPW, int EPI>
 hipError_t launch_vpt(const RowArgs& a, hipStream_t stream) {
   const int64_t rows_per_block = (int64_t)kWaves * RPW;
   const int64_t blocks = (a.rows + rows_per_block - 1) / rows_per_block;
   if (blocks > (int64_t)INT32_MAX) return hipErrorInvalidValue;
   if (a.mask.kind == kMaskKeep) {
-    hipLaunchKernelGGL((k_wave<DT, E, VPT, RPW, true>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((k_wave<DT, E, VPT, RPW, true, EPI>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
   } else {
-    hipLaunchKernelGGL((k_wave<DT, E, VPT, RPW, false>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((k_wave<DT, E, VPT, RPW, false, EPI>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
   }
   return hipGetLastError();
 }
 
 // the smallest register budget that holds the row; short rows go several to
 // a wave
-template <int DT, int E>
+template <int DT, int E, int EPI>
 hipError_t launch_e(const RowArgs& a, hipStream_t stream) {
   const int64_t per_vpt = 64 * E;
   const int64_t need = (a.cols + per_vpt - 1) / per_vpt;
   if constexpr (E == 1) {
-    if (need <= 2) return launch_vpt<DT, E, 2, 4>(a, stream);
-    if (need <= 8) return launch_vpt<DT, E, 8, 2>(a, stream);
-    return launch_vpt<DT, E, 32, 1>(a, stream);
+    if (need <= 2) return launch_vpt<DT, E, 2, 4, EPI>(a, stream);
+    if (need <= 8) return launch_vpt<DT, E, 8, 2, EPI>(a, stream);
+    return launch_vpt<DT, E, 32, 1, EPI>(a, stream);
   } else {
-    if (need <= 1) return launch_vpt<DT, E, 1, 4>(a, stream);
-    if (need <= 2) return launch_vpt<DT, E, 2, 2>(a, stream);
-    if (need <= 4) return launch_vpt<DT, E, 4, 1>(a, stream);
-    return launch_vpt<DT, E, 8, 1>(a, stream);
+    if (need <= 1) return launch_vpt<DT, E, 1, 4, EPI>(a, stream);
+    if (need <= 2) return launch_vpt<DT, E, 2, 2, EPI>(a, stream);
+    if (need <= 4) return launch_vpt<DT, E, 4, 1, EPI>(a, stream);
+    return launch_vpt<DT, E, 8, 1, EPI>(a, stream);
+  }
+}
+
+template <int EPI>
+hipError_t launch_epi(const RowArgs& a, int dtype, bool vec, hipStream_t stream) {
+  switch (dtype) {
+    case kF32:
+      return vec ? launch_e<kF32, 4, EPI>(a, stream) : launch_e<kF32, 1, EPI>(a, stream);
+    case kF16:
+      return vec ? launch_e<kF16, 8, EPI>(a, stream) : launch_e<kF16, 1, EPI>(a, stream);
+    default:
+      return vec ? launch_e<kBF16, 8, EPI>(a, stream) : launch_e<kBF16, 1, EPI>(a, stream);
   }
 }
 
@@ -161,15 +201,9 @@ hipError_t launch_e(const RowArgs& a, hipStream_t stream) {
 
 int64_t wave_max_cols(int dtype, bool vec) { return vec ? 64 * 8 * vec_elems(dtype) : 64 * 32; }
 
-hipError_t launch_wave(const RowArgs& a, int dtype, bool vec, hipStream_t stream) {
-  switch (dtype) {
-    case kF32:
-      return vec ? launch_e<kF32, 4>(a, stream) : launch_e<kF32, 1>(a, stream);
-    case kF16:
-      return vec ? launch_e<kF16, 8>(a, stream) : launch_e<kF16, 1>(a, stream);
-    default:
-      return vec ? launch_e<kBF16, 8>(a, stream) : launch_e<kBF16, 1>(a, stream);
-  }
+hipError_t launch_wave(const RowArgs& a, int dtype, bool vec, int epi, hipStream_t stream) {
+  return epi == kEpiSoftmax ? launch_epi<kEpiSoftmax>(a, dtype, vec, stream)
+                            : launch_epi<kEpiLogSoftmax>(a, dtype, vec, stream);
 }
 
 }  // namespace smx

@@ -109,7 +109,7 @@ int64_t default_chunk(int64_t rows, int64_t cols, int dtype, bool vec) {
   return chunk;
 }
 
-int run_split(const Call& c, int64_t chunk, hipStream_t stream) {
+int run_split(const Call& c, int64_t chunk, int epi, hipStream_t stream) {
   const int64_t e = vec_elems(c.dtype);
   const bool vec = c.vec && chunk % e == 0;
   const int64_t nch = (c.a.cols + chunk - 1) / chunk;
@@ -118,14 +118,14 @@ int run_split(const Call& c, int64_t chunk, hipStream_t stream) {
   hipError_t err = hipMallocAsync(&ws, bytes, stream);
   if (err != hipSuccess) return hip_fail(err, "hipMallocAsync of the summary workspace");
   err = launch_stats(c.a, c.dtype, vec, chunk, nch, (smx_stat*)ws, stream);
-  if (err == hipSuccess) err = launch_merge_normalize(c.a, c.dtype, vec, chunk, nch, (const smx_stat*)ws, stream);
+  if (err == hipSuccess) err = launch_merge_normalize(c.a, c.dtype, vec, epi, chunk, nch, (const smx_stat*)ws, stream);
   const hipError_t ferr = hipFreeAsync(ws, stream);
   if (err != hipSuccess) return hip_fail(err, "split-path launch");
   if (ferr != hipSuccess) return hip_fail(ferr, "hipFreeAsync of the summary workspace");
   return ok();
 }
 
-int run_rows(const Call& c, smx_path path, int64_t chunk_cols, hipStream_t stream) {
+int run_rows(const Call& c, smx_path path, int64_t chunk_cols, int epi, hipStream_t stream) {
   const int64_t rows = c.a.rows, cols = c.a.cols;
   if (path == SMX_PATH_AUTO) path = choose(rows, cols, c.dtype, c.vec);
   hipError_t err = hipSuccess;
@@ -134,7 +134,7 @@ int run_rows(const Call& c, smx_path path, int64_t chunk_cols, hipStream_t strea
       if (cols > wave_max_cols(c.dtype, c.vec))
         return fail(SMX_EINVAL, "the wave path holds at most %lld cols for this dtype/alignment",
                     (long long)wave_max_cols(c.dtype, c.vec));
-      err = launch_wave(c.a, c.dtype, c.vec, stream);
+      err = launch_wave(c.a, c.dtype, c.vec, epi, stream);
       break;
     case SMX_PATH_LDS:
       if (!c.vec)
@@ -142,12 +142,12 @@ int run_rows(const Call& c, smx_path path, int64_t chunk_cols, hipStream_t strea
       if (cols > lds_max_cols(c.dtype))
         return fail(SMX_EINVAL, "the LDS path holds at most %lld cols for this dtype",
                     (long long)lds_max_cols(c.dtype));
-      err = launch_lds(c.a, c.dtype, stream);
+      err = launch_lds(c.a, c.dtype, epi, stream);
       break;
     case SMX_PATH_SPLIT: {
       if (chunk_cols < 0) return fail(SMX_EINVAL, "chunk_cols must be >= 0");
       const int64_t chunk = chunk_cols > 0 ? chunk_cols : default_chunk(rows, cols, c.dtype, c.vec);
-      return run_split(c, chunk, stream);
+      return run_split(c, chunk, epi, stream);
     }
     default:
       return fail(SMX_EINVAL, "path %d is not a smx_path", (int)path);
@@ -170,7 +170,7 @@ int softmax_rows_path(const void* x, void* y, int64_t rows, int64_t cols, smx_dt
   if ((int)path < SMX_PATH_AUTO || (int)path > SMX_PATH_SPLIT) return fail(SMX_EINVAL, "path %d is not a smx_path", (int)path);
   if (chunk_cols < 0) return fail(SMX_EINVAL, "chunk_cols must be >= 0");
   if (rows == 0 || cols == 0) return ok();
-  return run_rows(c, path, chunk_cols, (hipStream_t)stream);
+  return run_rows(c, path, chunk_cols, kEpiSoftmax, (hipStream_t)stream);
 }
 
 int softmax_rows(const void* x, void* y, int64_t rows, int64_t cols, smx_dtype dtype, const smx_mask* mask,
@@ -216,9 +216,41 @@ int softmax_merge_normalize(const void* x, void* y, int64_t rows, int64_t cols, 
   if (rows > 0 && nch > 0 && stats == nullptr) return fail(SMX_EINVAL, "stats is NULL");
   if (rows == 0 || cols == 0) return ok();
   const bool vec = c.vec && chunk_cols % vec_elems(c.dtype) == 0;
-  hipError_t err = launch_merge_normalize(c.a, c.dtype, vec, chunk_cols, nch, stats, (hipStream_t)stream);
+  hipError_t err = launch_merge_normalize(c.a, c.dtype, vec, kEpiSoftmax, chunk_cols, nch, stats, (hipStream_t)stream);
   if (err != hipSuccess) return hip_fail(err, "merge/normalize launch");
   return ok();
+}
+
+int log_softmax_rows_path(const void* x, void* y, float* lse, int64_t rows, int64_t cols, smx_dtype dtype,
+                          const smx_mask* mask, smx_path path, int64_t chunk_cols, void* stream) {
+  Call c;
+  if (int rc = check_common(x, y, rows, cols, (int)dtype, mask, y != nullptr, c)) return rc;
+  if ((int)path < SMX_PATH_AUTO || (int)path > SMX_PATH_SPLIT) return fail(SMX_EINVAL, "path %d is not a smx_path", (int)path);
+  if (chunk_cols < 0) return fail(SMX_EINVAL, "chunk_cols must be >= 0");
+  if (y == nullptr && lse == nullptr && rows > 0 && cols > 0) return fail(SMX_EINVAL, "y and lse are both NULL");
+  if (lse != nullptr && rows > 0) {
+    const uintptr_t la = (uintptr_t)lse, lb = (uintptr_t)(rows * 4);
+    const uintptr_t xb = (uintptr_t)(rows * cols * elem_size((int)dtype));
+    const uintptr_t xa = (uintptr_t)x, ya = (uintptr_t)y;
+    if (xb > 0 && ((la < xa + xb && xa < la + lb) || (y != nullptr && la < ya + xb && ya < la + lb)))
+      return fail(SMX_EINVAL, "lse overlaps x or y");
+  }
+  c.a.lse = lse;
+  if (rows == 0) return ok();
+  if (cols == 0) {
+    // every row is empty: lse = -inf (nothing else to write)
+    if (lse == nullptr) return ok();
+    c.a.cols = 0;
+    hipError_t err = launch_wave(c.a, c.dtype, false, kEpiLogSoftmax, (hipStream_t)stream);
+    if (err != hipSuccess) return hip_fail(err, "kernel launch");
+    return ok();
+  }
+  return run_rows(c, path, chunk_cols, kEpiLogSoftmax, (hipStream_t)stream);
+}
+
+int log_softmax_rows(const void* x, void* y, float* lse, int64_t rows, int64_t cols, smx_dtype dtype,
+                     const smx_mask* mask, void* stream) {
+  return log_softmax_rows_path(x, y, lse, rows, cols, dtype, mask, SMX_PATH_AUTO, 0, stream);
 }
 
 const char* smx_last_error(void) { return g_err; }

@@ -22,6 +22,7 @@ template <int DT>
 struct Fmt {
   static constexpr int S = DT == kF32 ? 4 : 2;  // bytes per element
   static constexpr uint32_t kNaN = DT == kF32 ? 0x7FC00000u : (DT == kF16 ? 0x7E00u : 0x7FC0u);
+  static constexpr uint32_t kNegInf = DT == kF32 ? 0xFF800000u : (DT == kF16 ? 0xFC00u : 0xFF80u);
 };
 
 // Exact widening of one element's bits to fp32.
@@ -36,8 +37,9 @@ __device__ __forceinline__ float dec(uint32_t h) {
   }
 }
 
-// Nearest-even rounding of a finite non-negative fp32 value to the element
-// format, gradual underflow kept.
+// Nearest-even rounding of an fp32 value (finite or -inf; non-negative for
+// probabilities, non-positive for log-probabilities) to the element format,
+// gradual underflow kept; fp16 overflows to -inf as IEEE rounding does.
 template <int DT>
 __device__ __forceinline__ uint32_t enc(float f) {
   if constexpr (DT == kF32) {
@@ -225,6 +227,24 @@ __device__ __forceinline__ float exp_b64(float x, float m) {
   } else {
     return exp_hw_b64(x, m);
   }
+}
+
+// log(l) for the log-sum-exp (l >= 1): the library's correctly handled
+// natural logarithm (an accurate expansion of v_log_f32, not the fast one).
+__device__ __forceinline__ float log_l(float l) { return __builtin_logf(l); }
+
+// The epilogue's per-row scalar for the log-softmax outputs.
+__device__ __forceinline__ void write_lse(float* lse, int64_t row, bool poisoned, float m, float lsum) {
+  if (lse == nullptr) return;
+  float v;
+  if (poisoned) {
+    v = u2f(0x7FC00000u);
+  } else if (m == -kInf) {
+    v = -kInf;
+  } else {
+    v = m + log_l(lsum);
+  }
+  lse[row] = v;
 }
 
 // ---------------------------------------------------------------------------

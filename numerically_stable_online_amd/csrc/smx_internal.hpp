@@ -32,11 +32,16 @@ struct MaskArgs {
 
 struct RowArgs {
   const char* x;
-  char* y;
+  char* y;       // may be null for the log-sum-exp-only epilogue
+  float* lse;    // per-row log-sum-exp, or null
   int64_t rows;
   int64_t cols;
   MaskArgs mask;
 };
+
+// What the kernels write once a row's (m, l) is known.
+constexpr int kEpiSoftmax = 0;     // y = exp(x - m) / l
+constexpr int kEpiLogSoftmax = 1;  // y = x - (m + log l), and/or lse = m + log l
 
 inline int elem_size(int dtype) { return dtype == kF32 ? 4 : 2; }
 // elements per 128-bit access
@@ -45,18 +50,18 @@ inline int vec_elems(int dtype) { return 16 / elem_size(dtype); }
 // --- wave-per-row kernel (k_wave.hip) ---
 // Largest cols the wave path holds in registers.
 int64_t wave_max_cols(int dtype, bool vec);
-hipError_t launch_wave(const RowArgs& a, int dtype, bool vec, hipStream_t stream);
+hipError_t launch_wave(const RowArgs& a, int dtype, bool vec, int epi, hipStream_t stream);
 
 // --- workgroup-per-row, LDS-staged kernel (k_lds.hip) ---
 int64_t lds_max_cols(int dtype);
-hipError_t launch_lds(const RowArgs& a, int dtype, hipStream_t stream);
+hipError_t launch_lds(const RowArgs& a, int dtype, int epi, hipStream_t stream);
 
 // --- split path (k_split.hip) ---
 // Elements one workgroup holds per round of a chunk.
 int64_t split_round_cols(int dtype, bool vec);
 hipError_t launch_stats(const RowArgs& a, int dtype, bool vec, int64_t chunk_cols, int64_t n_chunks,
                         smx_stat* stats, hipStream_t stream);
-hipError_t launch_merge_normalize(const RowArgs& a, int dtype, bool vec, int64_t chunk_cols,
+hipError_t launch_merge_normalize(const RowArgs& a, int dtype, bool vec, int epi, int64_t chunk_cols,
                                   int64_t n_chunks, const smx_stat* stats, hipStream_t stream);
 
 }  // namespace smx

@@ -81,3 +81,67 @@ def check(y_raw: np.ndarray, dtype: str, p: np.ndarray, cls: np.ndarray, st: np.
         out["max_ulp"] = worst
         out["frac_off_by_one"] = float(np.count_nonzero(d[num])) / max(1, int(num.sum()))
     return out
+
+
+# ---------------------------------------------------------------------------
+# Log-domain outputs (log-softmax and the per-row log-sum-exp)
+# ---------------------------------------------------------------------------
+#
+# The references are the oracle's double-precision x - LSE and LSE. The GPU
+# forms LSE = m + log(l) and x - LSE in fp32, so near-cancelling lanes carry
+# the fp32 resolution of the operands:
+#   f32     : |y - r| <= 1e-6 * max(1, |x|, |LSE|)
+#   f16/bf16: within 1 ulp of the rounded reference, or
+#             |y - r| <= 2^-22 * max(1, |x|, |LSE|)
+#   LSE     : |lse - LSE| <= 1e-6 * max(1, |LSE|)
+# Policy lanes are bit-exact: masked / -inf lanes and empty rows -inf, NaN
+# rows the canonical NaN (and NaN / -inf in lse).
+
+LOG_F32_TOL = 1e-6
+LOG_16_ABS = 2.0 ** -22
+NEG_INF_BITS = {"f32": 0xFF800000, "f16": 0xFC00, "bf16": 0xFF80}
+
+
+def check_log(y_raw, dtype, logp, lse_ref, lse_got, cls, st, x_float, what=""):
+    out = {}
+    if lse_got is not None:
+        ok_rows = st == oracle.ROW_OK
+        g = lse_got.astype(np.float64)
+        assert np.array_equal(np.isnan(g), st == oracle.ROW_POISON), f"{what}: lse NaN rows differ"
+        assert (lse_got[st == oracle.ROW_POISON].view(np.uint32) == 0x7FC00000).all(), f"{what}: lse NaN bits"
+        assert (g[st == oracle.ROW_EMPTY] == -np.inf).all(), f"{what}: empty rows need lse = -inf"
+        if ok_rows.any():
+            err = np.abs(g[ok_rows] - lse_ref[ok_rows]) / np.maximum(1.0, np.abs(lse_ref[ok_rows]))
+            assert err.max() <= LOG_F32_TOL, f"{what}: lse error {err.max():.3e}"
+            out["lse_max_err"] = float(err.max())
+    if y_raw is None:
+        return out
+    bits = bits_of(y_raw, dtype)
+    zero = cls == oracle.LANE_ZERO
+    nan = cls == oracle.LANE_NAN
+    num = cls == oracle.LANE_NUMERIC
+    assert (bits[zero] == NEG_INF_BITS[dtype]).all(), f"{what}: masked lanes must be -inf"
+    assert (bits[nan] == NAN_BITS[dtype]).all(), f"{what}: NaN rows must be the canonical NaN"
+    lse_b = np.broadcast_to(np.where(st == oracle.ROW_OK, lse_ref, 0.0)[:, None], logp.shape)
+    scale = np.maximum(1.0, np.maximum(np.abs(x_float.astype(np.float64)), np.abs(lse_b)))
+    y = y_raw.astype(np.float64) if dtype == "f32" else \
+        (y_raw.view(np.float16).astype(np.float64) if dtype == "f16"
+         else (y_raw.astype(np.uint32) << 16).view(np.float32).astype(np.float64))
+    err = np.zeros_like(logp)
+    err[num] = np.abs(y[num] - logp[num]) / scale[num]
+    if dtype == "f32":
+        worst = float(err.max()) if err.size else 0.0
+        if worst > LOG_F32_TOL:
+            i = np.unravel_index(np.argmax(err), err.shape)
+            raise AssertionError(f"{what}: log error {worst:.3e} at {i}: got {y[i]!r} want {logp[i]!r}")
+        out["max_err"] = worst
+    else:
+        want = oracle.encode(np.where(num, logp, 0.0), dtype).astype(np.int64)
+        d = np.abs(bits - want)
+        bad = num & (d > ULP_TOL) & (err > LOG_16_ABS)
+        if bad.any():
+            i = np.argwhere(bad)[0]
+            i = tuple(i)
+            raise AssertionError(f"{what}: {d[i]} ulp at {i}: got {bits[i]:#06x} want {want[i]:#06x} (ref {logp[i]!r})")
+        out["max_ulp"] = int(d[num].max()) if num.any() else 0
+    return out

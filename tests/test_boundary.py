@@ -29,12 +29,13 @@ def smx():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_][a-z_0-9]*)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:SMX_API\s+)?(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_][a-z_0-9]*)\s*\(", text, flags=re.M)))
 
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("softmax_rows", "softmax_rows_path", "softmax_row_stats", "softmax_merge_normalize",
+              "log_softmax_rows", "log_softmax_rows_path",
               "softmax_default_chunk_cols", "softmax_select_path", "smx_last_error"):
         assert n in names, names
 
@@ -45,6 +46,8 @@ def test_library_exports_every_declared_symbol(smx):
     exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
     missing = [n for n in declared_functions() if n not in exported]
     assert not missing, missing
+    extra = sorted(exported - set(declared_functions()))
+    assert not extra, f"exported but not declared: {extra}"
     lib = smx.lib()
     for n in declared_functions():
         assert getattr(lib, n) is not None

@@ -364,3 +364,90 @@ def test_invalid_arguments_raise():
         smx.softmax_rows(torch.zeros(2, 5000, device="cuda"), path="wave")  # too long for registers
     with pytest.raises(smx.SmxError):
         smx.softmax_merge_normalize(x, torch.zeros(4, 3, 2, device="cuda"), 4)  # wrong n_chunks
+
+
+# ---------------------------------------------------------------------------
+# Log-softmax and log-sum-exp
+# ---------------------------------------------------------------------------
+
+from smx_compare import check_log  # noqa: E402
+
+
+def run_log(x_raw, dtype, mask=None, path="auto", chunk_cols=0, want_y=True, misalign=False):
+    rows, cols = x_raw.shape
+    if misalign:
+        buf = torch.empty(rows * cols + 1, dtype=TORCH_DTYPE[dtype], device="cuda")
+        x = buf[1:].view(rows, cols)
+        x.copy_(to_device(x_raw, dtype))
+        ybuf = torch.empty(rows * cols + 1, dtype=TORCH_DTYPE[dtype], device="cuda")
+        y = ybuf[1:].view(rows, cols)
+    else:
+        x = to_device(x_raw, dtype)
+        y = torch.empty_like(x)
+    y, lse = smx.log_softmax_rows(x, y if want_y else None, want_y=want_y, path=path, chunk_cols=chunk_cols,
+                                  **mask_kwargs(mask))
+    torch.cuda.synchronize()
+    return (to_host(y, dtype) if want_y else None), lse.cpu().numpy()
+
+
+def check_log_full(x_raw, dtype, mask, y, lse, what, r0=0, r1=None):
+    r1 = x_raw.shape[0] if r1 is None else r1
+    lse_ref, logp = oracle.log_softmax_rows(x_raw, dtype, mask, r0, r1)
+    _, cls, st = oracle.softmax_rows(x_raw, dtype, mask, r0, r1)
+    xf = W.to_float(x_raw[r0:r1], dtype)
+    return check_log(None if y is None else y[r0:r1], dtype, logp, lse_ref, lse[r0:r1], cls, st, xf, what)
+
+
+@pytest.mark.parametrize("cfg,path", [(1, "auto"), (1, "wave"), (1, "lds"), (1, "split"), (2, "auto"),
+                                      (2, "split"), (3, "auto"), (3, "split"), (4, "auto")])
+def test_log_softmax_workloads(cfg, path):
+    w = W.CONFIGS[cfg]()
+    banner(f"log config{cfg} {path}")
+    y, lse = run_log(w.x, w.dtype, w.mask, path=path)
+    r = check_log_full(w.x, w.dtype, w.mask, y, lse, f"log config{cfg}/{path}")
+    banner(f"log config{cfg} {path}: {r}")
+    _, lse_only = run_log(w.x, w.dtype, w.mask, path=path, want_y=False)
+    assert np.array_equal(lse_only.view(np.uint32), lse.view(np.uint32))  # LSE-only: the same bits
+
+
+@pytest.mark.timeout(600)
+def test_log_softmax_config5():
+    banner("log config5 generate")
+    w = W.config5()
+    banner("log config5 run")
+    y, lse = run_log(w.x, "bf16", w.mask)
+    n = 2048
+    groups = list(range(0, 256, 8))
+    for g in groups:
+        check_log_full(w.x, "bf16", w.mask, y, lse, f"log config5/group{g}", g * n, (g + 1) * n)
+    nanrows = np.concatenate([w.special_rows["pos_inf_valid"], w.special_rows["nan_valid"]])
+    assert (y[nanrows] == 0x7FC0).all() and np.isnan(lse[nanrows]).all()
+    empty = w.special_rows["all_neg_inf"]
+    assert (y[empty] == 0xFF80).all() and (lse[empty] == -np.inf).all()
+
+
+@pytest.mark.parametrize("dtype", W.DTYPES)
+def test_log_softmax_odd_shapes_and_policy(dtype):
+    rng = np.random.default_rng(200)
+    for cols in (1, 7, 64, 513, 2049, 5000):
+        rows = 11
+        x = W.random_rows(rows, cols, dtype, seed=cols + 1, scale=30.0)
+        W.set_bits(x, 2, 0, dtype, W.QNAN[dtype])
+        for mask in _masks(rows, cols, rng):
+            banner(f"log {dtype} cols={cols} mask={mask.kind}")
+            for misalign in (False, True):
+                for path in _paths(dtype, cols, misalign):
+                    chunk = 0 if path != "split" else 64
+                    y, lse = run_log(x, dtype, mask, path=path, chunk_cols=chunk, misalign=misalign)
+                    check_log_full(x, dtype, mask, y, lse, f"log {dtype} cols={cols} {mask.kind} {path} {misalign}")
+
+
+def test_log_softmax_matches_softmax_and_torch():
+    """log_softmax agrees with torch.log_softmax in float64 on fp32 rows, and
+    exp(log_softmax) with softmax_rows."""
+    x = W.random_rows(64, 1000, "f32", seed=9, scale=20.0)
+    y, lse = run_log(x, "f32")
+    ref = torch.log_softmax(torch.from_numpy(x.astype(np.float64)), 1).numpy()
+    assert np.allclose(y, ref, rtol=0, atol=1e-6 * max(1.0, np.abs(ref).max()))
+    p = run_rows(x, "f32")
+    assert np.allclose(np.exp(y.astype(np.float64)), p, rtol=2e-5, atol=1e-30)
