@@ -55,6 +55,8 @@ def parse():
     ap.add_argument("--configs", default="2,1,3,4,5",
                     help="workloads to time; the first is the headline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--next-ops", default="2,4",
+                    help="workloads on which the log-softmax entry point is also timed ('' for none)")
     ap.add_argument("--no-spread", action="store_true",
                     help="skip the single-launch spread loop (profiling runs)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -96,7 +98,8 @@ def make_workload(k: int):
     return W.CONFIGS[k]()
 
 
-def time_workload(w, steps: int, warmup: int, calibrate_copy: bool = False, spread: bool = True):
+def time_workload(w, steps: int, warmup: int, calibrate_copy: bool = False, spread: bool = True,
+                  op: str = "softmax_rows"):
     import torch
 
     import numerically_stable_online_amd as smx
@@ -123,6 +126,17 @@ def time_workload(w, steps: int, warmup: int, calibrate_copy: bool = False, spre
         chunk = smx.softmax_default_chunk_cols(w.rows, w.cols, x0.dtype)
         n_chunks = -(-w.cols // chunk)
     nbytes = algorithmic_bytes(w, path, n_chunks)
+    if op == "softmax_rows":
+        def call(i):
+            smx.softmax_rows(xs[i % copies], ys[i % copies], **kw)
+    elif op == "log_softmax_rows":
+        lses = [torch.empty(w.rows, dtype=torch.float32, device=x0.device) for _ in range(copies)]
+        nbytes += 4 * w.rows  # the per-row log-sum-exp
+
+        def call(i):
+            smx.log_softmax_rows(xs[i % copies], ys[i % copies], lses[i % copies], **kw)
+    else:
+        raise ValueError(op)
 
     if calibrate_copy:
         c = torch.empty_like(x0)
@@ -130,7 +144,7 @@ def time_workload(w, steps: int, warmup: int, calibrate_copy: bool = False, spre
         torch.cuda.synchronize()
 
     for i in range(warmup):
-        smx.softmax_rows(xs[i % copies], ys[i % copies], **kw)
+        call(i)
     torch.cuda.synchronize()
 
     # the timed region: K back-to-back calls, bracketed by synchronizations;
@@ -142,7 +156,7 @@ def time_workload(w, steps: int, warmup: int, calibrate_copy: bool = False, spre
     t0 = time.perf_counter()
     ev0.record(stream)
     for i in range(steps):
-        smx.softmax_rows(xs[i % copies], ys[i % copies], **kw)
+        call(i)
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -154,7 +168,7 @@ def time_workload(w, steps: int, warmup: int, calibrate_copy: bool = False, spre
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(n_single)]
     for i in range(n_single):
         starts[i].record(stream)
-        smx.softmax_rows(xs[i % copies], ys[i % copies], **kw)
+        call(i)
         ends[i].record(stream)
     torch.cuda.synchronize()
     launch_ms = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)] or [gpu_ms])
@@ -235,6 +249,19 @@ def main():
         else:
             del w
 
+    next_ops = {}
+    for k2 in [int(c) for c in args.next_ops.split(",") if c]:
+        w2 = make_workload(k2)
+        r2 = time_workload(w2, args.steps, args.warmup, spread=False, op="log_softmax_rows")
+        g2 = r2["bytes"] / (r2["gpu_ms_per_launch"] * 1e-3) / 1e9
+        next_ops.setdefault("log_softmax_rows", {})[f"config{k2}"] = {
+            "workload": w2.name, "path": r2["path"], "algorithmic_bytes": r2["bytes"],
+            "gpu_ms_per_launch": round(r2["gpu_ms_per_launch"], 5), "GBps_launch": round(g2, 1),
+            "frac_of_peak": round(g2 / HBM_PEAK_GBS, 4)}
+        print(f"# log_softmax_rows config{k2}: path={r2['path']} {g2:.0f} GB/s per launch "
+              f"({r2['gpu_ms_per_launch'] * 1e3:.1f} us)", file=sys.stderr, flush=True)
+        del w2
+
     k, w, r, gbs, kgbs = head
     sha = kernel_source_sha(r["path"])
     traffic = load_traffic(r["path"], sha, f"config{k}")
@@ -258,6 +285,7 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(kgbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel_source_sha": sha},
         "per_config": per,
+        "next_ops": next_ops,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, r["bytes"])

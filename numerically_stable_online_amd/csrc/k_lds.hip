@@ -123,12 +123,13 @@ __global__ __launch_bounds__(NT) void k_lds(RowArgs a) {
       total = block_sum<NW>(s, red);
     }
 
-    float shift;  // softmax: the reciprocal 2^-64 / l; log-softmax: m + log l
+    float inv = 0.0f;  // softmax: the reciprocal 2^-64 / l
+    Lse lse{0.0f, 0.0f};  // log-softmax: m + log l as hi + lo
     if constexpr (EPI == kEpiSoftmax) {
-      shift = 1.0f / total;
+      inv = 1.0f / total;
     } else {
       const float lsum = total * 5.42101086242752217e-20f;  // remove 2^64 (exact)
-      shift = mx + log_l(lsum);
+      lse = make_lse(mx, lsum);
       if (tid == 0) write_lse(a.lse, row, false, mx, lsum);
       if (a.y == nullptr) continue;
     }
@@ -138,7 +139,7 @@ __global__ __launch_bounds__(NT) void k_lds(RowArgs a) {
       if (j0 < cols) {
         uint32_t h[E];
 #pragma unroll
-        for (int e = 0; e < E; ++e) h[e] = enc<DT>(EPI == kEpiSoftmax ? v[k][e] * shift : v[k][e] - shift);
+        for (int e = 0; e < E; ++e) h[e] = enc<DT>(EPI == kEpiSoftmax ? v[k][e] * inv : minus_lse(v[k][e], lse));
         Pack<DT, E> p;
         p.put(h);
         p.template store<true>(yr + j0 * S);

@@ -181,8 +181,9 @@ __global__ __launch_bounds__(kThreads) void k_merge_normalize(RowArgs a, int64_t
       for (int64_t j0 = j_lo + (int64_t)tid * E; j0 < j_hi; j0 += (int64_t)kThreads * E) p.template store<true>(yr + j0 * S);
       continue;
     }
-    // softmax: the reciprocal 2^-64 / L; log-softmax: M + log L
-    const float shift = EPI == kEpiSoftmax ? 1.0f / (l * 18446744073709551616.0f) : m + log_l(l);
+    // softmax: the reciprocal 2^-64 / L; log-softmax: M + log L as hi + lo
+    const float inv = EPI == kEpiSoftmax ? 1.0f / (l * 18446744073709551616.0f) : 0.0f;
+    const Lse lse = EPI == kEpiSoftmax ? Lse{0.0f, 0.0f} : make_lse(m, l);
 
     for (int64_t base = j_lo; base < j_hi; base += kRound) {
       Pack<DT, E> in[VPT];
@@ -206,7 +207,7 @@ __global__ __launch_bounds__(kThreads) void k_merge_normalize(RowArgs a, int64_t
           for (int e = 0; e < E; ++e) {
             const bool ok = (j0 + e < lim) && (!KEEP || keep_lane(kb[k], e));
             const float f = ok ? in[k].get(e) : -kInf;
-            h[e] = enc<DT>(EPI == kEpiSoftmax ? exp_b64<ACC>(f, m) * shift : f - shift);
+            h[e] = enc<DT>(EPI == kEpiSoftmax ? exp_b64<ACC>(f, m) * inv : minus_lse(f, lse));
           }
           Pack<DT, E> out;
           out.put(h);

@@ -134,7 +134,7 @@ __global__ __launch_bounds__(kThreads) void k_wave(RowArgs a) {
     } else {
       // log-softmax: y = x - (m + log l); masked and -inf lanes stay -inf
       const float lsum = total * 5.42101086242752217e-20f;  // remove 2^64 (exact)
-      const float lse = m + log_l(lsum);
+      const Lse lse = make_lse(m, lsum);
       if (lane == 0) write_lse(a.lse, row, false, m, lsum);
       if (a.y != nullptr) {
 #pragma unroll
@@ -143,7 +143,7 @@ __global__ __launch_bounds__(kThreads) void k_wave(RowArgs a) {
           if (j0 < cols) {
             uint32_t h[E];
 #pragma unroll
-            for (int e = 0; e < E; ++e) h[e] = enc<DT>(v[r][k][e] - lse);
+            for (int e = 0; e < E; ++e) h[e] = enc<DT>(minus_lse(v[r][k][e], lse));
             Pack<DT, E> p;
             p.put(h);
             p.template store<true>(yr + j0 * S);

@@ -233,6 +233,19 @@ __device__ __forceinline__ float exp_b64(float x, float m) {
 // natural logarithm (an accurate expansion of v_log_f32, not the fast one).
 __device__ __forceinline__ float log_l(float l) { return __builtin_logf(l); }
 
+// LSE = m + log l carried as hi + lo (exact sum), so x - LSE can be formed as
+// (x - hi) - lo: where x is close to the LSE the first difference is exact
+// and the result keeps its own relative precision.
+struct Lse {
+  float hi, lo;
+};
+__device__ __forceinline__ Lse make_lse(float m, float lsum) {
+  Lse r;
+  two_sum(m, log_l(lsum), r.hi, r.lo);
+  return r;
+}
+__device__ __forceinline__ float minus_lse(float x, const Lse& s) { return (x - s.hi) - s.lo; }
+
 // The epilogue's per-row scalar for the log-softmax outputs.
 __device__ __forceinline__ void write_lse(float* lse, int64_t row, bool poisoned, float m, float lsum) {
   if (lse == nullptr) return;

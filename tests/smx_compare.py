@@ -144,4 +144,6 @@ def check_log(y_raw, dtype, logp, lse_ref, lse_got, cls, st, x_float, what=""):
             i = tuple(i)
             raise AssertionError(f"{what}: {d[i]} ulp at {i}: got {bits[i]:#06x} want {want[i]:#06x} (ref {logp[i]!r})")
         out["max_ulp"] = int(d[num].max()) if num.any() else 0
+        big = num & (np.abs(logp) >= 2.0 ** -8)
+        out["max_ulp_away_from_0"] = int(d[big].max()) if big.any() else 0
     return out
