@@ -135,6 +135,18 @@ def time_workload(w, steps: int, warmup: int, calibrate_copy: bool = False, spre
 
         def call(i):
             smx.log_softmax_rows(xs[i % copies], ys[i % copies], lses[i % copies], **kw)
+    elif op == "softmax_backward_rows":
+        # timing only: p and g are two different resident copies of the input
+        s_el = x0.element_size()
+        bpath = "split" if w.cols * s_el > 4096 and (w.rows < 1024 or w.cols > 256 * 8 * 16 // s_el) else "row"
+        nbytes = 3 * w.rows * w.cols * s_el
+        if bpath == "split":
+            chunk = smx.softmax_default_chunk_cols(w.rows, w.cols, x0.dtype)
+            nbytes += 2 * w.rows * w.cols * s_el + 2 * w.rows * (-(-w.cols // chunk)) * 8
+        path = "split" if bpath == "split" else path
+
+        def call(i):
+            smx.softmax_backward_rows(xs[i % copies], xs[(i + 1) % copies], ys[i % copies])
     else:
         raise ValueError(op)
 
@@ -252,14 +264,15 @@ def main():
     next_ops = {}
     for k2 in [int(c) for c in args.next_ops.split(",") if c]:
         w2 = make_workload(k2)
-        r2 = time_workload(w2, args.steps, args.warmup, spread=False, op="log_softmax_rows")
-        g2 = r2["bytes"] / (r2["gpu_ms_per_launch"] * 1e-3) / 1e9
-        next_ops.setdefault("log_softmax_rows", {})[f"config{k2}"] = {
-            "workload": w2.name, "path": r2["path"], "algorithmic_bytes": r2["bytes"],
-            "gpu_ms_per_launch": round(r2["gpu_ms_per_launch"], 5), "GBps_launch": round(g2, 1),
-            "frac_of_peak": round(g2 / HBM_PEAK_GBS, 4)}
-        print(f"# log_softmax_rows config{k2}: path={r2['path']} {g2:.0f} GB/s per launch "
-              f"({r2['gpu_ms_per_launch'] * 1e3:.1f} us)", file=sys.stderr, flush=True)
+        for op in ("log_softmax_rows", "softmax_backward_rows"):
+            r2 = time_workload(w2, args.steps, args.warmup, spread=False, op=op)
+            g2 = r2["bytes"] / (r2["gpu_ms_per_launch"] * 1e-3) / 1e9
+            next_ops.setdefault(op, {})[f"config{k2}"] = {
+                "workload": w2.name, "path": r2["path"], "algorithmic_bytes": r2["bytes"],
+                "gpu_ms_per_launch": round(r2["gpu_ms_per_launch"], 5), "GBps_launch": round(g2, 1),
+                "frac_of_peak": round(g2 / HBM_PEAK_GBS, 4)}
+            print(f"# {op} config{k2}: path={r2['path']} {g2:.0f} GB/s per launch "
+                  f"({r2['gpu_ms_per_launch'] * 1e3:.1f} us)", file=sys.stderr, flush=True)
         del w2
 
     k, w, r, gbs, kgbs = head

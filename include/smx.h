@@ -173,6 +173,25 @@ SMX_API int log_softmax_rows(const void* x, void* y, float* lse, int64_t rows, i
 SMX_API int log_softmax_rows_path(const void* x, void* y, float* lse, int64_t rows, int64_t cols, smx_dtype dtype,
                           const smx_mask* valid_len_or_mask, smx_path path, int64_t chunk_cols, void* stream);
 
+/* softmax_backward_rows — the vector-Jacobian product of the softmax
+ * ("Softmax numerics architecture", section on the Jacobian and the backward
+ * pass: J = diag(p) - p p^T is never formed; dx = p * (g - g.p)).
+ *   p  : device [rows, cols], a softmax output (masked lanes 0);
+ *   g  : device [rows, cols], the gradient with respect to p;
+ *   dx : device [rows, cols], dx[r, j] = p[r, j] * (g[r, j] - sum_k g[r, k] p[r, k]).
+ * All three share dtype; the dot product accumulates in compensated fp32. dx
+ * may equal p or g exactly (in place); partial overlap is SMX_EINVAL. A NaN
+ * in a row's p or g makes that row's dx the canonical NaN. Long rows take two
+ * passes (per-chunk partial dot products in a stream-ordered workspace of
+ * rows * ceil(cols / chunk) * 8 bytes). */
+SMX_API int softmax_backward_rows(const void* p, const void* g, void* dx, int64_t rows, int64_t cols,
+                                  smx_dtype dtype, void* stream);
+
+/* softmax_backward_rows with the path forced: SMX_PATH_WAVE (one wave per
+ * row), SMX_PATH_LDS (one workgroup per row), SMX_PATH_SPLIT (two passes). */
+SMX_API int softmax_backward_rows_path(const void* p, const void* g, void* dx, int64_t rows, int64_t cols,
+                                       smx_dtype dtype, smx_path path, int64_t chunk_cols, void* stream);
+
 /* The chunk width softmax_rows uses on the split path (a tuning hint). */
 SMX_API int64_t softmax_default_chunk_cols(int64_t rows, int64_t cols,
                                    smx_dtype dtype);

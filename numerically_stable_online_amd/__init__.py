@@ -11,6 +11,7 @@ Functions keep the C names:
   softmax_row_stats(x, chunk_cols)  -> stats [rows, n_chunks, 2] (m, l)
   softmax_merge_normalize(x, stats, chunk_cols) -> y
   log_softmax_rows(x, ...)          -> (y, lse)
+  softmax_backward_rows(p, g)       -> dx
   softmax_default_chunk_cols(rows, cols, dtype)
   softmax_select_path(rows, cols, dtype)
   smx_last_error()
@@ -78,6 +79,10 @@ def lib() -> C.CDLL:
         L.log_softmax_rows.restype = i32
         L.log_softmax_rows_path.argtypes = [vp, vp, vp, i64, i64, i32, mp, i32, i64, vp]
         L.log_softmax_rows_path.restype = i32
+        L.softmax_backward_rows.argtypes = [vp, vp, vp, i64, i64, i32, vp]
+        L.softmax_backward_rows.restype = i32
+        L.softmax_backward_rows_path.argtypes = [vp, vp, vp, i64, i64, i32, i32, i64, vp]
+        L.softmax_backward_rows_path.restype = i32
         L.softmax_default_chunk_cols.argtypes = [i64, i64, i32]
         L.softmax_default_chunk_cols.restype = i64
         L.smx_last_error.argtypes = []
@@ -208,6 +213,23 @@ def log_softmax_rows(x: torch.Tensor, out: Optional[torch.Tensor] = None, lse: O
                                      _mask_arg(m), PATH[path], int(chunk_cols), _stream_handle(stream, x.device))
     _check(rc)
     return y, ls
+
+
+def softmax_backward_rows(p: torch.Tensor, g: torch.Tensor, out: Optional[torch.Tensor] = None, *,
+                          path: str = "auto", chunk_cols: int = 0, stream=None) -> torch.Tensor:
+    """dx = p * (g - sum(g * p)) row by row (the softmax vector-Jacobian product)."""
+    rows, cols = _rows_cols(p)
+    if g.shape != p.shape or g.dtype != p.dtype or not g.is_contiguous():
+        raise ValueError("g must be a contiguous tensor of p's shape and dtype")
+    _on(g, p.device, "g")
+    dx = torch.empty_like(p) if out is None else out
+    if dx.shape != p.shape or dx.dtype != p.dtype or not dx.is_contiguous():
+        raise ValueError("out must be a contiguous tensor of p's shape and dtype")
+    _on(dx, p.device, "out")
+    rc = lib().softmax_backward_rows_path(p.data_ptr(), g.data_ptr(), dx.data_ptr(), rows, cols, _dtype_code(p),
+                                          PATH[path], int(chunk_cols), _stream_handle(stream, p.device))
+    _check(rc)
+    return dx
 
 
 def softmax_row_stats(x: torch.Tensor, chunk_cols: int, out: Optional[torch.Tensor] = None, *,

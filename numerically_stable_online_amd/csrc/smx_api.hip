@@ -253,6 +253,62 @@ int log_softmax_rows(const void* x, void* y, float* lse, int64_t rows, int64_t c
   return log_softmax_rows_path(x, y, lse, rows, cols, dtype, mask, SMX_PATH_AUTO, 0, stream);
 }
 
+int softmax_backward_rows_path(const void* p, const void* g, void* dx, int64_t rows, int64_t cols, smx_dtype dtype,
+                               smx_path path, int64_t chunk_cols, void* stream) {
+  const int dt = (int)dtype;
+  if (dt != SMX_F32 && dt != SMX_F16 && dt != SMX_BF16)
+    return fail(SMX_EINVAL, "dtype %d is not SMX_F32, SMX_F16 or SMX_BF16", dt);
+  if (rows < 0 || cols < 0) return fail(SMX_EINVAL, "rows and cols must be >= 0");
+  const int64_t s = elem_size(dt);
+  if (cols > 0 && rows > INT64_MAX / cols / s) return fail(SMX_EINVAL, "rows * cols * element size overflows int64");
+  if ((int)path < SMX_PATH_AUTO || (int)path > SMX_PATH_SPLIT) return fail(SMX_EINVAL, "path %d is not a smx_path", (int)path);
+  if (chunk_cols < 0) return fail(SMX_EINVAL, "chunk_cols must be >= 0");
+  const int64_t n = rows * cols;
+  if (n == 0) return ok();
+  if (p == nullptr || g == nullptr || dx == nullptr) return fail(SMX_EINVAL, "p, g and dx must not be NULL");
+  const uintptr_t bytes = (uintptr_t)(n * s), da = (uintptr_t)dx;
+  for (const void* in : {p, g}) {
+    const uintptr_t ia = (uintptr_t)in;
+    if (ia != da && ia < da + bytes && da < ia + bytes) return fail(SMX_EINVAL, "dx overlaps p or g without being equal");
+  }
+  const bool vec = (uintptr_t)p % 16 == 0 && (uintptr_t)g % 16 == 0 && da % 16 == 0 && (cols * s) % 16 == 0;
+  if (path == SMX_PATH_AUTO) {
+    if (cols <= bwd_wave_max_cols(dt, vec) && cols * s <= 4096)
+      path = SMX_PATH_WAVE;
+    else if (cols <= bwd_block_max_cols(dt, vec) && rows >= 1024)
+      path = SMX_PATH_LDS;
+    else
+      path = SMX_PATH_SPLIT;
+  }
+  hipError_t err = hipSuccess;
+  const hipStream_t st = (hipStream_t)stream;
+  if (path == SMX_PATH_WAVE || path == SMX_PATH_LDS) {
+    const bool wave = path == SMX_PATH_WAVE;
+    const int64_t cap = wave ? bwd_wave_max_cols(dt, vec) : bwd_block_max_cols(dt, vec);
+    if (cols > cap) return fail(SMX_EINVAL, "this path holds at most %lld cols for this dtype/alignment", (long long)cap);
+    err = launch_bwd_rows((const char*)p, (const char*)g, (char*)dx, rows, cols, dt, vec, wave, st);
+    if (err != hipSuccess) return hip_fail(err, "kernel launch");
+    return ok();
+  }
+  const int64_t e = vec_elems(dt);
+  const int64_t chunk = chunk_cols > 0 ? chunk_cols : default_chunk(rows, cols, dt, vec);
+  const bool cvec = vec && chunk % e == 0;
+  const int64_t nch = (cols + chunk - 1) / chunk;
+  void* ws = nullptr;
+  err = hipMallocAsync(&ws, (size_t)(rows * nch) * sizeof(float2), st);
+  if (err != hipSuccess) return hip_fail(err, "hipMallocAsync of the partial-dot workspace");
+  err = launch_bwd_split((const char*)p, (const char*)g, (char*)dx, rows, cols, dt, cvec, chunk, nch, (float2*)ws, st);
+  const hipError_t ferr = hipFreeAsync(ws, st);
+  if (err != hipSuccess) return hip_fail(err, "kernel launch");
+  if (ferr != hipSuccess) return hip_fail(ferr, "hipFreeAsync of the partial-dot workspace");
+  return ok();
+}
+
+int softmax_backward_rows(const void* p, const void* g, void* dx, int64_t rows, int64_t cols, smx_dtype dtype,
+                          void* stream) {
+  return softmax_backward_rows_path(p, g, dx, rows, cols, dtype, SMX_PATH_AUTO, 0, stream);
+}
+
 const char* smx_last_error(void) { return g_err; }
 
 }  // extern "C"

@@ -64,4 +64,12 @@ hipError_t launch_stats(const RowArgs& a, int dtype, bool vec, int64_t chunk_col
 hipError_t launch_merge_normalize(const RowArgs& a, int dtype, bool vec, int epi, int64_t chunk_cols,
                                   int64_t n_chunks, const smx_stat* stats, hipStream_t stream);
 
+// --- softmax backward (k_backward.hip) ---
+int64_t bwd_wave_max_cols(int dtype, bool vec);
+int64_t bwd_block_max_cols(int dtype, bool vec);
+hipError_t launch_bwd_rows(const char* p, const char* g, char* dx, int64_t rows, int64_t cols, int dtype,
+                           bool vec, bool wave, hipStream_t stream);
+hipError_t launch_bwd_split(const char* p, const char* g, char* dx, int64_t rows, int64_t cols, int dtype, bool vec,
+                            int64_t chunk, int64_t n_chunks, float2* partials, hipStream_t stream);
+
 }  // namespace smx

@@ -147,3 +147,50 @@ def check_log(y_raw, dtype, logp, lse_ref, lse_got, cls, st, x_float, what=""):
         big = num & (np.abs(logp) >= 2.0 ** -8)
         out["max_ulp_away_from_0"] = int(d[big].max()) if big.any() else 0
     return out
+
+
+# ---------------------------------------------------------------------------
+# Softmax backward (dx = p * (g - g.p))
+# ---------------------------------------------------------------------------
+#
+# The forward error of p_j * (g_j - s) scales with p_j * (|g_j| + sum|g_k p_k|),
+# so the bars are relative to that scale:
+#   f32      : |dx - r| <= 1e-6  * max(p_j (|g_j| + sum_k |g_k p_k|), 2^-126)
+#              (the floor is the forward's: a subnormal result is held to
+#              about 8 subnormal steps)
+#   f16/bf16 : within 1 ulp of the rounded reference, or
+#              |dx - r| <= 2^-20 * p_j (|g_j| + sum_k |g_k p_k|)
+# Rows holding a NaN in p or g must be the canonical NaN in every lane.
+
+BWD_F32_TOL = 1e-6
+BWD_16_TOL = 2.0 ** -20
+
+
+def check_bwd(dx_raw, dtype, ref, p_f64, g_f64, what=""):
+    nan_rows = np.isnan(p_f64).any(1) | np.isnan(g_f64).any(1)
+    bits = bits_of(dx_raw, dtype)
+    assert (bits[nan_rows] == NAN_BITS[dtype]).all(), f"{what}: NaN rows must be the canonical NaN"
+    ok = ~nan_rows
+    p, g, r = p_f64[ok], g_f64[ok], ref[ok]
+    scale = np.abs(p) * (np.abs(g) + np.abs(g * p).sum(1, keepdims=True))
+    if dtype == "f32":
+        y = dx_raw[ok].astype(np.float64)
+        err = np.abs(y - r)
+        scale = np.maximum(scale, FLT_MIN)
+        bad = err > BWD_F32_TOL * scale
+        if bad.any():
+            i = tuple(np.argwhere(bad)[0])
+            raise AssertionError(f"{what}: dx error {err[i]:.3e} > {BWD_F32_TOL * scale[i]:.3e} at {i}")
+        return {"max_err_over_scale": float((err / np.maximum(scale, 1e-300)).max()) if err.size else 0.0}
+    y = (dx_raw[ok].view(np.float16).astype(np.float64) if dtype == "f16"
+         else (dx_raw[ok].astype(np.uint32) << 16).view(np.float32).astype(np.float64))
+    want = oracle.encode(r, dtype).astype(np.int64)
+    d = np.abs(bits[ok] - want)
+    err = np.abs(y - r)
+    bad = (d > ULP_TOL) & (err > BWD_16_TOL * scale)
+    if bad.any():
+        i = tuple(np.argwhere(bad)[0])
+        raise AssertionError(f"{what}: {d[i]} ulp and error {err[i]:.3e} at {i} (ref {r[i]!r})")
+    far = np.abs(r) >= 2.0 ** -8 * scale
+    return {"max_ulp": int(d.max()) if d.size else 0,
+            "max_ulp_without_cancellation": int(d[far].max()) if far.any() else 0}

@@ -451,3 +451,81 @@ def test_log_softmax_matches_softmax_and_torch():
     assert np.allclose(y, ref, rtol=0, atol=1e-6 * max(1.0, np.abs(ref).max()))
     p = run_rows(x, "f32")
     assert np.allclose(np.exp(y.astype(np.float64)), p, rtol=2e-5, atol=1e-30)
+
+
+# ---------------------------------------------------------------------------
+# Softmax backward
+# ---------------------------------------------------------------------------
+
+from smx_compare import check_bwd  # noqa: E402
+
+
+def bwd_inputs(x_raw, dtype, mask, seed):
+    """p = the oracle's softmax of x in the element format; g seeded N(0, 1)."""
+    p, cls, st = oracle.softmax_rows(x_raw, dtype, mask)
+    p_raw = oracle.encode(p, dtype)
+    g_raw = W.random_rows(x_raw.shape[0], x_raw.shape[1], dtype, seed=seed, scale=1.0)
+    return p_raw, g_raw
+
+
+def run_bwd(p_raw, g_raw, dtype, path="auto", chunk_cols=0, misalign=False, inplace=False):
+    rows, cols = p_raw.shape
+    if misalign:
+        bufs = [torch.empty(rows * cols + 1, dtype=TORCH_DTYPE[dtype], device="cuda") for _ in range(3)]
+        p, g, dx = (b[1:].view(rows, cols) for b in bufs)
+        p.copy_(to_device(p_raw, dtype))
+        g.copy_(to_device(g_raw, dtype))
+    else:
+        p, g = to_device(p_raw, dtype), to_device(g_raw, dtype)
+        dx = g if inplace else torch.empty_like(p)
+    smx.softmax_backward_rows(p, g, dx, path=path, chunk_cols=chunk_cols)
+    torch.cuda.synchronize()
+    return to_host(dx, dtype)
+
+
+def check_bwd_full(p_raw, g_raw, dtype, dx, what):
+    ref = oracle.softmax_backward_rows(p_raw, g_raw, dtype)
+    return check_bwd(dx, dtype, ref, W.to_float(p_raw, dtype).astype(np.float64),
+                     W.to_float(g_raw, dtype).astype(np.float64), what)
+
+
+@pytest.mark.parametrize("cfg,path", [(1, "auto"), (1, "wave"), (1, "lds"), (1, "split"), (2, "auto"),
+                                      (2, "split"), (3, "auto"), (4, "auto")])
+def test_backward_workloads(cfg, path):
+    w = W.CONFIGS[cfg]()
+    p_raw, g_raw = bwd_inputs(w.x, w.dtype, w.mask, seed=100 + cfg)
+    banner(f"backward config{cfg} {path}")
+    dx = run_bwd(p_raw, g_raw, w.dtype, path=path)
+    r = check_bwd_full(p_raw, g_raw, w.dtype, dx, f"backward config{cfg}/{path}")
+    banner(f"backward config{cfg} {path}: {r}")
+
+
+@pytest.mark.parametrize("dtype", W.DTYPES)
+def test_backward_odd_shapes(dtype):
+    for cols in (1, 3, 64, 511, 2048, 2049, 9000, 33000):
+        rows = 9
+        x = W.random_rows(rows, cols, dtype, seed=cols + 7, scale=10.0)
+        p_raw, g_raw = bwd_inputs(x, dtype, None, seed=cols)
+        if cols > 3:
+            W.set_bits(g_raw, 4, 2, dtype, W.QNAN[dtype])  # a NaN gradient poisons its row
+        for misalign in (False, True):
+            for path in ("auto", "wave", "lds", "split"):
+                vec = not misalign and (cols * (4 if dtype == "f32" else 2)) % 16 == 0
+                e = (4 if dtype == "f32" else 8) if vec else 1
+                if path == "wave" and cols > 64 * 8 * e:
+                    continue
+                if path == "lds" and cols > 256 * 8 * e:
+                    continue
+                what = f"backward {dtype} cols={cols} {path} misalign={misalign}"
+                dx = run_bwd(p_raw, g_raw, dtype, path=path, chunk_cols=700 if path == "split" else 0,
+                             misalign=misalign)
+                check_bwd_full(p_raw, g_raw, dtype, dx, what)
+
+
+def test_backward_in_place_and_deterministic():
+    w = W.config2(rows=256)
+    p_raw, g_raw = bwd_inputs(w.x, "bf16", w.mask, seed=3)
+    a = run_bwd(p_raw, g_raw, "bf16")
+    b = run_bwd(p_raw, g_raw, "bf16", inplace=True)
+    assert np.array_equal(a, b)
+    check_bwd_full(p_raw, g_raw, "bf16", a, "backward in place")

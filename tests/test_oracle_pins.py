@@ -534,3 +534,25 @@ def test_config_generators_shapes():
     assert (st[w.special_rows["all_neg_inf"]] == oracle.ROW_EMPTY).all()
     for name in ("nan_masked", "pos_inf_masked"):
         assert (st[w.special_rows[name]] == oracle.ROW_OK).all()
+
+
+def test_softmax_backward_closed_forms():
+    """"Softmax numerics architecture", Jacobian section: J = diag(p) - p p^T.
+    A one-hot g picks a column of J in closed form, and a constant g (the
+    gradient of a shift) gives zero, since the rows of J sum to 0."""
+    rng = np.random.default_rng(25)
+    x = (4 * rng.standard_normal((3, 17))).astype(np.float64)
+    p = np.exp(x - x.max(1, keepdims=True))
+    p /= p.sum(1, keepdims=True)
+    p32 = p.astype(np.float32)
+    pd = p32.astype(np.float64)
+    for t in (0, 5, 16):
+        g = np.zeros((3, 17), dtype=np.float32)
+        g[:, t] = 1.0
+        dx = oracle.softmax_backward_rows(p32, g, "f32")
+        col = -pd * pd[:, t:t + 1]
+        col[:, t] += pd[:, t]
+        assert np.allclose(dx, col, rtol=1e-15, atol=1e-18)
+    g = np.full((3, 17), 2.5, dtype=np.float32)
+    dx = oracle.softmax_backward_rows(p32, g, "f32")
+    assert np.abs(dx).max() <= 2.5 * 17 * 2.0 ** -23  # sum(p) is 1 to fp32 rounding
