@@ -68,6 +68,7 @@ def lib():
         L.oracle_online_tiled.restype = None
         L.oracle_log_softmax_rows.argtypes = [vp, i32, i64, i64, mp, i64, i64, vp, vp]
         L.oracle_softmax_backward_rows.argtypes = [vp, vp, i32, i64, i64, i64, i64, vp]
+        L.oracle_cross_entropy_rows.argtypes = [vp, i32, i64, i64, mp, vp, i64, i64, vp, vp]
         L.oracle_round_f32_bits.argtypes = [C.c_double]
         L.oracle_round_f32_bits.restype = C.c_uint32
         L.oracle_round_f16_bits.argtypes = [C.c_double]
@@ -233,6 +234,24 @@ def softmax_backward_rows(p: np.ndarray, g: np.ndarray, dtype: str, r0: int = 0,
     if rc != 0:
         raise ValueError("oracle_softmax_backward_rows: bad arguments")
     return dx
+
+
+def cross_entropy_rows(x: np.ndarray, dtype: str, target: np.ndarray, mask=None, r0: int = 0,
+                       r1: Optional[int] = None, want_dx: bool = True):
+    """Per-row loss LSE - x_t (float64) and, if asked, dx = p - onehot(t)."""
+    x = _raw(x, dtype)
+    rows, cols = x.shape
+    r1 = rows if r1 is None else r1
+    t = np.ascontiguousarray(target, dtype=np.int32)
+    assert t.shape == (rows,)
+    loss = np.empty(r1 - r0, dtype=np.float64)
+    dx = np.empty((r1 - r0, cols), dtype=np.float64) if want_dx else None
+    ms, keep = _mask_struct(mask, rows, cols)
+    rc = lib().oracle_cross_entropy_rows(_ptr(x), DTYPE_CODE[dtype], rows, cols, C.byref(ms), _ptr(t), r0, r1,
+                                         _ptr(loss), _ptr(dx))
+    if rc != 0:
+        raise ValueError("oracle_cross_entropy_rows: bad arguments")
+    return loss, dx
 
 
 def round_f16_bits(v: float) -> int:

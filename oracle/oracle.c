@@ -488,6 +488,78 @@ int oracle_softmax_backward_rows(const void* p, const void* g, int dtype,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Cross-entropy with logits ("Softmax numerics architecture", log-sum-exp   */
+/* section: CE = LSE - x_t; Jacobian section: the fused gradient p - y with  */
+/* y the one-hot target).                                                    */
+/* ------------------------------------------------------------------------ */
+
+int oracle_cross_entropy_rows(const void* x, int dtype, int64_t rows,
+                              int64_t cols, const oracle_mask* mk,
+                              const int32_t* target, int64_t r0, int64_t r1,
+                              double* loss, double* dx) {
+  if (dtype < 0 || dtype > 2 || rows < 0 || cols < 0 || r0 < 0 || r1 > rows ||
+      r0 > r1 || !mask_ok(mk) || target == NULL)
+    return -1;
+  double* p = (double*)malloc(sizeof(double) * (size_t)(cols ? cols : 1));
+  uint8_t* cls = (uint8_t*)malloc((size_t)(cols ? cols : 1));
+  if (!p || !cls) {
+    free(p);
+    free(cls);
+    return -1;
+  }
+  for (int64_t r = r0; r < r1; ++r) {
+    double* d = dx ? dx + (r - r0) * cols : NULL;
+    const int64_t t = target[r];
+    if (t < 0 || t >= cols) { /* ignored row */
+      loss[r - r0] = 0.0;
+      if (d)
+        for (int64_t j = 0; j < cols; ++j) d[j] = 0.0;
+      continue;
+    }
+    const int32_t st = softmax_one_row(x, dtype, cols, mk, r, p, cls);
+    if (st == ORACLE_ROW_POISON) {
+      loss[r - r0] = NAN;
+      if (d)
+        for (int64_t j = 0; j < cols; ++j) d[j] = NAN;
+      continue;
+    }
+    if (st == ORACLE_ROW_EMPTY || cls[t] != ORACLE_LANE_NUMERIC) {
+      loss[r - r0] = INFINITY; /* the target has probability 0 */
+    } else {
+      /* LSE - x_t = (m - x_t) + log(l). When the target holds the maximum
+       * the loss is log(1 + sum over the other lanes of exp(x_j - m)),
+       * written with log1p so a confident prediction's tiny loss keeps its
+       * relative precision; otherwise both terms are positive. */
+      const int64_t prefix = oracle_valid_prefix(mk, r, cols);
+      const double xt = oracle_decode(x, dtype, r * cols + t);
+      double m = -INFINITY;
+      for (int64_t j = 0; j < cols; ++j) {
+        if (!lane_valid(mk, r, j, cols, prefix)) continue;
+        double v = oracle_decode(x, dtype, r * cols + j);
+        if (v > m) m = v;
+      }
+      nsum all = {0.0, 0.0}, others = {0.0, 0.0};
+      for (int64_t j = 0; j < cols; ++j) {
+        if (!lane_valid(mk, r, j, cols, prefix)) continue;
+        double v = oracle_decode(x, dtype, r * cols + j);
+        if (v == -INFINITY) continue;
+        const double e = exp(v - m);
+        nsum_add(&all, e);
+        if (j != t) nsum_add(&others, e);
+      }
+      loss[r - r0] = (xt == m) ? log1p(nsum_value(&others))
+                               : (m - xt) + log(nsum_value(&all));
+    }
+    if (d) {
+      for (int64_t j = 0; j < cols; ++j) d[j] = p[j] - (j == t ? 1.0 : 0.0);
+    }
+  }
+  free(p);
+  free(cls);
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Output rounding: nearest-even with gradual underflow.                     */
 /* ------------------------------------------------------------------------ */
 

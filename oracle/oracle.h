@@ -128,6 +128,17 @@ int oracle_softmax_backward_rows(const void* p, const void* g, int dtype,
                                  int64_t rows, int64_t cols, int64_t r0,
                                  int64_t r1, double* dx);
 
+/* Cross-entropy with logits and its gradient for rows [r0, r1):
+ *   loss_r = LSE_r - x[r, t_r],   dx[r, j] = p[r, j] - [j == t_r].
+ * Policy: t_r outside [0, cols) ignores the row (loss 0, dx 0); a poisoned
+ * row gives NaN loss and dx; an empty row, or a target lane that is masked
+ * or -inf, gives loss +inf (p_t = 0) with dx = p - onehot(t). dx may be
+ * NULL; loss has r1 - r0 entries, dx (r1 - r0) * cols.                      */
+int oracle_cross_entropy_rows(const void* x, int dtype, int64_t rows,
+                              int64_t cols, const oracle_mask* mk,
+                              const int32_t* target, int64_t r0, int64_t r1,
+                              double* loss, double* dx);
+
 /* Rounding of a double to an element format, to nearest-even with gradual
  * underflow. NaN becomes the canonical quiet NaN (f32 0x7FC00000, f16 0x7E00,
  * bf16 0x7FC0).                                                             */

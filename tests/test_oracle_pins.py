@@ -556,3 +556,38 @@ def test_softmax_backward_closed_forms():
     g = np.full((3, 17), 2.5, dtype=np.float32)
     dx = oracle.softmax_backward_rows(p32, g, "f32")
     assert np.abs(dx).max() <= 2.5 * 17 * 2.0 ** -23  # sum(p) is 1 to fp32 rounding
+
+
+def test_cross_entropy_closed_forms_and_library():
+    """CE = LSE - x_t ("Softmax numerics architecture", log-sum-exp section).
+    The two-logit family of the network lab gives CE([0, z], 1) = -log sigma(z)
+    = log(1 + e^-z), and the fused gradient is p - onehot ("Jacobian" section);
+    torch's cross_entropy in float64 is the library check."""
+    for z in (0.5, 2.5, -7.0, 30.0):
+        x = np.array([[0.0, z]], dtype=np.float32)
+        loss, dx = oracle.cross_entropy_rows(x, "f32", np.array([1], np.int32))
+        zz = float(np.float32(z))
+        assert abs(loss[0] - math.log1p(math.exp(-zz))) <= 1e-15 * max(1.0, loss[0])
+        s = 1.0 / (1.0 + math.exp(-zz))
+        assert abs(dx[0, 1] - (s - 1.0)) <= 1e-15 and abs(dx[0, 0] - (1.0 - s)) <= 1e-15
+    rng = np.random.default_rng(26)
+    x = (6 * rng.standard_normal((20, 50))).astype(np.float32)
+    t = rng.integers(0, 50, 20).astype(np.int32)
+    loss, dx = oracle.cross_entropy_rows(x, "f32", t)
+    xt = torch.from_numpy(x.astype(np.float64)).requires_grad_(True)
+    ref = torch.nn.functional.cross_entropy(xt, torch.from_numpy(t.astype(np.int64)), reduction="none")
+    ref.sum().backward()
+    assert np.allclose(loss, ref.detach().numpy(), rtol=1e-13, atol=1e-13)
+    assert np.allclose(dx, xt.grad.numpy(), rtol=1e-12, atol=1e-15)
+
+
+def test_cross_entropy_policy():
+    x = np.array([[1.0, 2.0, 3.0, 4.0]] * 5, dtype=np.float32)
+    x[2, 1] = np.nan
+    valid = np.array([4, 4, 4, 2, 0], dtype=np.int32)
+    t = np.array([-1, 9, 0, 3, 1], dtype=np.int32)
+    loss, dx = oracle.cross_entropy_rows(x, "f32", t, W.MaskSpec("valid_len", valid_len=valid))
+    assert loss[0] == 0 and (dx[0] == 0).all() and loss[1] == 0 and (dx[1] == 0).all()  # ignored
+    assert np.isnan(loss[2]) and np.isnan(dx[2]).all()  # poisoned
+    assert loss[3] == np.inf and dx[3, 3] == -1.0 and abs(dx[3].sum() + 0.0) <= 1e-15  # masked target
+    assert loss[4] == np.inf and list(dx[4]) == [0.0, -1.0, 0.0, 0.0]  # empty row
