@@ -523,6 +523,7 @@ int oracle_cross_entropy_rows(const void* x, int dtype, int64_t rows,
         for (int64_t j = 0; j < cols; ++j) d[j] = NAN;
       continue;
     }
+    double at_t = -1.0; /* dx at the target lane: p_t - 1 */
     if (st == ORACLE_ROW_EMPTY || cls[t] != ORACLE_LANE_NUMERIC) {
       loss[r - r0] = INFINITY; /* the target has probability 0 */
     } else {
@@ -549,9 +550,12 @@ int oracle_cross_entropy_rows(const void* x, int dtype, int64_t rows,
       }
       loss[r - r0] = (xt == m) ? log1p(nsum_value(&others))
                                : (m - xt) + log(nsum_value(&all));
+      /* p_t - 1 = -(sum of the other lanes' p): the same number, without the
+       * cancellation of 1 - p_t when the target holds almost all the mass */
+      at_t = -(nsum_value(&others) / nsum_value(&all));
     }
     if (d) {
-      for (int64_t j = 0; j < cols; ++j) d[j] = p[j] - (j == t ? 1.0 : 0.0);
+      for (int64_t j = 0; j < cols; ++j) d[j] = (j == t) ? at_t : p[j];
     }
   }
   free(p);

@@ -569,7 +569,10 @@ def test_cross_entropy_closed_forms_and_library():
         zz = float(np.float32(z))
         assert abs(loss[0] - math.log1p(math.exp(-zz))) <= 1e-15 * max(1.0, loss[0])
         s = 1.0 / (1.0 + math.exp(-zz))
-        assert abs(dx[0, 1] - (s - 1.0)) <= 1e-15 and abs(dx[0, 0] - (1.0 - s)) <= 1e-15
+        assert abs(dx[0, 0] - (1.0 - s)) <= 1e-15
+        # the target lane, sigma(z) - 1 = -1 / (1 + e^z), to full relative precision
+        exact = -1.0 / (1.0 + math.exp(zz))
+        assert abs(dx[0, 1] - exact) <= 4e-16 * abs(exact)
     rng = np.random.default_rng(26)
     x = (6 * rng.standard_normal((20, 50))).astype(np.float32)
     t = rng.integers(0, 50, 20).astype(np.int32)
