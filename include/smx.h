@@ -173,6 +173,33 @@ SMX_API int log_softmax_rows(const void* x, void* y, float* lse, int64_t rows, i
 SMX_API int log_softmax_rows_path(const void* x, void* y, float* lse, int64_t rows, int64_t cols, smx_dtype dtype,
                           const smx_mask* valid_len_or_mask, smx_path path, int64_t chunk_cols, void* stream);
 
+/* softmax_cross_entropy_rows — cross-entropy with logits and its fused
+ * gradient ("Softmax numerics architecture": log-sum-exp section, CE =
+ * LSE - x_t; Jacobian section, the gradient p - y with y the one-hot target,
+ * which never divides by a probability).
+ *   x     : device [rows, cols] logits;
+ *   target: device int32 [rows]; a target outside [0, cols) ignores its row;
+ *   loss  : device float [rows], loss_r = LSE_r - x[r, t_r];
+ *   dx    : device [rows, cols] in dtype, dx = softmax(x) - onehot(t), or
+ *           NULL for the loss alone; dx may equal x (in place).
+ * Policy: an ignored row has loss 0 and dx 0; a poisoned row (+inf/NaN in a
+ * valid lane) has loss NaN and a NaN dx row; an empty row, or a target lane
+ * that is masked or -inf, has loss +inf with dx = p - onehot(t) (p = 0 on an
+ * empty row). When the target holds the row maximum the loss is computed as
+ * log1p of the other lanes' shifted sum, and dx_t as -(others / sum), so a
+ * confident prediction keeps full relative precision. Paths, masks, errors
+ * and streams as softmax_rows; the split path's workspace adds 4 bytes per
+ * row. loss must not overlap x or dx. */
+SMX_API int softmax_cross_entropy_rows(const void* x, const int32_t* target, float* loss, void* dx, int64_t rows,
+                                       int64_t cols, smx_dtype dtype, const smx_mask* valid_len_or_mask,
+                                       void* stream);
+
+/* softmax_cross_entropy_rows with the kernel path forced. */
+SMX_API int softmax_cross_entropy_rows_path(const void* x, const int32_t* target, float* loss, void* dx,
+                                            int64_t rows, int64_t cols, smx_dtype dtype,
+                                            const smx_mask* valid_len_or_mask, smx_path path, int64_t chunk_cols,
+                                            void* stream);
+
 /* softmax_backward_rows — the vector-Jacobian product of the softmax
  * ("Softmax numerics architecture", section on the Jacobian and the backward
  * pass: J = diag(p) - p p^T is never formed; dx = p * (g - g.p)).

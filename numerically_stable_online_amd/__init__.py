@@ -12,6 +12,7 @@ Functions keep the C names:
   softmax_merge_normalize(x, stats, chunk_cols) -> y
   log_softmax_rows(x, ...)          -> (y, lse)
   softmax_backward_rows(p, g)       -> dx
+  softmax_cross_entropy_rows(x, t)  -> (loss, dx)
   softmax_default_chunk_cols(rows, cols, dtype)
   softmax_select_path(rows, cols, dtype)
   smx_last_error()
@@ -79,6 +80,10 @@ def lib() -> C.CDLL:
         L.log_softmax_rows.restype = i32
         L.log_softmax_rows_path.argtypes = [vp, vp, vp, i64, i64, i32, mp, i32, i64, vp]
         L.log_softmax_rows_path.restype = i32
+        L.softmax_cross_entropy_rows.argtypes = [vp, vp, vp, vp, i64, i64, i32, mp, vp]
+        L.softmax_cross_entropy_rows.restype = i32
+        L.softmax_cross_entropy_rows_path.argtypes = [vp, vp, vp, vp, i64, i64, i32, mp, i32, i64, vp]
+        L.softmax_cross_entropy_rows_path.restype = i32
         L.softmax_backward_rows.argtypes = [vp, vp, vp, i64, i64, i32, vp]
         L.softmax_backward_rows.restype = i32
         L.softmax_backward_rows_path.argtypes = [vp, vp, vp, i64, i64, i32, i32, i64, vp]
@@ -213,6 +218,35 @@ def log_softmax_rows(x: torch.Tensor, out: Optional[torch.Tensor] = None, lse: O
                                      _mask_arg(m), PATH[path], int(chunk_cols), _stream_handle(stream, x.device))
     _check(rc)
     return y, ls
+
+
+def softmax_cross_entropy_rows(x: torch.Tensor, target: torch.Tensor, loss: Optional[torch.Tensor] = None,
+                               dx: Optional[torch.Tensor] = None, *, want_dx: bool = True, valid_len=None,
+                               causal_period=None, causal_offset: int = 0, keep=None, path: str = "auto",
+                               chunk_cols: int = 0, stream=None):
+    """Per-row cross-entropy LSE - x_t (float32 [rows]) and, if asked, the
+    gradient softmax(x) - onehot(t) in x's dtype. Returns (loss, dx or None)."""
+    rows, cols = _rows_cols(x)
+    if target.dtype != torch.int32 or target.shape != (rows,) or not target.is_contiguous():
+        raise ValueError("target must be a contiguous int32 tensor [rows]")
+    _on(target, x.device, "target")
+    ls = torch.empty(rows, dtype=torch.float32, device=x.device) if loss is None else loss
+    if ls.shape != (rows,) or ls.dtype != torch.float32 or not ls.is_contiguous():
+        raise ValueError("loss must be a contiguous float32 tensor [rows]")
+    _on(ls, x.device, "loss")
+    g = None
+    if want_dx:
+        g = torch.empty_like(x) if dx is None else dx
+        if g.shape != x.shape or g.dtype != x.dtype or not g.is_contiguous():
+            raise ValueError("dx must be a contiguous tensor of x's shape and dtype")
+        _on(g, x.device, "dx")
+    m, keepalive = make_mask(rows, cols, valid_len, causal_period, causal_offset, keep, x.device)
+    rc = lib().softmax_cross_entropy_rows_path(x.data_ptr(), target.data_ptr(), ls.data_ptr(),
+                                               None if g is None else g.data_ptr(), rows, cols, _dtype_code(x),
+                                               _mask_arg(m), PATH[path], int(chunk_cols),
+                                               _stream_handle(stream, x.device))
+    _check(rc)
+    return ls, g
 
 
 def softmax_backward_rows(p: torch.Tensor, g: torch.Tensor, out: Optional[torch.Tensor] = None, *,

@@ -82,64 +82,119 @@ __global__ __launch_bounds__(NT) void k_lds(RowArgs a) {
     mx = block_max<NW>(bad ? kInf : mx, red);
     const bool poisoned = mx == kInf;
 
+    // cross-entropy: the row's target lane (-1: ignored row) and its logit
+    int64_t t = -1;
+    float xt = -kInf;
+    if constexpr (EPI == kEpiXent) {
+      t = row_target(a.target, row, cols);
+      if (t < 0) {  // ignored row: loss 0, gradient 0
+        if (tid == 0) a.loss[row] = 0.0f;
+        if (a.y != nullptr) {
+          Pack<DT, E> z;
+          z.fill(0u);
+#pragma unroll
+          for (int k = 0; k < VPT; ++k) {
+            const int64_t j0 = ((int64_t)k * NT + tid) * E;
+            if (j0 < cols) z.template store<true>(yr + j0 * S);
+          }
+        }
+        continue;
+      }
+      if (t < prefix && (!KEEP || a.mask.keep[row * cols + t] != 0)) {
+        Pack<DT, 1> q;
+        q.load(a.x + (row * cols + t) * S);
+        xt = q.get(0);
+      }
+    }
+
     if (poisoned || mx == -kInf) {
       if constexpr (EPI == kEpiLogSoftmax) {
         if (tid == 0) write_lse(a.lse, row, poisoned, mx, 0.0f);
       }
+      if constexpr (EPI == kEpiXent) {
+        if (tid == 0) a.loss[row] = poisoned ? u2f(0x7FC00000u) : kInf;
+      }
       if (a.y != nullptr) {
-        Pack<DT, E> p;
-        p.fill(poisoned ? Fmt<DT>::kNaN : (EPI == kEpiSoftmax ? 0u : Fmt<DT>::kNegInf));
+        const uint32_t fill = poisoned ? Fmt<DT>::kNaN : (EPI == kEpiLogSoftmax ? Fmt<DT>::kNegInf : 0u);
 #pragma unroll
         for (int k = 0; k < VPT; ++k) {
           const int64_t j0 = ((int64_t)k * NT + tid) * E;
-          if (j0 < cols) p.template store<true>(yr + j0 * S);
+          if (j0 < cols) {
+            uint32_t h[E];
+#pragma unroll
+            for (int e = 0; e < E; ++e) h[e] = (!poisoned && j0 + e == t) ? enc<DT>(-1.0f) : fill;
+            Pack<DT, E> p;
+            p.put(h);
+            p.template store<true>(yr + j0 * S);
+          }
         }
       }
       continue;
     }
 
-    float total;
+    float total, others = 0.0f;
     if constexpr (ACC) {
-      KahanSum ks;
+      KahanSum ks, ko;
 #pragma unroll
       for (int k = 0; k < VPT; ++k)
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-          const float t = exp_acc_b64(v[k][e], mx);
-          if constexpr (EPI == kEpiSoftmax) v[k][e] = t;
-          ks.add(t);
+          const float te = exp_acc_b64(v[k][e], mx);
+          if constexpr (EPI != kEpiLogSoftmax) v[k][e] = te;
+          ks.add(te);
+          if constexpr (EPI == kEpiXent) ko.add(((int64_t)k * NT + tid) * E + e == t ? 0.0f : te);
         }
       total = block_sum_pair<NW>(ks.hi(), ks.lo(), red);
+      if constexpr (EPI == kEpiXent) others = block_sum_pair<NW>(ko.hi(), ko.lo(), red);
     } else {
-      float s = 0.0f;
+      float s = 0.0f, so = 0.0f;
 #pragma unroll
       for (int k = 0; k < VPT; ++k)
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-          const float t = exp_hw_b64(v[k][e], mx);
-          if constexpr (EPI == kEpiSoftmax) v[k][e] = t;
-          s += t;
+          const float te = exp_hw_b64(v[k][e], mx);
+          if constexpr (EPI != kEpiLogSoftmax) v[k][e] = te;
+          s += te;
+          if constexpr (EPI == kEpiXent) so += ((int64_t)k * NT + tid) * E + e == t ? 0.0f : te;
         }
       total = block_sum<NW>(s, red);
+      if constexpr (EPI == kEpiXent) others = block_sum<NW>(so, red);
     }
 
-    float inv = 0.0f;  // softmax: the reciprocal 2^-64 / l
+    float inv = 0.0f;  // softmax / cross-entropy: the reciprocal 2^-64 / l
     Lse lse{0.0f, 0.0f};  // log-softmax: m + log l as hi + lo
-    if constexpr (EPI == kEpiSoftmax) {
-      inv = 1.0f / total;
-    } else {
+    if constexpr (EPI == kEpiLogSoftmax) {
       const float lsum = total * 5.42101086242752217e-20f;  // remove 2^64 (exact)
       lse = make_lse(mx, lsum);
       if (tid == 0) write_lse(a.lse, row, false, mx, lsum);
       if (a.y == nullptr) continue;
+    } else {
+      inv = 1.0f / total;
+      if constexpr (EPI == kEpiXent) {
+        if (tid == 0) {
+          a.loss[row] = xent_loss(mx, xt, others * 5.42101086242752217e-20f, total * 5.42101086242752217e-20f);
+        }
+        if (a.y == nullptr) continue;
+      }
     }
+    // cross-entropy target lane: -(others / l), correctly rounded (exactly -1
+    // when the target lane is masked)
+    const float at_t = (0.0f - others) / total;
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
       const int64_t j0 = ((int64_t)k * NT + tid) * E;
       if (j0 < cols) {
         uint32_t h[E];
 #pragma unroll
-        for (int e = 0; e < E; ++e) h[e] = enc<DT>(EPI == kEpiSoftmax ? v[k][e] * inv : minus_lse(v[k][e], lse));
+        for (int e = 0; e < E; ++e) {
+          float val;
+          if constexpr (EPI == kEpiLogSoftmax) {
+            val = minus_lse(v[k][e], lse);
+          } else {
+            val = (EPI == kEpiXent && j0 + e == t) ? at_t : v[k][e] * inv;
+          }
+          h[e] = enc<DT>(val);
+        }
         Pack<DT, E> p;
         p.put(h);
         p.template store<true>(yr + j0 * S);
@@ -193,7 +248,9 @@ hipError_t launch_epi(const RowArgs& a, int dtype, hipStream_t s) {
 int64_t lds_max_cols(int dtype) { return kMaxRowBytes / elem_size(dtype); }
 
 hipError_t launch_lds(const RowArgs& a, int dtype, int epi, hipStream_t s) {
-  return epi == kEpiSoftmax ? launch_epi<kEpiSoftmax>(a, dtype, s) : launch_epi<kEpiLogSoftmax>(a, dtype, s);
+  if (epi == kEpiSoftmax) return launch_epi<kEpiSoftmax>(a, dtype, s);
+  if (epi == kEpiLogSoftmax) return launch_epi<kEpiLogSoftmax>(a, dtype, s);
+  return launch_epi<kEpiXent>(a, dtype, s);
 }
 
 }  // namespace smx

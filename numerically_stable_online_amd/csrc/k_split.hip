@@ -35,7 +35,7 @@ constexpr int vpt_stats() {
   return E == 1 ? 8 : 4;
 }
 
-template <int DT, int E, int VPT, bool KEEP>
+template <int DT, int E, int VPT, bool KEEP, bool XENT>
 __global__ __launch_bounds__(kThreads) void k_stats(RowArgs a, int64_t chunk, int64_t nch, smx_stat* stats) {
   constexpr int S = Fmt<DT>::S;
   constexpr bool ACC = DT == kF32;
@@ -52,6 +52,18 @@ __global__ __launch_bounds__(kThreads) void k_stats(RowArgs a, int64_t chunk, in
     const int64_t lim = j_hi < prefix ? j_hi : prefix;
     const char* xr = a.x + row * a.cols * S;
     const uint8_t* kr = KEEP ? a.mask.keep + row * a.cols : nullptr;
+    // cross-entropy: the target lane stays out of the summary (its NaN/+inf
+    // still poisons the chunk) and the chunk holding it records its logit
+    const int64_t t = XENT ? row_target(a.target, row, a.cols) : -1;
+    if (XENT && t >= j_lo && t < j_hi && tid == 0) {
+      float xt = -kInf;
+      if (t < prefix && (!KEEP || kr[t] != 0)) {
+        Pack<DT, 1> q;
+        q.load(xr + t * S);
+        xt = q.get(0);
+      }
+      a.xt[row] = xt;
+    }
 
     // issue one round's loads into registers
     auto fetch = [&](int64_t base, Pack<DT, E>(&p)[VPT], uint64_t(&kb)[VPT]) {
@@ -87,8 +99,9 @@ __global__ __launch_bounds__(kThreads) void k_stats(RowArgs a, int64_t chunk, in
 #pragma unroll
         for (int e = 0; e < E; ++e) {
           const bool ok = (j0 + e < lim) && (!KEEP || keep_lane(kcur[k], e));
-          const float f = ok ? cur[k].get(e) : -kInf;
+          float f = ok ? cur[k].get(e) : -kInf;
           bad |= !(f < kInf);
+          if constexpr (XENT) f = j0 + e == t ? -kInf : f;
           mr = fmaxf(mr, f);
           v[k * E + e] = f;
         }
@@ -149,7 +162,8 @@ __global__ __launch_bounds__(kThreads) void k_merge_normalize(RowArgs a, int64_t
   for (int64_t b = blockIdx.x; b < total; b += gridDim.x) {
     const int64_t row = b / nch;
     const int64_t c = b - row * nch;
-    // with no y, only the log-sum-exp is wanted: one workgroup per row
+    // with no y, only the per-row scalars (log-sum-exp, loss) are wanted:
+    // one workgroup per row
     if (a.y == nullptr && c != 0) continue;
     const int64_t j_lo = c * chunk;
     const int64_t j_hi = j_lo + chunk < a.cols ? j_lo + chunk : a.cols;
@@ -157,6 +171,19 @@ __global__ __launch_bounds__(kThreads) void k_merge_normalize(RowArgs a, int64_t
     const int64_t lim = j_hi < prefix ? j_hi : prefix;
     const char* xr = a.x + row * a.cols * S;
     char* yr = a.y + row * a.cols * S;
+
+    // cross-entropy: an ignored row has loss 0 and gradient 0
+    const int64_t t = EPI == kEpiXent ? row_target(a.target, row, a.cols) : -1;
+    if (EPI == kEpiXent && t < 0) {
+      if (c == 0 && tid == 0) a.loss[row] = 0.0f;
+      if (a.y != nullptr) {
+        Pack<DT, E> z;
+        z.fill(0u);
+        for (int64_t j0 = j_lo + (int64_t)tid * E; j0 < j_hi; j0 += (int64_t)kThreads * E)
+          z.template store<true>(yr + j0 * S);
+      }
+      continue;
+    }
 
     // merge this row's summaries
     float m = -kInf, l = 0.0f;
@@ -170,20 +197,42 @@ __global__ __launch_bounds__(kThreads) void k_merge_normalize(RowArgs a, int64_t
       }
     }
     const bool poisoned = block_merge_flagged<kWaves>(m, l, bad, red);
+    // cross-entropy: the summaries leave out the target lane; fold it back in
+    float others = 0.0f, xt = -kInf;
+    if constexpr (EPI == kEpiXent) {
+      if (!poisoned) {
+        xt = a.xt[row];
+        const float mm = fmaxf(m, xt);
+        others = l * exp_diff(m, mm);
+        l = others + exp_diff(xt, mm);
+        m = mm;
+      }
+      if (c == 0 && tid == 0) {
+        a.loss[row] = poisoned ? u2f(0x7FC00000u) : (m == -kInf ? kInf : xent_loss(m, xt, others, l));
+      }
+      if (a.y == nullptr) continue;
+    }
     if constexpr (EPI == kEpiLogSoftmax) {
       if (c == 0 && tid == 0) write_lse(a.lse, row, poisoned, poisoned ? kInf : m, l);
       if (a.y == nullptr) continue;
     }
 
     if (poisoned || m == -kInf) {
-      Pack<DT, E> p;
-      p.fill(poisoned ? Fmt<DT>::kNaN : (EPI == kEpiSoftmax ? 0u : Fmt<DT>::kNegInf));
-      for (int64_t j0 = j_lo + (int64_t)tid * E; j0 < j_hi; j0 += (int64_t)kThreads * E) p.template store<true>(yr + j0 * S);
+      const uint32_t fill = poisoned ? Fmt<DT>::kNaN : (EPI == kEpiLogSoftmax ? Fmt<DT>::kNegInf : 0u);
+      for (int64_t j0 = j_lo + (int64_t)tid * E; j0 < j_hi; j0 += (int64_t)kThreads * E) {
+        uint32_t h[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) h[e] = (!poisoned && j0 + e == t) ? enc<DT>(-1.0f) : fill;
+        Pack<DT, E> p;
+        p.put(h);
+        p.template store<true>(yr + j0 * S);
+      }
       continue;
     }
-    // softmax: the reciprocal 2^-64 / L; log-softmax: M + log L as hi + lo
-    const float inv = EPI == kEpiSoftmax ? 1.0f / (l * 18446744073709551616.0f) : 0.0f;
-    const Lse lse = EPI == kEpiSoftmax ? Lse{0.0f, 0.0f} : make_lse(m, l);
+    // softmax / cross-entropy: the reciprocal 2^-64 / L; log-softmax: M + log L as hi + lo
+    const float inv = EPI != kEpiLogSoftmax ? 1.0f / (l * 18446744073709551616.0f) : 0.0f;
+    const Lse lse = EPI != kEpiLogSoftmax ? Lse{0.0f, 0.0f} : make_lse(m, l);
+    const float at_t = (0.0f - others) / l;  // cross-entropy target lane: -(others / L)
 
     for (int64_t base = j_lo; base < j_hi; base += kRound) {
       Pack<DT, E> in[VPT];
@@ -207,7 +256,13 @@ __global__ __launch_bounds__(kThreads) void k_merge_normalize(RowArgs a, int64_t
           for (int e = 0; e < E; ++e) {
             const bool ok = (j0 + e < lim) && (!KEEP || keep_lane(kb[k], e));
             const float f = ok ? in[k].get(e) : -kInf;
-            h[e] = enc<DT>(EPI == kEpiSoftmax ? exp_b64<ACC>(f, m) * inv : minus_lse(f, lse));
+            float val;
+            if constexpr (EPI == kEpiLogSoftmax) {
+              val = minus_lse(f, lse);
+            } else {
+              val = (EPI == kEpiXent && j0 + e == t) ? at_t : exp_b64<ACC>(f, m) * inv;
+            }
+            h[e] = enc<DT>(val);
           }
           Pack<DT, E> out;
           out.put(h);
@@ -221,14 +276,22 @@ __global__ __launch_bounds__(kThreads) void k_merge_normalize(RowArgs a, int64_t
 constexpr int64_t kMaxGrid = 1 << 20;
 
 template <int DT, int E>
-hipError_t launch_stats_t(const RowArgs& a, int64_t chunk, int64_t nch, smx_stat* stats, hipStream_t s) {
+hipError_t launch_stats_t(const RowArgs& a, bool xent, int64_t chunk, int64_t nch, smx_stat* stats, hipStream_t s) {
   constexpr int VPT = vpt_stats<DT, E>();
   const int64_t total = a.rows * nch;
   const unsigned grid = (unsigned)(total < kMaxGrid ? total : kMaxGrid);
   if (a.mask.kind == kMaskKeep) {
-    hipLaunchKernelGGL((k_stats<DT, E, VPT, true>), dim3(grid), dim3(kThreads), 0, s, a, chunk, nch, stats);
+    if (xent) {
+      hipLaunchKernelGGL((k_stats<DT, E, VPT, true, true>), dim3(grid), dim3(kThreads), 0, s, a, chunk, nch, stats);
+    } else {
+      hipLaunchKernelGGL((k_stats<DT, E, VPT, true, false>), dim3(grid), dim3(kThreads), 0, s, a, chunk, nch, stats);
+    }
   } else {
-    hipLaunchKernelGGL((k_stats<DT, E, VPT, false>), dim3(grid), dim3(kThreads), 0, s, a, chunk, nch, stats);
+    if (xent) {
+      hipLaunchKernelGGL((k_stats<DT, E, VPT, false, true>), dim3(grid), dim3(kThreads), 0, s, a, chunk, nch, stats);
+    } else {
+      hipLaunchKernelGGL((k_stats<DT, E, VPT, false, false>), dim3(grid), dim3(kThreads), 0, s, a, chunk, nch, stats);
+    }
   }
   return hipGetLastError();
 }
@@ -266,23 +329,26 @@ int64_t split_round_cols(int dtype, bool vec) {
   return (int64_t)kThreads * 8 * vec_elems(dtype);
 }
 
-hipError_t launch_stats(const RowArgs& a, int dtype, bool vec, int64_t chunk, int64_t nch, smx_stat* stats,
+hipError_t launch_stats(const RowArgs& a, int dtype, bool vec, bool xent, int64_t chunk, int64_t nch, smx_stat* stats,
                         hipStream_t s) {
   switch (dtype) {
     case kF32:
-      return vec ? launch_stats_t<kF32, 4>(a, chunk, nch, stats, s) : launch_stats_t<kF32, 1>(a, chunk, nch, stats, s);
+      return vec ? launch_stats_t<kF32, 4>(a, xent, chunk, nch, stats, s)
+                 : launch_stats_t<kF32, 1>(a, xent, chunk, nch, stats, s);
     case kF16:
-      return vec ? launch_stats_t<kF16, 8>(a, chunk, nch, stats, s) : launch_stats_t<kF16, 1>(a, chunk, nch, stats, s);
+      return vec ? launch_stats_t<kF16, 8>(a, xent, chunk, nch, stats, s)
+                 : launch_stats_t<kF16, 1>(a, xent, chunk, nch, stats, s);
     default:
-      return vec ? launch_stats_t<kBF16, 8>(a, chunk, nch, stats, s)
-                 : launch_stats_t<kBF16, 1>(a, chunk, nch, stats, s);
+      return vec ? launch_stats_t<kBF16, 8>(a, xent, chunk, nch, stats, s)
+                 : launch_stats_t<kBF16, 1>(a, xent, chunk, nch, stats, s);
   }
 }
 
 hipError_t launch_merge_normalize(const RowArgs& a, int dtype, bool vec, int epi, int64_t chunk, int64_t nch,
                                   const smx_stat* stats, hipStream_t s) {
-  return epi == kEpiSoftmax ? launch_mn_epi<kEpiSoftmax>(a, dtype, vec, chunk, nch, stats, s)
-                            : launch_mn_epi<kEpiLogSoftmax>(a, dtype, vec, chunk, nch, stats, s);
+  if (epi == kEpiSoftmax) return launch_mn_epi<kEpiSoftmax>(a, dtype, vec, chunk, nch, stats, s);
+  if (epi == kEpiLogSoftmax) return launch_mn_epi<kEpiLogSoftmax>(a, dtype, vec, chunk, nch, stats, s);
+  return launch_mn_epi<kEpiXent>(a, dtype, vec, chunk, nch, stats, s);
 }
 
 }  // namespace smx

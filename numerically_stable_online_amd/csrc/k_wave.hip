@@ -72,66 +72,99 @@ __global__ __launch_bounds__(kThreads) void k_wave(RowArgs a) {
     // exactly when its maximum is +inf, so one reduction carries both
     const float m = wave_max(bad[r] ? kInf : mx[r]);
     const bool poisoned = m == kInf;
+
+    // cross-entropy: the row's target lane (-1: ignored row) and its logit
+    int64_t t = -1;
+    float xt = -kInf;
+    if constexpr (EPI == kEpiXent) {
+      t = row_target(a.target, row, cols);
+      if (t < 0) {  // ignored row: loss 0, gradient 0
+        if (lane == 0) a.loss[row] = 0.0f;
+        if (a.y != nullptr) {
+          Pack<DT, E> z;
+          z.fill(0u);
+#pragma unroll
+          for (int k = 0; k < VPT; ++k) {
+            const int64_t j0 = (int64_t)(k * 64 + lane) * E;
+            if (j0 < cols) z.template store<true>(yr + j0 * S);
+          }
+        }
+        continue;
+      }
+      if (t < prefix[r] && (!KEEP || a.mask.keep[row * cols + t] != 0)) {
+        Pack<DT, 1> q;
+        q.load(a.x + (row * cols + t) * S);
+        xt = q.get(0);
+      }
+    }
+
     if (poisoned || m == -kInf) {
-      // declared policy rows: canonical NaN, or the empty row (all +0.0, or
-      // all -inf for log-probabilities) with no -inf - -inf
+      // declared policy rows: canonical NaN, or the empty row (all +0.0; all
+      // -inf for log-probabilities; -onehot(t) and an infinite loss for the
+      // cross-entropy) with no -inf - -inf
       if constexpr (EPI == kEpiLogSoftmax) {
         if (lane == 0) write_lse(a.lse, row, poisoned, m, 0.0f);
       }
+      if constexpr (EPI == kEpiXent) {
+        if (lane == 0) a.loss[row] = poisoned ? u2f(0x7FC00000u) : kInf;
+      }
       if (a.y != nullptr) {
-        Pack<DT, E> p;
-        p.fill(poisoned ? Fmt<DT>::kNaN : (EPI == kEpiSoftmax ? 0u : Fmt<DT>::kNegInf));
+        const uint32_t fill = poisoned ? Fmt<DT>::kNaN : (EPI == kEpiLogSoftmax ? Fmt<DT>::kNegInf : 0u);
 #pragma unroll
         for (int k = 0; k < VPT; ++k) {
           const int64_t j0 = (int64_t)(k * 64 + lane) * E;
-          if (j0 < cols) p.template store<true>(yr + j0 * S);
+          if (j0 < cols) {
+            uint32_t h[E];
+#pragma unroll
+            for (int e = 0; e < E; ++e) h[e] = (!poisoned && j0 + e == t) ? enc<DT>(-1.0f) : fill;
+            Pack<DT, E> p;
+            p.put(h);
+            p.template store<true>(yr + j0 * S);
+          }
         }
       }
       continue;
     }
 
     // exp(x - m) * 2^64 and its sum; masked lanes give exactly 0. The
-    // softmax keeps the exponentials for its stores; log-softmax only sums.
-    float total;
+    // softmax and the cross-entropy keep the exponentials for their stores;
+    // the cross-entropy also sums the lanes other than the target.
+    float total, others = 0.0f;
     if constexpr (ACC) {
-      KahanSum ks;
+      KahanSum ks, ko;
 #pragma unroll
       for (int k = 0; k < VPT; ++k)
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-          const float t = exp_acc_b64(v[r][k][e], m);
-          if constexpr (EPI == kEpiSoftmax) v[r][k][e] = t;
-          ks.add(t);
+          const float te = exp_acc_b64(v[r][k][e], m);
+          if constexpr (EPI != kEpiLogSoftmax) v[r][k][e] = te;
+          ks.add(te);
+          if constexpr (EPI == kEpiXent) {
+            const int64_t j = (int64_t)(k * 64 + lane) * E + e;
+            ko.add(j == t ? 0.0f : te);
+          }
         }
       total = wave_sum_pair(ks.hi(), ks.lo());
+      if constexpr (EPI == kEpiXent) others = wave_sum_pair(ko.hi(), ko.lo());
     } else {
-      float s = 0.0f;
+      float s = 0.0f, so = 0.0f;
 #pragma unroll
       for (int k = 0; k < VPT; ++k)
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-          const float t = exp_hw_b64(v[r][k][e], m);
-          if constexpr (EPI == kEpiSoftmax) v[r][k][e] = t;
-          s += t;
+          const float te = exp_hw_b64(v[r][k][e], m);
+          if constexpr (EPI != kEpiLogSoftmax) v[r][k][e] = te;
+          s += te;
+          if constexpr (EPI == kEpiXent) {
+            const int64_t j = (int64_t)(k * 64 + lane) * E + e;
+            so += j == t ? 0.0f : te;
+          }
         }
       total = wave_sum(s);
+      if constexpr (EPI == kEpiXent) others = wave_sum(so);
     }
 
-    if constexpr (EPI == kEpiSoftmax) {
-      const float inv = 1.0f / total;  // 2^-64 / l
-#pragma unroll
-      for (int k = 0; k < VPT; ++k) {
-        const int64_t j0 = (int64_t)(k * 64 + lane) * E;
-        if (j0 < cols) {
-          uint32_t h[E];
-#pragma unroll
-          for (int e = 0; e < E; ++e) h[e] = enc<DT>(v[r][k][e] * inv);
-          Pack<DT, E> p;
-          p.put(h);
-          p.template store<true>(yr + j0 * S);
-        }
-      }
-    } else {
+    if constexpr (EPI == kEpiLogSoftmax) {
       // log-softmax: y = x - (m + log l); masked and -inf lanes stay -inf
       const float lsum = total * 5.42101086242752217e-20f;  // remove 2^64 (exact)
       const Lse lse = make_lse(m, lsum);
@@ -148,6 +181,32 @@ __global__ __launch_bounds__(kThreads) void k_wave(RowArgs a) {
             p.put(h);
             p.template store<true>(yr + j0 * S);
           }
+        }
+      }
+    } else {
+      const float inv = 1.0f / total;  // 2^-64 / l
+      if constexpr (EPI == kEpiXent) {
+        if (lane == 0) {
+          a.loss[row] = xent_loss(m, xt, others * 5.42101086242752217e-20f, total * 5.42101086242752217e-20f);
+        }
+        if (a.y == nullptr) continue;
+      }
+      // the target lane of the cross-entropy gradient: p_t - 1 = -(others / l)
+      // (a correctly rounded divide: exactly -1 when the target lane is masked)
+      const float at_t = (0.0f - others) / total;
+#pragma unroll
+      for (int k = 0; k < VPT; ++k) {
+        const int64_t j0 = (int64_t)(k * 64 + lane) * E;
+        if (j0 < cols) {
+          uint32_t h[E];
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            const float val = (EPI == kEpiXent && j0 + e == t) ? at_t : v[r][k][e] * inv;
+            h[e] = enc<DT>(val);
+          }
+          Pack<DT, E> p;
+          p.put(h);
+          p.template store<true>(yr + j0 * S);
         }
       }
     }
@@ -202,8 +261,9 @@ hipError_t launch_epi(const RowArgs& a, int dtype, bool vec, hipStream_t stream)
 int64_t wave_max_cols(int dtype, bool vec) { return vec ? 64 * 8 * vec_elems(dtype) : 64 * 32; }
 
 hipError_t launch_wave(const RowArgs& a, int dtype, bool vec, int epi, hipStream_t stream) {
-  return epi == kEpiSoftmax ? launch_epi<kEpiSoftmax>(a, dtype, vec, stream)
-                            : launch_epi<kEpiLogSoftmax>(a, dtype, vec, stream);
+  if (epi == kEpiSoftmax) return launch_epi<kEpiSoftmax>(a, dtype, vec, stream);
+  if (epi == kEpiLogSoftmax) return launch_epi<kEpiLogSoftmax>(a, dtype, vec, stream);
+  return launch_epi<kEpiXent>(a, dtype, vec, stream);
 }
 
 }  // namespace smx

@@ -109,15 +109,19 @@ int64_t default_chunk(int64_t rows, int64_t cols, int dtype, bool vec) {
   return chunk;
 }
 
-int run_split(const Call& c, int64_t chunk, int epi, hipStream_t stream) {
+int run_split(const Call& c0, int64_t chunk, int epi, hipStream_t stream) {
+  Call c = c0;
   const int64_t e = vec_elems(c.dtype);
   const bool vec = c.vec && chunk % e == 0;
   const int64_t nch = (c.a.cols + chunk - 1) / chunk;
+  // workspace: the chunk summaries, then (cross-entropy) one target logit per row
+  const size_t stat_bytes = (size_t)(c.a.rows * nch) * sizeof(smx_stat);
+  const size_t bytes = stat_bytes + (epi == kEpiXent ? (size_t)c.a.rows * sizeof(float) : 0);
   void* ws = nullptr;
-  const size_t bytes = (size_t)(c.a.rows * nch) * sizeof(smx_stat);
   hipError_t err = hipMallocAsync(&ws, bytes, stream);
   if (err != hipSuccess) return hip_fail(err, "hipMallocAsync of the summary workspace");
-  err = launch_stats(c.a, c.dtype, vec, chunk, nch, (smx_stat*)ws, stream);
+  if (epi == kEpiXent) c.a.xt = (float*)((char*)ws + stat_bytes);
+  err = launch_stats(c.a, c.dtype, vec, epi == kEpiXent, chunk, nch, (smx_stat*)ws, stream);
   if (err == hipSuccess) err = launch_merge_normalize(c.a, c.dtype, vec, epi, chunk, nch, (const smx_stat*)ws, stream);
   const hipError_t ferr = hipFreeAsync(ws, stream);
   if (err != hipSuccess) return hip_fail(err, "split-path launch");
@@ -198,7 +202,7 @@ int softmax_row_stats(const void* x, int64_t rows, int64_t cols, smx_dtype dtype
   if (rows > 0 && nch > 0 && stats == nullptr) return fail(SMX_EINVAL, "stats is NULL");
   if (rows == 0 || cols == 0) return ok();
   const bool vec = c.vec && chunk_cols % vec_elems(c.dtype) == 0;
-  hipError_t err = launch_stats(c.a, c.dtype, vec, chunk_cols, nch, stats, (hipStream_t)stream);
+  hipError_t err = launch_stats(c.a, c.dtype, vec, false, chunk_cols, nch, stats, (hipStream_t)stream);
   if (err != hipSuccess) return hip_fail(err, "stats launch");
   return ok();
 }
@@ -251,6 +255,38 @@ int log_softmax_rows_path(const void* x, void* y, float* lse, int64_t rows, int6
 int log_softmax_rows(const void* x, void* y, float* lse, int64_t rows, int64_t cols, smx_dtype dtype,
                      const smx_mask* mask, void* stream) {
   return log_softmax_rows_path(x, y, lse, rows, cols, dtype, mask, SMX_PATH_AUTO, 0, stream);
+}
+
+int softmax_cross_entropy_rows_path(const void* x, const int32_t* target, float* loss, void* dx, int64_t rows,
+                                    int64_t cols, smx_dtype dtype, const smx_mask* mask, smx_path path,
+                                    int64_t chunk_cols, void* stream) {
+  Call c;
+  if (int rc = check_common(x, dx, rows, cols, (int)dtype, mask, dx != nullptr, c)) return rc;
+  if ((int)path < SMX_PATH_AUTO || (int)path > SMX_PATH_SPLIT) return fail(SMX_EINVAL, "path %d is not a smx_path", (int)path);
+  if (chunk_cols < 0) return fail(SMX_EINVAL, "chunk_cols must be >= 0");
+  if (rows > 0 && (target == nullptr || loss == nullptr)) return fail(SMX_EINVAL, "target and loss must not be NULL");
+  if (rows > 0) {
+    const uintptr_t la = (uintptr_t)loss, lb = (uintptr_t)(rows * 4);
+    const uintptr_t xb = (uintptr_t)(rows * cols * elem_size((int)dtype));
+    const uintptr_t xa = (uintptr_t)x, ya = (uintptr_t)dx;
+    if (xb > 0 && ((la < xa + xb && xa < la + lb) || (dx != nullptr && la < ya + xb && ya < la + lb)))
+      return fail(SMX_EINVAL, "loss overlaps x or dx");
+  }
+  c.a.target = target;
+  c.a.loss = loss;
+  if (rows == 0) return ok();
+  if (cols == 0) {
+    // every target is out of range: every row is ignored (loss 0)
+    hipError_t err = launch_wave(c.a, c.dtype, false, kEpiXent, (hipStream_t)stream);
+    if (err != hipSuccess) return hip_fail(err, "kernel launch");
+    return ok();
+  }
+  return run_rows(c, path, chunk_cols, kEpiXent, (hipStream_t)stream);
+}
+
+int softmax_cross_entropy_rows(const void* x, const int32_t* target, float* loss, void* dx, int64_t rows,
+                               int64_t cols, smx_dtype dtype, const smx_mask* mask, void* stream) {
+  return softmax_cross_entropy_rows_path(x, target, loss, dx, rows, cols, dtype, mask, SMX_PATH_AUTO, 0, stream);
 }
 
 int softmax_backward_rows_path(const void* p, const void* g, void* dx, int64_t rows, int64_t cols, smx_dtype dtype,

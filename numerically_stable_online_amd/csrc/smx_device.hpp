@@ -246,6 +246,22 @@ __device__ __forceinline__ Lse make_lse(float m, float lsum) {
 }
 __device__ __forceinline__ float minus_lse(float x, const Lse& s) { return (x - s.hi) - s.lo; }
 
+// The cross-entropy of a row from its maximum m, the target logit xt, the
+// sum of the other lanes' exp(x - m) ("others") and of all lanes ("all"),
+// both unscaled: LSE - xt = (m - xt) + log(all), or, when the target holds
+// the maximum, log1p(others), which keeps a confident prediction's tiny loss
+// exact to fp32 precision instead of cancelling.
+__device__ __forceinline__ float xent_loss(float m, float xt, float others, float all) {
+  return xt == m ? log1pf(others) : (m - xt) + log_l(all);
+}
+
+// The target lane of a row, or -1 when the row is ignored (target outside
+// [0, cols)).
+__device__ __forceinline__ int64_t row_target(const int32_t* target, int64_t row, int64_t cols) {
+  const int64_t t = target[row];
+  return (t >= 0 && t < cols) ? t : -1;
+}
+
 // The epilogue's per-row scalar for the log-softmax outputs.
 __device__ __forceinline__ void write_lse(float* lse, int64_t row, bool poisoned, float m, float lsum) {
   if (lse == nullptr) return;

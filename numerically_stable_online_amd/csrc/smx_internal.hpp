@@ -32,8 +32,11 @@ struct MaskArgs {
 
 struct RowArgs {
   const char* x;
-  char* y;       // may be null for the log-sum-exp-only epilogue
-  float* lse;    // per-row log-sum-exp, or null
+  char* y;                // may be null (log-sum-exp only, loss only)
+  float* lse;             // per-row log-sum-exp, or null
+  const int32_t* target;  // cross-entropy: per-row target lane
+  float* loss;            // cross-entropy: per-row loss
+  float* xt;              // cross-entropy on the split path: per-row target logit
   int64_t rows;
   int64_t cols;
   MaskArgs mask;
@@ -42,6 +45,7 @@ struct RowArgs {
 // What the kernels write once a row's (m, l) is known.
 constexpr int kEpiSoftmax = 0;     // y = exp(x - m) / l
 constexpr int kEpiLogSoftmax = 1;  // y = x - (m + log l), and/or lse = m + log l
+constexpr int kEpiXent = 2;        // loss = LSE - x_t, y = p - onehot(t)
 
 inline int elem_size(int dtype) { return dtype == kF32 ? 4 : 2; }
 // elements per 128-bit access
@@ -59,7 +63,9 @@ hipError_t launch_lds(const RowArgs& a, int dtype, int epi, hipStream_t stream);
 // --- split path (k_split.hip) ---
 // Elements one workgroup holds per round of a chunk.
 int64_t split_round_cols(int dtype, bool vec);
-hipError_t launch_stats(const RowArgs& a, int dtype, bool vec, int64_t chunk_cols, int64_t n_chunks,
+// xent: the target lane is left out of the summaries and its logit is
+// written to a.xt
+hipError_t launch_stats(const RowArgs& a, int dtype, bool vec, bool xent, int64_t chunk_cols, int64_t n_chunks,
                         smx_stat* stats, hipStream_t stream);
 hipError_t launch_merge_normalize(const RowArgs& a, int dtype, bool vec, int epi, int64_t chunk_cols,
                                   int64_t n_chunks, const smx_stat* stats, hipStream_t stream);

@@ -194,3 +194,83 @@ def check_bwd(dx_raw, dtype, ref, p_f64, g_f64, what=""):
     far = np.abs(r) >= 2.0 ** -8 * scale
     return {"max_ulp": int(d.max()) if d.size else 0,
             "max_ulp_without_cancellation": int(d[far].max()) if far.any() else 0}
+
+
+# ---------------------------------------------------------------------------
+# Cross-entropy with logits (loss_r = LSE - x_t, dx = p - onehot(t))
+# ---------------------------------------------------------------------------
+#
+# loss (fp32): |loss - r| <= 1e-6 * max(|r|, a), with a = 0 when the target
+#   holds the row maximum (the log1p form keeps full relative precision) and
+#   a = 1 otherwise (the fp32 resolution of m - x_t + log l);
+# dx: the softmax bars (f32 relative 1e-6 with the 2^-126 floor, f16/bf16
+#   1 ulp), the target lane included (its value -(others / l) is accurate);
+# policy: ignored rows loss 0 and dx +0.0; poisoned rows NaN; an empty row or
+#   a masked / -inf target gives loss +inf; policy lanes of dx bit-exact
+#   (+0.0, or -1.0 at the target of an empty row).
+
+XENT_TOL = 1e-6
+
+
+def check_xent(loss_got, dx_raw, dtype, loss_ref, dx_ref, x_float, target, what=""):
+    rows, cols = x_float.shape
+    t = target.astype(np.int64)
+    ignored = (t < 0) | (t >= cols)
+    lr = loss_ref
+    assert (loss_got[ignored] == 0).all(), f"{what}: ignored rows need loss 0"
+    nanr = np.isnan(lr)
+    assert (loss_got[nanr].view(np.uint32) == 0x7FC00000).all(), f"{what}: poisoned rows need the canonical NaN"
+    infr = lr == np.inf
+    assert (loss_got[infr] == np.inf).all(), f"{what}: rows with an unreachable target need +inf"
+    num = ~(ignored | nanr | infr)
+    out = {}
+    if num.any():
+        rows_i = np.nonzero(num)[0]
+        xt = x_float[rows_i, t[rows_i]].astype(np.float64)
+        rowmax = np.nanmax(np.where(np.isfinite(x_float[rows_i]), x_float[rows_i], -np.inf), axis=1)
+        a = np.where(xt == rowmax, 0.0, 1.0)
+        err = np.abs(loss_got[rows_i].astype(np.float64) - lr[rows_i])
+        bound = XENT_TOL * np.maximum(np.abs(lr[rows_i]), a)
+        bad = err > bound
+        if bad.any():
+            i = rows_i[np.argmax(bad)]
+            raise AssertionError(f"{what}: loss row {i}: got {loss_got[i]!r} want {lr[i]!r}")
+        out["loss_max_err_ratio"] = float((err / np.maximum(bound, 1e-300)).max())
+    if dx_raw is None:
+        return out
+    bits = bits_of(dx_raw, dtype)
+    zero_bits = 0
+    assert (bits[ignored] == zero_bits).all(), f"{what}: ignored rows need dx = +0.0"
+    assert (bits[nanr] == NAN_BITS[dtype]).all(), f"{what}: poisoned rows need NaN dx"
+    live = ~(ignored | nanr)
+    # lanes whose reference is exactly 0 or -1 (masked lanes, empty rows) are
+    # policy values and must match bit for bit
+    exact = live[:, None] & ((dx_ref == 0) | (dx_ref == -1)) & (np.abs(dx_ref) >= 0)
+    want_bits = bits_of(oracle.encode(np.where(exact, dx_ref, 0.0), dtype), dtype)
+    mism = exact & (bits != want_bits)
+    # a numeric lane may round to exactly 0 or -1 legitimately; only lanes the
+    # oracle puts at exactly 0 / -1 are held to bits, and those are policy
+    # lanes or exact results (one valid lane: dx_t = 0)
+    if mism.any():
+        i = tuple(np.argwhere(mism)[0])
+        raise AssertionError(f"{what}: policy lane {i} got {bits[i]:#x} want {want_bits[i]:#x}")
+    numl = live[:, None] & ~exact
+    if dtype == "f32":
+        y = dx_raw.astype(np.float64)
+        rel = np.zeros_like(dx_ref)
+        rel[numl] = np.abs(y[numl] - dx_ref[numl]) / np.maximum(np.abs(dx_ref[numl]), FLT_MIN)
+        worst = float(rel.max()) if rel.size else 0.0
+        if worst > F32_REL_TOL:
+            i = np.unravel_index(np.argmax(rel), rel.shape)
+            raise AssertionError(f"{what}: dx relative error {worst:.3e} at {i}: got {y[i]!r} want {dx_ref[i]!r}")
+        out["dx_max_rel"] = worst
+    else:
+        want = oracle.encode(np.where(numl, dx_ref, 0.0), dtype).astype(np.int64)
+        d = np.abs(bits - want)
+        d[~numl] = 0
+        worst = int(d.max()) if d.size else 0
+        if worst > ULP_TOL:
+            i = np.unravel_index(np.argmax(d), d.shape)
+            raise AssertionError(f"{what}: dx {worst} ulp at {i}: got {bits[i]:#06x} want {want[i]:#06x} (ref {dx_ref[i]!r})")
+        out["dx_max_ulp"] = worst
+    return out

@@ -36,7 +36,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("softmax_rows", "softmax_rows_path", "softmax_row_stats", "softmax_merge_normalize",
               "log_softmax_rows", "log_softmax_rows_path", "softmax_backward_rows",
-              "softmax_backward_rows_path",
+              "softmax_backward_rows_path", "softmax_cross_entropy_rows", "softmax_cross_entropy_rows_path",
               "softmax_default_chunk_cols", "softmax_select_path", "smx_last_error"):
         assert n in names, names
 

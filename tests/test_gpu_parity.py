@@ -529,3 +529,92 @@ def test_backward_in_place_and_deterministic():
     b = run_bwd(p_raw, g_raw, "bf16", inplace=True)
     assert np.array_equal(a, b)
     check_bwd_full(p_raw, g_raw, "bf16", a, "backward in place")
+
+
+# ---------------------------------------------------------------------------
+# Cross-entropy with logits
+# ---------------------------------------------------------------------------
+
+from smx_compare import check_xent  # noqa: E402
+
+
+def xent_targets(rows, cols, seed, confident_x=None):
+    rng = np.random.default_rng(seed)
+    t = rng.integers(0, cols, rows).astype(np.int32)
+    return t
+
+
+def run_xent(x_raw, dtype, target, mask=None, path="auto", chunk_cols=0, want_dx=True, inplace=False,
+             misalign=False):
+    rows, cols = x_raw.shape
+    if misalign:
+        buf = torch.empty(rows * cols + 1, dtype=TORCH_DTYPE[dtype], device="cuda")
+        x = buf[1:].view(rows, cols)
+        x.copy_(to_device(x_raw, dtype))
+    else:
+        x = to_device(x_raw, dtype)
+    t = torch.from_numpy(np.ascontiguousarray(target, dtype=np.int32)).cuda()
+    dx = x if inplace else None
+    loss, g = smx.softmax_cross_entropy_rows(x, t, dx=dx, want_dx=want_dx, path=path, chunk_cols=chunk_cols,
+                                             **mask_kwargs(mask))
+    torch.cuda.synchronize()
+    return loss.cpu().numpy(), (to_host(g, dtype) if want_dx else None)
+
+
+def check_xent_full(x_raw, dtype, target, mask, loss, dx, what):
+    lr, dref = oracle.cross_entropy_rows(x_raw, dtype, target, mask)
+    return check_xent(loss, dx, dtype, lr, dref, W.to_float(x_raw, dtype), target, what)
+
+
+@pytest.mark.parametrize("cfg,path", [(1, "auto"), (1, "wave"), (1, "lds"), (1, "split"), (2, "auto"),
+                                      (2, "split"), (3, "auto"), (3, "split"), (4, "auto")])
+def test_cross_entropy_workloads(cfg, path):
+    w = W.CONFIGS[cfg]()
+    t = xent_targets(w.rows, w.cols, seed=300 + cfg)
+    t[::17] = -1  # ignored rows
+    banner(f"xent config{cfg} {path}")
+    loss, dx = run_xent(w.x, w.dtype, t, w.mask, path=path)
+    r = check_xent_full(w.x, w.dtype, t, w.mask, loss, dx, f"xent config{cfg}/{path}")
+    banner(f"xent config{cfg} {path}: {r}")
+    loss2, _ = run_xent(w.x, w.dtype, t, w.mask, path=path, want_dx=False)
+    assert np.array_equal(loss2.view(np.uint32), loss.view(np.uint32))  # loss alone: the same bits
+
+
+@pytest.mark.parametrize("dtype", W.DTYPES)
+def test_cross_entropy_confident_and_policy(dtype):
+    rng = np.random.default_rng(301)
+    for cols in (2, 7, 64, 1000, 4096, 20000):
+        rows = 12
+        a = rng.standard_normal((rows, cols)) * 3
+        t = rng.integers(0, cols, rows).astype(np.int32)
+        a[np.arange(rows), t] = a.max(1) + 30.0  # p_t = 1 - O(e^-30): a tiny loss
+        x = W.to_format(a, dtype)
+        W.set_bits(x, 3, (int(t[3]) + 1) % cols, dtype, W.QNAN[dtype])  # poisoned row
+        t[4] = -5
+        t[5] = cols  # ignored rows
+        valid = np.full(rows, cols, dtype=np.int32)
+        valid[6] = 0  # empty row
+        valid[7] = int(t[7])  # the target is masked
+        mask = W.MaskSpec("valid_len", valid_len=valid)
+        for misalign in (False, True):
+            for path in _paths(dtype, cols, misalign):
+                what = f"xent confident {dtype} cols={cols} {path} misalign={misalign}"
+                banner(what)
+                loss, dx = run_xent(x, dtype, t, mask, path=path, chunk_cols=300 if path == "split" else 0,
+                                    misalign=misalign)
+                check_xent_full(x, dtype, t, mask, loss, dx, what)
+
+
+def test_cross_entropy_in_place():
+    w = W.config4(rows=4, cols=1 << 16)
+    t = xent_targets(4, 1 << 16, seed=9)
+    for path in ("split", "auto"):
+        loss, dx = run_xent(w.x, "f32", t, path=path)
+        loss2, dx2 = run_xent(w.x, "f32", t, path=path, inplace=True)
+        assert np.array_equal(loss, loss2) and np.array_equal(dx, dx2)
+    w = W.config2(rows=64)
+    t = xent_targets(64, 4096, seed=10)
+    loss, dx = run_xent(w.x, "bf16", t)
+    loss2, dx2 = run_xent(w.x, "bf16", t, inplace=True)
+    assert np.array_equal(loss, loss2) and np.array_equal(dx, dx2)
+    check_xent_full(w.x, "bf16", t, w.mask, loss, dx, "xent in place")
