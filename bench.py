@@ -56,7 +56,8 @@ def parse():
                     help="workloads to time; the first is the headline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--next-ops", default="2,4",
-                    help="workloads on which the log-softmax entry point is also timed ('' for none)")
+                    help="workloads on which the log-softmax, softmax-backward and cross-entropy "
+                         "entry points are also timed ('' for none)")
     ap.add_argument("--no-spread", action="store_true",
                     help="skip the single-launch spread loop (profiling runs)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -147,6 +148,17 @@ def time_workload(w, steps: int, warmup: int, calibrate_copy: bool = False, spre
 
         def call(i):
             smx.softmax_backward_rows(xs[i % copies], xs[(i + 1) % copies], ys[i % copies])
+    elif op == "softmax_cross_entropy_rows":
+        import workloads as W
+
+        tgt = torch.from_numpy(W.class_targets(w.rows, w.cols, w.seed)).cuda()
+        losses = [torch.empty(w.rows, dtype=torch.float32, device=x0.device) for _ in range(copies)]
+        nbytes += 4 * w.rows + 4 * w.rows  # the targets read and the losses written
+        if path == "split":
+            nbytes += 2 * 4 * w.rows  # the target logit passed between the two kernels
+
+        def call(i):
+            smx.softmax_cross_entropy_rows(xs[i % copies], tgt, losses[i % copies], ys[i % copies], **kw)
     else:
         raise ValueError(op)
 
@@ -264,7 +276,7 @@ def main():
     next_ops = {}
     for k2 in [int(c) for c in args.next_ops.split(",") if c]:
         w2 = make_workload(k2)
-        for op in ("log_softmax_rows", "softmax_backward_rows"):
+        for op in ("log_softmax_rows", "softmax_backward_rows", "softmax_cross_entropy_rows"):
             r2 = time_workload(w2, args.steps, args.warmup, spread=False, op=op)
             g2 = r2["bytes"] / (r2["gpu_ms_per_launch"] * 1e-3) / 1e9
             next_ops.setdefault(op, {})[f"config{k2}"] = {

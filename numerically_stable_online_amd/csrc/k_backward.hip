@@ -26,10 +26,9 @@ struct BwdArgs {
   int64_t cols;
 };
 
-template <int DT>
-__device__ __forceinline__ uint32_t enc_any(float v) {
-  return v != v ? Fmt<DT>::kNaN : enc<DT>(v);
-}
+// a NaN result becomes the canonical quiet NaN before rounding (0x7FC00000
+// rounds to the canonical fp16 / bf16 NaN)
+__device__ __forceinline__ float canon(float v) { return v != v ? u2f(0x7FC00000u) : v; }
 
 // one workgroup of NT threads per row (NT = 64: one wave per row)
 template <int DT, int E, int NT, int VPT>
@@ -69,11 +68,11 @@ __global__ __launch_bounds__(NT) void k_bwd_rows(BwdArgs a) {
     for (int k = 0; k < VPT; ++k) {
       const int64_t j0 = ((int64_t)k * NT + tid) * E;
       if (j0 < a.cols) {
-        uint32_t h[E];
+        float o[E];
 #pragma unroll
-        for (int e = 0; e < E; ++e) h[e] = enc_any<DT>(pv[k][e] * (gv[k][e] - s));
+        for (int e = 0; e < E; ++e) o[e] = canon(pv[k][e] * (gv[k][e] - s));
         Pack<DT, E> out;
-        out.put(h);
+        out.put_values(o);
         out.template store<true>(a.dx + (base + j0) * S);
       }
     }
@@ -175,11 +174,11 @@ __global__ __launch_bounds__(kThreads) void k_bwd_apply(BwdArgs a, int64_t chunk
       for (int k = 0; k < VPT; ++k) {
         const int64_t j0 = r0 + ((int64_t)k * kThreads + tid) * E;
         if (j0 < j_hi) {
-          uint32_t h[E];
+          float o[E];
 #pragma unroll
-          for (int e = 0; e < E; ++e) h[e] = enc_any<DT>(pp[k].get(e) * (gg[k].get(e) - s));
+          for (int e = 0; e < E; ++e) o[e] = canon(pp[k].get(e) * (gg[k].get(e) - s));
           Pack<DT, E> out;
-          out.put(h);
+          out.put_values(o);
           out.template store<true>(a.dx + (base + j0) * S);
         }
       }

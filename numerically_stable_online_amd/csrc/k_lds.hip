@@ -34,6 +34,10 @@ __global__ __launch_bounds__(NT) void k_lds(RowArgs a) {
     const int64_t prefix = valid_prefix(a.mask, row, cols);
     const char* xr = a.x + row * cols * S;
     char* yr = a.y + row * cols * S;
+    // cross-entropy: the row's target lane (-1: ignored row), read before the
+    // row is staged so its latency overlaps the copy
+    const int64_t t = EPI == kEpiXent ? row_target(a.target, row, cols) : -1;
+    const int slot = target_slot<NT, E>(t, tid);
 
     // stage the valid prefix: wave w copies pieces w, w + 4, ...
     const int64_t nvec = (prefix + E - 1) / E;
@@ -48,45 +52,54 @@ __global__ __launch_bounds__(NT) void k_lds(RowArgs a) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
+    // packs out of LDS; masked lanes become -inf. A pack holds `rem` valid
+    // lanes (E inside the prefix, 0 past it), so each lane's test is a 32-bit
+    // compare with a constant.
     float v[VPT][E];
     float mx = -kInf;
-    bool bad = false;
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
       const int64_t vi = (int64_t)k * NT + tid;
-      const int64_t j0 = vi * E;
+      const int64_t left = prefix - vi * E;
+      const int rem = left <= 0 ? 0 : (left >= E ? E : (int)left);
       Pack<DT, E> p;
       p.fill(0);
       uint64_t kb = ~0ull;
-      const bool ld = j0 < prefix;
-      if (ld) {
+      if (rem > 0) {
         const uint4 w = *reinterpret_cast<const uint4*>(row_lds + vi * 16);
         p.w[0] = w.x;
         p.w[1] = w.y;
         p.w[2] = w.z;
         p.w[3] = w.w;
-        if constexpr (KEEP) kb = load_keep<E>(a.mask.keep + row * cols + j0);
+        if constexpr (KEEP) kb = load_keep<E>(a.mask.keep + row * cols + vi * E);
       }
 #pragma unroll
       for (int e = 0; e < E; ++e) {
-        const bool ok = ld && (j0 + e < prefix) && (!KEEP || keep_lane(kb, e));
-        const float f = ok ? p.get(e) : -kInf;
-        bad |= !(f < kInf);
-        mx = fmaxf(mx, f);
-        v[k][e] = f;
+        const bool ok = e < rem && (!KEEP || keep_lane(kb, e));
+        v[k][e] = ok ? p.get(e) : -kInf;
       }
+#pragma unroll
+      for (int e = 0; e < E; ++e) mx = vmax(mx, v[k][e]);
     }
-    // the reductions' barriers also release the LDS row for the next one; a
-    // thread that saw NaN or +inf contributes +inf, so the row is poisoned
-    // exactly when its maximum is +inf
-    mx = block_max<NW>(bad ? kInf : mx, red);
-    const bool poisoned = mx == kInf;
-
-    // cross-entropy: the row's target lane (-1: ignored row) and its logit
-    int64_t t = -1;
+    // cross-entropy: the target's logit, taken from the staged row. Every
+    // read of the staged row comes before the barriers of block_max, which
+    // release the LDS for the next row (policy rows take no later barrier).
     float xt = -kInf;
     if constexpr (EPI == kEpiXent) {
-      t = row_target(a.target, row, cols);
+      if (t >= 0 && t < prefix && (!KEEP || a.mask.keep[row * cols + t] != 0)) {
+        if constexpr (S == 4) {
+          xt = dec<DT>(*reinterpret_cast<const uint32_t*>(row_lds + t * S));
+        } else {
+          xt = dec<DT>(*reinterpret_cast<const uint16_t*>(row_lds + t * S));
+        }
+      }
+    }
+    // the maximum propagates NaN, so one reduction gives the row's maximum
+    // and its policy: NaN or +inf in a valid lane poisons the row
+    mx = block_max<NW>(mx, red);
+    const bool poisoned = !(mx < kInf);
+
+    if constexpr (EPI == kEpiXent) {
       if (t < 0) {  // ignored row: loss 0, gradient 0
         if (tid == 0) a.loss[row] = 0.0f;
         if (a.y != nullptr) {
@@ -99,11 +112,6 @@ __global__ __launch_bounds__(NT) void k_lds(RowArgs a) {
           }
         }
         continue;
-      }
-      if (t < prefix && (!KEEP || a.mask.keep[row * cols + t] != 0)) {
-        Pack<DT, 1> q;
-        q.load(a.x + (row * cols + t) * S);
-        xt = q.get(0);
       }
     }
 
@@ -122,7 +130,7 @@ __global__ __launch_bounds__(NT) void k_lds(RowArgs a) {
           if (j0 < cols) {
             uint32_t h[E];
 #pragma unroll
-            for (int e = 0; e < E; ++e) h[e] = (!poisoned && j0 + e == t) ? enc<DT>(-1.0f) : fill;
+            for (int e = 0; e < E; ++e) h[e] = (!poisoned && k * E + e == slot) ? enc<DT>(-1.0f) : fill;
             Pack<DT, E> p;
             p.put(h);
             p.template store<true>(yr + j0 * S);
@@ -132,33 +140,61 @@ __global__ __launch_bounds__(NT) void k_lds(RowArgs a) {
       continue;
     }
 
+    // exp(x - m) * 2^64 and the sums. The cross-entropy sums the lanes other
+    // than the target and adds the target's exponential (recomputed bit for
+    // bit by every thread) after the one reduction.
     float total, others = 0.0f;
     if constexpr (ACC) {
-      KahanSum ks, ko;
+      KahanSum ks;
 #pragma unroll
       for (int k = 0; k < VPT; ++k)
 #pragma unroll
         for (int e = 0; e < E; ++e) {
           const float te = exp_acc_b64(v[k][e], mx);
           if constexpr (EPI != kEpiLogSoftmax) v[k][e] = te;
-          ks.add(te);
-          if constexpr (EPI == kEpiXent) ko.add(((int64_t)k * NT + tid) * E + e == t ? 0.0f : te);
+          if constexpr (EPI == kEpiXent) {
+            ks.add(k * E + e == slot ? 0.0f : te);
+          } else {
+            ks.add(te);
+          }
         }
-      total = block_sum_pair<NW>(ks.hi(), ks.lo(), red);
-      if constexpr (EPI == kEpiXent) others = block_sum_pair<NW>(ko.hi(), ko.lo(), red);
+      float hi = ks.hi(), lo = ks.lo();
+      block_pair_reduce<NW>(hi, lo, red);
+      if constexpr (EPI == kEpiXent) {
+        others = hi + lo;
+        pair_add(hi, lo, exp_acc_b64(xt, mx), 0.0f);
+      }
+      total = hi + lo;
     } else {
-      float s = 0.0f, so = 0.0f;
+      float s = 0.0f;
+      if (EPI == kEpiSoftmax && __builtin_fabsf(mx) < kBiasMaxAbs) {
+        const float c = row_exp_bias(mx);
 #pragma unroll
-      for (int k = 0; k < VPT; ++k)
+        for (int k = 0; k < VPT; ++k)
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-          const float te = exp_hw_b64(v[k][e], mx);
-          if constexpr (EPI != kEpiLogSoftmax) v[k][e] = te;
-          s += te;
-          if constexpr (EPI == kEpiXent) so += ((int64_t)k * NT + tid) * E + e == t ? 0.0f : te;
-        }
+          for (int e = 0; e < E; ++e) {
+            v[k][e] = exp_hw_bias(v[k][e], c);
+            s += v[k][e];
+          }
+      } else {
+#pragma unroll
+        for (int k = 0; k < VPT; ++k)
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            const float te = exp_hw_b64(v[k][e], mx);
+            if constexpr (EPI != kEpiLogSoftmax) v[k][e] = te;
+            if constexpr (EPI == kEpiXent) {
+              s += k * E + e == slot ? 0.0f : te;
+            } else {
+              s += te;
+            }
+          }
+      }
       total = block_sum<NW>(s, red);
-      if constexpr (EPI == kEpiXent) others = block_sum<NW>(so, red);
+      if constexpr (EPI == kEpiXent) {
+        others = total;
+        total = others + exp_hw_b64(xt, mx);
+      }
     }
 
     float inv = 0.0f;  // softmax / cross-entropy: the reciprocal 2^-64 / l
@@ -170,12 +206,6 @@ __global__ __launch_bounds__(NT) void k_lds(RowArgs a) {
       if (a.y == nullptr) continue;
     } else {
       inv = 1.0f / total;
-      if constexpr (EPI == kEpiXent) {
-        if (tid == 0) {
-          a.loss[row] = xent_loss(mx, xt, others * 5.42101086242752217e-20f, total * 5.42101086242752217e-20f);
-        }
-        if (a.y == nullptr) continue;
-      }
     }
     // cross-entropy target lane: -(others / l), correctly rounded (exactly -1
     // when the target lane is masked)
@@ -183,21 +213,25 @@ __global__ __launch_bounds__(NT) void k_lds(RowArgs a) {
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
       const int64_t j0 = ((int64_t)k * NT + tid) * E;
-      if (j0 < cols) {
-        uint32_t h[E];
+      if (a.y != nullptr && j0 < cols) {
+        float o[E];
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-          float val;
           if constexpr (EPI == kEpiLogSoftmax) {
-            val = minus_lse(v[k][e], lse);
+            o[e] = minus_lse(v[k][e], lse);
           } else {
-            val = (EPI == kEpiXent && j0 + e == t) ? at_t : v[k][e] * inv;
+            o[e] = (EPI == kEpiXent && k * E + e == slot) ? at_t : v[k][e] * inv;
           }
-          h[e] = enc<DT>(val);
         }
         Pack<DT, E> p;
-        p.put(h);
+        p.put_values(o);
         p.template store<true>(yr + j0 * S);
+      }
+    }
+    // the loss last, once the row's values are no longer live
+    if constexpr (EPI == kEpiXent) {
+      if (tid == 0) {
+        a.loss[row] = xent_loss(mx, xt, others * 5.42101086242752217e-20f, total * 5.42101086242752217e-20f);
       }
     }
   }

@@ -52,9 +52,11 @@ __global__ __launch_bounds__(kThreads) void k_stats(RowArgs a, int64_t chunk, in
     const int64_t lim = j_hi < prefix ? j_hi : prefix;
     const char* xr = a.x + row * a.cols * S;
     const uint8_t* kr = KEEP ? a.mask.keep + row * a.cols : nullptr;
-    // cross-entropy: the target lane stays out of the summary (its NaN/+inf
-    // still poisons the chunk) and the chunk holding it records its logit
+    // cross-entropy: the target lane stays out of the summary and the chunk
+    // holding it records its logit; a NaN or +inf there still poisons the
+    // chunk
     const int64_t t = XENT ? row_target(a.target, row, a.cols) : -1;
+    bool tbad = false;
     if (XENT && t >= j_lo && t < j_hi && tid == 0) {
       float xt = -kInf;
       if (t < prefix && (!KEEP || kr[t] != 0)) {
@@ -63,9 +65,10 @@ __global__ __launch_bounds__(kThreads) void k_stats(RowArgs a, int64_t chunk, in
         xt = q.get(0);
       }
       a.xt[row] = xt;
+      tbad = !(xt < kInf);
     }
 
-    // issue one round's loads into registers
+    // one round's loads into registers
     auto fetch = [&](int64_t base, Pack<DT, E>(&p)[VPT], uint64_t(&kb)[VPT]) {
 #pragma unroll
       for (int k = 0; k < VPT; ++k) {
@@ -79,34 +82,27 @@ __global__ __launch_bounds__(kThreads) void k_stats(RowArgs a, int64_t chunk, in
       }
     };
 
+    // fold one round into the thread's running (m, l): the tiled recurrence.
+    // The maximum propagates NaN, so a thread's m ends NaN or +inf exactly
+    // when one of its valid lanes holds NaN or +inf.
     float m_t = -kInf, l_t = 0.0f;
-    bool bad = false;
-    Pack<DT, E> cur[VPT];
-    uint64_t kcur[VPT];
-    if (j_lo < lim) fetch(j_lo, cur, kcur);
-    for (int64_t base = j_lo; base < lim; base += kRound) {
-      // the next round's loads are in flight while this one is reduced
-      Pack<DT, E> nxt[VPT];
-      uint64_t knxt[VPT];
-      const bool more = base + kRound < lim;
-      if (more) fetch(base + kRound, nxt, knxt);
-
+    auto fold = [&](int64_t base, const Pack<DT, E>(&p)[VPT], const uint64_t(&kb)[VPT]) {
+      const int slot = XENT ? target_slot<kThreads, E>(t >= base && t - base < kRound ? t - base : -1, tid) : -1;
       float v[VPT * E];
       float mr = -kInf;
 #pragma unroll
       for (int k = 0; k < VPT; ++k) {
-        const int64_t j0 = base + (int64_t)(k * kThreads + tid) * E;
+        const int64_t left = lim - (base + (int64_t)(k * kThreads + tid) * E);
+        const int rem = left <= 0 ? 0 : (left >= E ? E : (int)left);
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-          const bool ok = (j0 + e < lim) && (!KEEP || keep_lane(kcur[k], e));
-          float f = ok ? cur[k].get(e) : -kInf;
-          bad |= !(f < kInf);
-          if constexpr (XENT) f = j0 + e == t ? -kInf : f;
-          mr = fmaxf(mr, f);
-          v[k * E + e] = f;
+          const bool ok = e < rem && (!KEEP || keep_lane(kb[k], e)) && (!XENT || k * E + e != slot);
+          v[k * E + e] = ok ? p[k].get(e) : -kInf;
         }
+#pragma unroll
+        for (int e = 0; e < E; ++e) mr = vmax(mr, v[k * E + e]);
       }
-      const float m_new = fmaxf(m_t, mr);
+      const float m_new = vmax(m_t, mr);
       if (m_new != -kInf) {
         // correct the running sum, then add this round against m_new; the
         // round's terms are summed as a tree in registers
@@ -121,17 +117,24 @@ __global__ __launch_bounds__(kThreads) void k_stats(RowArgs a, int64_t chunk, in
         l_t = l_t * exp_diff(m_t, m_new) + tree_sum<VPT * E>(v);
         m_t = m_new;
       }
-      if (more) {
-#pragma unroll
-        for (int k = 0; k < VPT; ++k) {
-          cur[k] = nxt[k];
-          kcur[k] = knxt[k];
-        }
-      }
+    };
+
+    // two register rounds, alternating: while one is folded the other's
+    // loads are in flight, and nothing is copied between them
+    Pack<DT, E> ra[VPT], rb[VPT];
+    uint64_t ka[VPT], kb[VPT];
+    if (j_lo < lim) fetch(j_lo, ra, ka);
+    for (int64_t base = j_lo; base < lim; base += 2 * kRound) {
+      const bool more_b = base + kRound < lim;
+      if (more_b) fetch(base + kRound, rb, kb);
+      fold(base, ra, ka);
+      if (!more_b) break;
+      if (base + 2 * kRound < lim) fetch(base + 2 * kRound, ra, ka);
+      fold(base + kRound, rb, kb);
     }
     // thread summaries -> chunk summary; NaN/inf poisons the chunk
     float m = m_t, l = l_t;
-    const bool poisoned = block_merge_flagged<kWaves>(m, l, bad, red);
+    const bool poisoned = block_merge_flagged<kWaves>(m, l, tbad || !(m_t < kInf), red);
     if (tid == 0) {
       smx_stat s;
       if (poisoned) {
@@ -172,18 +175,12 @@ __global__ __launch_bounds__(kThreads) void k_merge_normalize(RowArgs a, int64_t
     const char* xr = a.x + row * a.cols * S;
     char* yr = a.y + row * a.cols * S;
 
-    // cross-entropy: an ignored row has loss 0 and gradient 0
+    // cross-entropy: the row's target lane (-1: ignored row) and the target's
+    // logit as the stats pass left it, loaded together with the summaries
+    // (the ignored-row branch waits for the merge, so no load waits on
+    // another)
     const int64_t t = EPI == kEpiXent ? row_target(a.target, row, a.cols) : -1;
-    if (EPI == kEpiXent && t < 0) {
-      if (c == 0 && tid == 0) a.loss[row] = 0.0f;
-      if (a.y != nullptr) {
-        Pack<DT, E> z;
-        z.fill(0u);
-        for (int64_t j0 = j_lo + (int64_t)tid * E; j0 < j_hi; j0 += (int64_t)kThreads * E)
-          z.template store<true>(yr + j0 * S);
-      }
-      continue;
-    }
+    const float xt_in = EPI == kEpiXent ? a.xt[row] : -kInf;
 
     // merge this row's summaries
     float m = -kInf, l = 0.0f;
@@ -197,11 +194,23 @@ __global__ __launch_bounds__(kThreads) void k_merge_normalize(RowArgs a, int64_t
       }
     }
     const bool poisoned = block_merge_flagged<kWaves>(m, l, bad, red);
+
+    // cross-entropy: an ignored row has loss 0 and gradient 0
+    if (EPI == kEpiXent && t < 0) {
+      if (c == 0 && tid == 0) a.loss[row] = 0.0f;
+      if (a.y != nullptr) {
+        Pack<DT, E> z;
+        z.fill(0u);
+        for (int64_t j0 = j_lo + (int64_t)tid * E; j0 < j_hi; j0 += (int64_t)kThreads * E)
+          z.template store<true>(yr + j0 * S);
+      }
+      continue;
+    }
     // cross-entropy: the summaries leave out the target lane; fold it back in
     float others = 0.0f, xt = -kInf;
     if constexpr (EPI == kEpiXent) {
       if (!poisoned) {
-        xt = a.xt[row];
+        xt = xt_in;
         const float mm = fmaxf(m, xt);
         others = l * exp_diff(m, mm);
         l = others + exp_diff(xt, mm);
@@ -235,6 +244,9 @@ __global__ __launch_bounds__(kThreads) void k_merge_normalize(RowArgs a, int64_t
     const float at_t = (0.0f - others) / l;  // cross-entropy target lane: -(others / L)
 
     for (int64_t base = j_lo; base < j_hi; base += kRound) {
+      // cross-entropy: the target's place in this round's registers (-1: not here)
+      const int slot = EPI == kEpiXent ? target_slot<kThreads, E>(t >= base && t - base < kRound ? t - base : -1, tid)
+                                       : -1;
       Pack<DT, E> in[VPT];
       uint64_t kb[VPT];
 #pragma unroll
@@ -251,21 +263,22 @@ __global__ __launch_bounds__(kThreads) void k_merge_normalize(RowArgs a, int64_t
       for (int k = 0; k < VPT; ++k) {
         const int64_t j0 = base + (int64_t)(k * kThreads + tid) * E;
         if (j0 < j_hi) {
-          uint32_t h[E];
+          // the pack's valid lanes: E inside the prefix, 0 past it
+          const int64_t left = lim - j0;
+          const int rem = left <= 0 ? 0 : (left >= E ? E : (int)left);
+          float o[E];
 #pragma unroll
           for (int e = 0; e < E; ++e) {
-            const bool ok = (j0 + e < lim) && (!KEEP || keep_lane(kb[k], e));
+            const bool ok = e < rem && (!KEEP || keep_lane(kb[k], e));
             const float f = ok ? in[k].get(e) : -kInf;
-            float val;
             if constexpr (EPI == kEpiLogSoftmax) {
-              val = minus_lse(f, lse);
+              o[e] = minus_lse(f, lse);
             } else {
-              val = (EPI == kEpiXent && j0 + e == t) ? at_t : exp_b64<ACC>(f, m) * inv;
+              o[e] = (EPI == kEpiXent && k * E + e == slot) ? at_t : exp_b64<ACC>(f, m) * inv;
             }
-            h[e] = enc<DT>(val);
           }
           Pack<DT, E> out;
-          out.put(h);
+          out.put_values(o);
           out.template store<true>(yr + j0 * S);
         }
       }

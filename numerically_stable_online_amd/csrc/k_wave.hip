@@ -26,40 +26,50 @@ __global__ __launch_bounds__(kThreads) void k_wave(RowArgs a) {
   if (row0 >= a.rows) return;  // wave-uniform
   const int64_t cols = a.cols;
 
-  // load, mask, lane-wise max and the policy flag, for every row of the wave
+  // load, mask and lane-wise max for every row of the wave
   float v[RPW][VPT][E];
   float mx[RPW];
-  bool bad[RPW];
   int64_t prefix[RPW];
+  // cross-entropy: each row's target lane (-1: ignored row), read before the
+  // row so its latency overlaps the row's loads, and the target's logit as
+  // this lane holds it (-inf in every other lane)
+  int64_t tgt[RPW];
+  int slot[RPW];
+  float xo[RPW];
 #pragma unroll
   for (int r = 0; r < RPW; ++r) {
     const int64_t row = row0 + r;
     prefix[r] = row < a.rows ? valid_prefix(a.mask, row, cols) : 0;
     mx[r] = -kInf;
-    bad[r] = false;
+    tgt[r] = (EPI == kEpiXent && row < a.rows) ? row_target(a.target, row, cols) : -1;
+    slot[r] = target_slot<64, E>(tgt[r], lane);
+    xo[r] = -kInf;
   }
 #pragma unroll
   for (int r = 0; r < RPW; ++r) {
     const char* xr = a.x + (row0 + r) * cols * S;
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
+      // the pack's valid lanes: E inside the prefix, 0 past it, so each
+      // lane's test is a 32-bit compare with a constant
       const int64_t j0 = (int64_t)(k * 64 + lane) * E;
+      const int64_t left = prefix[r] - j0;
+      const int rem = left <= 0 ? 0 : (left >= E ? E : (int)left);
       Pack<DT, E> p;
       p.fill(0);
       uint64_t kb = ~0ull;
-      const bool ld = j0 < prefix[r];
-      if (ld) {
+      if (rem > 0) {
         p.template load<true>(xr + j0 * S);
         if constexpr (KEEP) kb = load_keep<E>(a.mask.keep + (row0 + r) * cols + j0);
       }
 #pragma unroll
       for (int e = 0; e < E; ++e) {
-        const bool ok = ld && (j0 + e < prefix[r]) && (!KEEP || keep_lane(kb, e));
-        const float f = ok ? p.get(e) : -kInf;
-        bad[r] |= !(f < kInf);  // NaN or +inf in a valid lane
-        mx[r] = fmaxf(mx[r], f);
-        v[r][k][e] = f;
+        const bool ok = e < rem && (!KEEP || keep_lane(kb, e));
+        v[r][k][e] = ok ? p.get(e) : -kInf;
+        if constexpr (EPI == kEpiXent) xo[r] = k * E + e == slot[r] ? v[r][k][e] : xo[r];
       }
+#pragma unroll
+      for (int e = 0; e < E; ++e) mx[r] = vmax(mx[r], v[r][k][e]);
     }
   }
 
@@ -68,16 +78,16 @@ __global__ __launch_bounds__(kThreads) void k_wave(RowArgs a) {
     const int64_t row = row0 + r;
     if (row >= a.rows) break;  // wave-uniform
     char* yr = a.y + row * cols * S;
-    // a lane that saw NaN or +inf contributes +inf: the row is poisoned
-    // exactly when its maximum is +inf, so one reduction carries both
-    const float m = wave_max(bad[r] ? kInf : mx[r]);
-    const bool poisoned = m == kInf;
+    // the maximum propagates NaN, so one reduction gives the row's maximum
+    // and its policy: NaN or +inf in a valid lane poisons the row
+    const float m = wave_max(mx[r]);
+    const bool poisoned = !(m < kInf);
 
     // cross-entropy: the row's target lane (-1: ignored row) and its logit
     int64_t t = -1;
     float xt = -kInf;
     if constexpr (EPI == kEpiXent) {
-      t = row_target(a.target, row, cols);
+      t = tgt[r];
       if (t < 0) {  // ignored row: loss 0, gradient 0
         if (lane == 0) a.loss[row] = 0.0f;
         if (a.y != nullptr) {
@@ -91,11 +101,8 @@ __global__ __launch_bounds__(kThreads) void k_wave(RowArgs a) {
         }
         continue;
       }
-      if (t < prefix[r] && (!KEEP || a.mask.keep[row * cols + t] != 0)) {
-        Pack<DT, 1> q;
-        q.load(a.x + (row * cols + t) * S);
-        xt = q.get(0);
-      }
+      // the lane holding element t: pack t / E of the row, lane (t / E) mod 64
+      xt = lane_read(xo[r], (int)((t / E) & 63));
     }
 
     if (poisoned || m == -kInf) {
@@ -116,7 +123,7 @@ __global__ __launch_bounds__(kThreads) void k_wave(RowArgs a) {
           if (j0 < cols) {
             uint32_t h[E];
 #pragma unroll
-            for (int e = 0; e < E; ++e) h[e] = (!poisoned && j0 + e == t) ? enc<DT>(-1.0f) : fill;
+            for (int e = 0; e < E; ++e) h[e] = (!poisoned && k * E + e == slot[r]) ? enc<DT>(-1.0f) : fill;
             Pack<DT, E> p;
             p.put(h);
             p.template store<true>(yr + j0 * S);
@@ -127,41 +134,62 @@ __global__ __launch_bounds__(kThreads) void k_wave(RowArgs a) {
     }
 
     // exp(x - m) * 2^64 and its sum; masked lanes give exactly 0. The
-    // softmax and the cross-entropy keep the exponentials for their stores;
-    // the cross-entropy also sums the lanes other than the target.
+    // softmax and the cross-entropy keep the exponentials for their stores.
+    // The cross-entropy sums the lanes other than the target ("others") and
+    // adds the target's exponential, which every lane recomputes bit for bit,
+    // afterwards: one reduction gives both sums.
     float total, others = 0.0f;
     if constexpr (ACC) {
-      KahanSum ks, ko;
+      KahanSum ks;
 #pragma unroll
       for (int k = 0; k < VPT; ++k)
 #pragma unroll
         for (int e = 0; e < E; ++e) {
           const float te = exp_acc_b64(v[r][k][e], m);
           if constexpr (EPI != kEpiLogSoftmax) v[r][k][e] = te;
-          ks.add(te);
           if constexpr (EPI == kEpiXent) {
-            const int64_t j = (int64_t)(k * 64 + lane) * E + e;
-            ko.add(j == t ? 0.0f : te);
+            ks.add(k * E + e == slot[r] ? 0.0f : te);
+          } else {
+            ks.add(te);
           }
         }
-      total = wave_sum_pair(ks.hi(), ks.lo());
-      if constexpr (EPI == kEpiXent) others = wave_sum_pair(ko.hi(), ko.lo());
+      float hi = ks.hi(), lo = ks.lo();
+      wave_pair_reduce(hi, lo);
+      if constexpr (EPI == kEpiXent) {
+        others = hi + lo;
+        pair_add(hi, lo, exp_acc_b64(xt, m), 0.0f);
+      }
+      total = hi + lo;
     } else {
-      float s = 0.0f, so = 0.0f;
+      float s = 0.0f;
+      if (EPI == kEpiSoftmax && __builtin_fabsf(m) < kBiasMaxAbs) {
+        const float c = row_exp_bias(m);
 #pragma unroll
-      for (int k = 0; k < VPT; ++k)
+        for (int k = 0; k < VPT; ++k)
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-          const float te = exp_hw_b64(v[r][k][e], m);
-          if constexpr (EPI != kEpiLogSoftmax) v[r][k][e] = te;
-          s += te;
-          if constexpr (EPI == kEpiXent) {
-            const int64_t j = (int64_t)(k * 64 + lane) * E + e;
-            so += j == t ? 0.0f : te;
+          for (int e = 0; e < E; ++e) {
+            v[r][k][e] = exp_hw_bias(v[r][k][e], c);
+            s += v[r][k][e];
           }
-        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < VPT; ++k)
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            const float te = exp_hw_b64(v[r][k][e], m);
+            if constexpr (EPI != kEpiLogSoftmax) v[r][k][e] = te;
+            if constexpr (EPI == kEpiXent) {
+              s += k * E + e == slot[r] ? 0.0f : te;
+            } else {
+              s += te;
+            }
+          }
+      }
       total = wave_sum(s);
-      if constexpr (EPI == kEpiXent) others = wave_sum(so);
+      if constexpr (EPI == kEpiXent) {
+        others = total;
+        total = others + exp_hw_b64(xt, m);
+      }
     }
 
     if constexpr (EPI == kEpiLogSoftmax) {
@@ -174,39 +202,36 @@ __global__ __launch_bounds__(kThreads) void k_wave(RowArgs a) {
         for (int k = 0; k < VPT; ++k) {
           const int64_t j0 = (int64_t)(k * 64 + lane) * E;
           if (j0 < cols) {
-            uint32_t h[E];
+            float o[E];
 #pragma unroll
-            for (int e = 0; e < E; ++e) h[e] = enc<DT>(minus_lse(v[r][k][e], lse));
+            for (int e = 0; e < E; ++e) o[e] = minus_lse(v[r][k][e], lse);
             Pack<DT, E> p;
-            p.put(h);
+            p.put_values(o);
             p.template store<true>(yr + j0 * S);
           }
         }
       }
     } else {
       const float inv = 1.0f / total;  // 2^-64 / l
-      if constexpr (EPI == kEpiXent) {
-        if (lane == 0) {
-          a.loss[row] = xent_loss(m, xt, others * 5.42101086242752217e-20f, total * 5.42101086242752217e-20f);
-        }
-        if (a.y == nullptr) continue;
-      }
       // the target lane of the cross-entropy gradient: p_t - 1 = -(others / l)
       // (a correctly rounded divide: exactly -1 when the target lane is masked)
       const float at_t = (0.0f - others) / total;
 #pragma unroll
       for (int k = 0; k < VPT; ++k) {
         const int64_t j0 = (int64_t)(k * 64 + lane) * E;
-        if (j0 < cols) {
-          uint32_t h[E];
+        if (a.y != nullptr && j0 < cols) {
+          float o[E];
 #pragma unroll
-          for (int e = 0; e < E; ++e) {
-            const float val = (EPI == kEpiXent && j0 + e == t) ? at_t : v[r][k][e] * inv;
-            h[e] = enc<DT>(val);
-          }
+          for (int e = 0; e < E; ++e) o[e] = (EPI == kEpiXent && k * E + e == slot[r]) ? at_t : v[r][k][e] * inv;
           Pack<DT, E> p;
-          p.put(h);
+          p.put_values(o);
           p.template store<true>(yr + j0 * S);
+        }
+      }
+      // the loss last, once the row's values are no longer live
+      if constexpr (EPI == kEpiXent) {
+        if (lane == 0) {
+          a.loss[row] = xent_loss(m, xt, others * 5.42101086242752217e-20f, total * 5.42101086242752217e-20f);
         }
       }
     }

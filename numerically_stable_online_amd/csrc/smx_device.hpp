@@ -39,7 +39,10 @@ __device__ __forceinline__ float dec(uint32_t h) {
 
 // Nearest-even rounding of an fp32 value (finite or -inf; non-negative for
 // probabilities, non-positive for log-probabilities) to the element format,
-// gradual underflow kept; fp16 overflows to -inf as IEEE rounding does.
+// gradual underflow kept; fp16 overflows to -inf as IEEE rounding does. The
+// 16-bit formats use gfx950's conversion instructions (v_cvt_f16_f32,
+// v_cvt_pk_bf16_f32), which round to nearest-even and keep subnormals in the
+// kernels' floating-point mode.
 template <int DT>
 __device__ __forceinline__ uint32_t enc(float f) {
   if constexpr (DT == kF32) {
@@ -47,7 +50,22 @@ __device__ __forceinline__ uint32_t enc(float f) {
   } else if constexpr (DT == kF16) {
     return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
   } else {
-    return bf16_rne(f);
+    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
+  }
+}
+
+// Two values rounded as enc does, packed low half first: one packed
+// conversion (v_cvt_pk_f16_f32 / v_cvt_pk_bf16_f32) for both.
+template <int DT>
+__device__ __forceinline__ uint32_t enc2(float a, float b) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  const f2 v = {a, b};
+  if constexpr (DT == kF16) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, h2));
+  } else {
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, b2));
   }
 }
 
@@ -121,6 +139,16 @@ struct Pack {
     } else {
 #pragma unroll
       for (int i = 0; i < E / 2; ++i) w[i] = h[2 * i] | (h[2 * i + 1] << 16);
+    }
+  }
+  // fill from E values, each rounded to the element format as enc does
+  __device__ __forceinline__ void put_values(const float (&v)[E]) {
+    if constexpr (S == 4 || E == 1) {
+#pragma unroll
+      for (int i = 0; i < E; ++i) w[i] = enc<DT>(v[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < E / 2; ++i) w[i] = enc2<DT>(v[2 * i], v[2 * i + 1]);
     }
   }
   __device__ __forceinline__ void fill(uint32_t h) {
@@ -208,6 +236,20 @@ __device__ __forceinline__ float exp_hw_b64(float x, float m) {
   return __builtin_amdgcn_exp2f(__builtin_fmaf(x - m, kLog2e, 64.0f));
 }
 
+// The 16-bit softmax's exponential with the row's shift folded into one
+// constant: 2^(x log2 e + c), c = 64 - m log2 e, one fused multiply-add and
+// one v_exp_f32 per lane. Each lane's argument is rounded once; the rounding
+// of c scales every lane of the row by the same factor 2^(delta c), which the
+// normalization p = e / sum(e) divides out. That holds while c is small
+// enough for delta c to stay tiny (|m| < 2^15: |delta c| <= 2^-9), so rows
+// with a larger maximum take exp_hw_b64. Not for outputs that keep log(sum):
+// there the common factor would show.
+constexpr float kBiasMaxAbs = 32768.0f;
+__device__ __forceinline__ float row_exp_bias(float m) { return __builtin_fmaf(-m, kLog2e, 64.0f); }
+__device__ __forceinline__ float exp_hw_bias(float x, float c) {
+  return __builtin_amdgcn_exp2f(__builtin_fmaf(x, kLog2e, c));
+}
+
 // Sum of N register values as a balanced binary tree: the same N - 1
 // additions as a running sum, with the error bound growing as log2 N instead
 // of N ("Softmax numerics architecture", fp32 accumulator section).
@@ -248,11 +290,18 @@ __device__ __forceinline__ float minus_lse(float x, const Lse& s) { return (x - 
 
 // The cross-entropy of a row from its maximum m, the target logit xt, the
 // sum of the other lanes' exp(x - m) ("others") and of all lanes ("all"),
-// both unscaled: LSE - xt = (m - xt) + log(all), or, when the target holds
-// the maximum, log1p(others), which keeps a confident prediction's tiny loss
-// exact to fp32 precision instead of cancelling.
+// both unscaled: LSE - xt = (m - xt) + log(all). When the target holds the
+// maximum, all = fl(1 + others) and the loss is log1p(others); it is taken
+// as log(w) * u / (w - 1) with w = all, u = others (Goldberg, "What Every
+// Computer Scientist Should Know About Floating-Point Arithmetic", Theorem 4):
+// w - 1 is exact, so the quotient cancels the rounding of w, and a confident
+// prediction's tiny loss keeps full fp32 relative precision at the cost of
+// one logarithm (the library log1p is a far longer dependency chain).
 __device__ __forceinline__ float xent_loss(float m, float xt, float others, float all) {
-  return xt == m ? log1pf(others) : (m - xt) + log_l(all);
+  const float lg = log_l(all);
+  if (xt != m) return (m - xt) + lg;
+  const float w1 = all - 1.0f;
+  return w1 == 0.0f ? others : lg * (others / w1);
 }
 
 // The target lane of a row, or -1 when the row is ignored (target outside
@@ -260,6 +309,18 @@ __device__ __forceinline__ float xent_loss(float m, float xt, float others, floa
 __device__ __forceinline__ int64_t row_target(const int32_t* target, int64_t row, int64_t cols) {
   const int64_t t = target[row];
   return (t >= 0 && t < cols) ? t : -1;
+}
+
+// Where the target lane t sits among one thread's registers, when element j
+// of the row is slot e of pack k of thread (j / E) mod NT, with
+// j = (k * NT + thread) * E + e: k * E + e for the thread holding t, -1 for
+// every other thread and for t < 0. Compared with compile-time k * E + e, it
+// costs one 32-bit compare per element instead of a 64-bit index.
+template <int NT, int E>
+__device__ __forceinline__ int target_slot(int64_t t, int tid) {
+  if (t < 0) return -1;
+  const int64_t q = t / E;
+  return (int)(q % NT) == tid ? (int)(q / NT) * E + (int)(t % E) : -1;
 }
 
 // The epilogue's per-row scalar for the log-softmax outputs.
@@ -315,12 +376,17 @@ __device__ __forceinline__ float lane_read(float v, int lane) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
 }
 
+// The IEEE maximum that propagates NaN (v_maximum3_f32 on gfx950): a NaN in
+// any operand makes the result NaN, so a row's maximum is NaN exactly when a
+// valid lane holds NaN, and +inf exactly when one holds +inf and none NaN.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 __device__ __forceinline__ float wave_max(float v) {
-  v = fmaxf(v, dpp<kDppXor1>(v));
-  v = fmaxf(v, dpp<kDppXor2>(v));
-  v = fmaxf(v, dpp<kDppHalfMirror>(v));
-  v = fmaxf(v, dpp<kDppMirror>(v));
-  return fmaxf(fmaxf(lane_read(v, 0), lane_read(v, 16)), fmaxf(lane_read(v, 32), lane_read(v, 48)));
+  v = vmax(v, dpp<kDppXor1>(v));
+  v = vmax(v, dpp<kDppXor2>(v));
+  v = vmax(v, dpp<kDppHalfMirror>(v));
+  v = vmax(v, dpp<kDppMirror>(v));
+  return vmax(vmax(lane_read(v, 0), lane_read(v, 16)), vmax(lane_read(v, 32), lane_read(v, 48)));
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -347,7 +413,8 @@ __device__ __forceinline__ void pair_step(float& hi, float& lo) {
   pair_add(hi, lo, h2, l2);
 }
 
-__device__ __forceinline__ float wave_sum_pair(float hi, float lo) {
+// the wave's sum of (hi, lo) pairs, left as a pair in (hi, lo)
+__device__ __forceinline__ void wave_pair_reduce(float& hi, float& lo) {
   pair_step<kDppXor1>(hi, lo);
   pair_step<kDppXor2>(hi, lo);
   pair_step<kDppHalfMirror>(hi, lo);
@@ -359,7 +426,13 @@ __device__ __forceinline__ float wave_sum_pair(float hi, float lo) {
   pair_add(h0, l0, h1, l1);
   pair_add(h2, l2, h3, l3);
   pair_add(h0, l0, h2, l2);
-  return h0 + l0;
+  hi = h0;
+  lo = l0;
+}
+
+__device__ __forceinline__ float wave_sum_pair(float hi, float lo) {
+  wave_pair_reduce(hi, lo);
+  return hi + lo;
 }
 
 template <int CTRL>
@@ -406,7 +479,7 @@ __device__ __forceinline__ float block_max(float v, RedScratch& s) {
   __syncthreads();
   float r = s.a[0];
 #pragma unroll
-  for (int i = 1; i < NW; ++i) r = fmaxf(r, s.a[i]);
+  for (int i = 1; i < NW; ++i) r = vmax(r, s.a[i]);
   __syncthreads();
   return r;
 }
@@ -435,30 +508,28 @@ __device__ __forceinline__ float block_sum(float v, RedScratch& s) {
   return r;
 }
 
+// the workgroup's sum of (hi, lo) pairs, left as a pair in (hi, lo): each
+// wave's result as a pair, then the pairs across waves
 template <int NW>
-__device__ __forceinline__ float block_sum_pair(float hi, float lo, RedScratch& s) {
-  // wave result as an exact-ish pair, then pairs across waves
-  pair_step<kDppXor1>(hi, lo);
-  pair_step<kDppXor2>(hi, lo);
-  pair_step<kDppHalfMirror>(hi, lo);
-  pair_step<kDppMirror>(hi, lo);
-  float h0 = lane_read(hi, 0), l0 = lane_read(lo, 0);
-  float h1 = lane_read(hi, 16), l1 = lane_read(lo, 16);
-  float h2 = lane_read(hi, 32), l2 = lane_read(lo, 32);
-  float h3 = lane_read(hi, 48), l3 = lane_read(lo, 48);
-  pair_add(h0, l0, h1, l1);
-  pair_add(h2, l2, h3, l3);
-  pair_add(h0, l0, h2, l2);
+__device__ __forceinline__ void block_pair_reduce(float& hi, float& lo, RedScratch& s) {
+  wave_pair_reduce(hi, lo);
   if ((threadIdx.x & 63) == 0) {
-    s.a[threadIdx.x >> 6] = h0;
-    s.b[threadIdx.x >> 6] = l0;
+    s.a[threadIdx.x >> 6] = hi;
+    s.b[threadIdx.x >> 6] = lo;
   }
   __syncthreads();
   float rh = s.a[0], rl = s.b[0];
 #pragma unroll
   for (int i = 1; i < NW; ++i) pair_add(rh, rl, s.a[i], s.b[i]);
   __syncthreads();
-  return rh + rl;
+  hi = rh;
+  lo = rl;
+}
+
+template <int NW>
+__device__ __forceinline__ float block_sum_pair(float hi, float lo, RedScratch& s) {
+  block_pair_reduce<NW>(hi, lo, s);
+  return hi + lo;
 }
 
 // The workgroup's summaries merged in two reductions: M = the maximum of the

@@ -6,7 +6,10 @@
   double).
 * f16 / bf16 output: within 1 ulp of the oracle's value rounded once to the
   format (bit patterns compared as integers; outputs are >= 0 so the order is
-  monotone).
+  monotone), and exactly that rounded value wherever the oracle's value is
+  clear of a rounding midpoint by more than the kernel's fp32 error (2^-16
+  relative): the 1-ulp allowance covers near-ties only, so a kernel that
+  truncated, or rounded ties the wrong way far from a tie, fails.
 * policy lanes (masked, -inf, empty row, NaN row): bit-exact +0.0 or the
   canonical quiet NaN.
 """
@@ -41,6 +44,30 @@ def to_host(y: torch.Tensor, dtype: str) -> np.ndarray:
 
 def bits_of(y_raw: np.ndarray, dtype: str) -> np.ndarray:
     return y_raw.view(np.uint32).astype(np.int64) if dtype == "f32" else y_raw.astype(np.int64)
+
+
+CLEAR_REL = 2.0 ** -16
+
+
+def exact_where_clear(bits, ref, dtype, sel, margin, what):
+    """16-bit lanes in sel whose reference rounds to the same pattern at
+    ref - margin and ref + margin must hold exactly that pattern."""
+    if not sel.any():
+        return 0
+    r = ref[sel]
+    m = np.broadcast_to(margin, ref.shape)[sel]
+    want = oracle.encode(r, dtype).astype(np.int64)
+    lo = oracle.encode(r - m, dtype).astype(np.int64)
+    hi = oracle.encode(r + m, dtype).astype(np.int64)
+    clear = (lo == want) & (hi == want)
+    got = bits[sel]
+    bad = clear & (got != want)
+    if bad.any():
+        i = int(np.argmax(bad))
+        idx = tuple(np.argwhere(sel)[i])
+        raise AssertionError(f"{what}: lane {idx} is clear of a rounding midpoint but got {got[i]:#06x}, "
+                             f"the correctly rounded value is {want[i]:#06x} (ref {r[i]!r})")
+    return int(clear.sum())
 
 
 def check(y_raw: np.ndarray, dtype: str, p: np.ndarray, cls: np.ndarray, st: np.ndarray, what: str = ""):
@@ -80,6 +107,7 @@ def check(y_raw: np.ndarray, dtype: str, p: np.ndarray, cls: np.ndarray, st: np.
             raise AssertionError(f"{what}: {worst} ulp at {i}: got {bits[i]:#06x} want {want[i]:#06x} (ref {p[i]!r})")
         out["max_ulp"] = worst
         out["frac_off_by_one"] = float(np.count_nonzero(d[num])) / max(1, int(num.sum()))
+        out["exact_lanes"] = exact_where_clear(bits, p, dtype, num, CLEAR_REL * np.abs(p), what)
     return out
 
 
@@ -146,6 +174,7 @@ def check_log(y_raw, dtype, logp, lse_ref, lse_got, cls, st, x_float, what=""):
         out["max_ulp"] = int(d[num].max()) if num.any() else 0
         big = num & (np.abs(logp) >= 2.0 ** -8)
         out["max_ulp_away_from_0"] = int(d[big].max()) if big.any() else 0
+        out["exact_lanes"] = exact_where_clear(bits, logp, dtype, num, 2.0 ** -20 * scale, what)
     return out
 
 
@@ -192,8 +221,15 @@ def check_bwd(dx_raw, dtype, ref, p_f64, g_f64, what=""):
         i = tuple(np.argwhere(bad)[0])
         raise AssertionError(f"{what}: {d[i]} ulp and error {err[i]:.3e} at {i} (ref {r[i]!r})")
     far = np.abs(r) >= 2.0 ** -8 * scale
+    full = np.zeros(bits.shape, dtype=bool)
+    full[ok] = True
+    ref_full = np.zeros(bits.shape)
+    ref_full[ok] = r
+    scale_full = np.zeros(bits.shape)
+    scale_full[ok] = scale
     return {"max_ulp": int(d.max()) if d.size else 0,
-            "max_ulp_without_cancellation": int(d[far].max()) if far.any() else 0}
+            "max_ulp_without_cancellation": int(d[far].max()) if far.any() else 0,
+            "exact_lanes": exact_where_clear(bits, ref_full, dtype, full, CLEAR_REL * scale_full, what)}
 
 
 # ---------------------------------------------------------------------------
@@ -273,4 +309,5 @@ def check_xent(loss_got, dx_raw, dtype, loss_ref, dx_ref, x_float, target, what=
             i = np.unravel_index(np.argmax(d), d.shape)
             raise AssertionError(f"{what}: dx {worst} ulp at {i}: got {bits[i]:#06x} want {want[i]:#06x} (ref {dx_ref[i]!r})")
         out["dx_max_ulp"] = worst
+        out["dx_exact_lanes"] = exact_where_clear(bits, dx_ref, dtype, numl, CLEAR_REL * np.abs(dx_ref), what)
     return out

@@ -243,3 +243,10 @@ def random_rows(rows: int, cols: int, dtype: str, seed: int, scale: float = 4.0,
     else:
         raise ValueError(dist)
     return to_format(a, dtype)
+
+
+def class_targets(rows: int, cols: int, seed: int) -> np.ndarray:
+    """Seeded class indices in [0, cols), one per row (int32), for the
+    cross-entropy entry point."""
+    rng = _rng(seed, rows, cols, 7)
+    return rng.integers(0, cols, rows).astype(np.int32)
