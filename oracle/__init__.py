@@ -69,6 +69,12 @@ def lib():
         L.oracle_log_softmax_rows.argtypes = [vp, i32, i64, i64, mp, i64, i64, vp, vp]
         L.oracle_softmax_backward_rows.argtypes = [vp, vp, i32, i64, i64, i64, i64, vp]
         L.oracle_cross_entropy_rows.argtypes = [vp, i32, i64, i64, mp, vp, i64, i64, vp, vp]
+        L.oracle_softmax_weighted_rows.argtypes = [vp, vp, i32, i64, i64, i64, i64, mp, i64, i64, vp, vp]
+        L.oracle_weighted_chunk_states.argtypes = [vp, vp, i32, i64, i64, i64, i64, mp, i64, i64, i64,
+                                                   vp, vp, vp]
+        L.oracle_weighted_merge.argtypes = [C.c_double, C.c_double, vp, C.c_double, C.c_double, vp, i64,
+                                            dp, dp, vp]
+        L.oracle_weighted_merge.restype = None
         L.oracle_round_f32_bits.argtypes = [C.c_double]
         L.oracle_round_f32_bits.restype = C.c_uint32
         L.oracle_round_f16_bits.argtypes = [C.c_double]
@@ -252,6 +258,56 @@ def cross_entropy_rows(x: np.ndarray, dtype: str, target: np.ndarray, mask=None,
     if rc != 0:
         raise ValueError("oracle_cross_entropy_rows: bad arguments")
     return loss, dx
+
+
+def softmax_weighted_rows(s: np.ndarray, v: np.ndarray, dtype: str, rows_per_group: int, mask=None,
+                          r0: int = 0, r1: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """out[r] = softmax(s[r]) @ v[r // rows_per_group] in double; returns (out [r1-r0, d], row status)."""
+    s = _raw(s, dtype)
+    v = _raw(v, dtype)
+    rows, cols = s.shape
+    d = v.shape[-1]
+    if v.shape != (rows // rows_per_group, cols, d):
+        raise ValueError(f"v must be [rows / rows_per_group, cols, d], got {v.shape}")
+    r1 = rows if r1 is None else r1
+    out = np.empty((r1 - r0, d), dtype=np.float64)
+    st = np.empty(r1 - r0, dtype=np.int32)
+    ms, keep = _mask_struct(mask, rows, cols)
+    rc = lib().oracle_softmax_weighted_rows(_ptr(s), _ptr(v), DTYPE_CODE[dtype], rows, cols, d, rows_per_group,
+                                            C.byref(ms), r0, r1, _ptr(out), _ptr(st))
+    if rc != 0:
+        raise ValueError("oracle_softmax_weighted_rows: bad arguments")
+    return out, st
+
+
+def weighted_chunk_states(s: np.ndarray, v: np.ndarray, dtype: str, rows_per_group: int, chunk_cols: int,
+                          mask=None, r0: int = 0, r1: Optional[int] = None):
+    """Per-chunk (m, l, o) states: m, l [r1-r0, n_chunks], o [r1-r0, n_chunks, d]."""
+    s = _raw(s, dtype)
+    v = _raw(v, dtype)
+    rows, cols = s.shape
+    d = v.shape[-1]
+    r1 = rows if r1 is None else r1
+    nch = (cols + chunk_cols - 1) // chunk_cols
+    m = np.empty((r1 - r0, nch), dtype=np.float64)
+    l = np.empty((r1 - r0, nch), dtype=np.float64)
+    o = np.empty((r1 - r0, nch, d), dtype=np.float64)
+    ms, keep = _mask_struct(mask, rows, cols)
+    rc = lib().oracle_weighted_chunk_states(_ptr(s), _ptr(v), DTYPE_CODE[dtype], rows, cols, d, rows_per_group,
+                                            C.byref(ms), chunk_cols, r0, r1, _ptr(m), _ptr(l), _ptr(o))
+    if rc != 0:
+        raise ValueError("oracle_weighted_chunk_states: bad arguments")
+    return m, l, o
+
+
+def weighted_merge(m_a: float, l_a: float, o_a: np.ndarray, m_b: float, l_b: float, o_b: np.ndarray):
+    o_a = np.ascontiguousarray(o_a, dtype=np.float64)
+    o_b = np.ascontiguousarray(o_b, dtype=np.float64)
+    out = np.empty_like(o_a)
+    mo, lo = C.c_double(), C.c_double()
+    lib().oracle_weighted_merge(m_a, l_a, _ptr(o_a), m_b, l_b, _ptr(o_b), o_a.size, C.byref(mo), C.byref(lo),
+                                _ptr(out))
+    return mo.value, lo.value, out
 
 
 def round_f16_bits(v: float) -> int:

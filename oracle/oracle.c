@@ -264,6 +264,90 @@ int oracle_chunk_stats(const void* x, int dtype, int64_t rows, int64_t cols,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Softmax-weighted value sums ("Online stable softmax", section on the      */
+/* weighted-value numerator: attention also needs the sum of                 */
+/* exp(score_j - m) V_j; "Softmax numerics architecture", tiled attention:   */
+/* the output is O / d at the end). The plain definition: the three-pass     */
+/* probabilities of the row, then each output component as a compensated    */
+/* sum of p_j V_jk in ascending j.                                           */
+/* ------------------------------------------------------------------------ */
+
+int oracle_softmax_weighted_rows(const void* s, const void* v, int dtype,
+                                 int64_t rows, int64_t cols, int64_t d,
+                                 int64_t rows_per_group, const oracle_mask* mk,
+                                 int64_t r0, int64_t r1, double* out,
+                                 int32_t* row_status) {
+  if (dtype < 0 || dtype > 2 || rows < 0 || cols < 0 || d < 0 ||
+      rows_per_group <= 0 || rows % rows_per_group != 0 || r0 < 0 ||
+      r1 > rows || r0 > r1 || !mask_ok(mk))
+    return -1;
+  double* p = (double*)malloc(sizeof(double) * (size_t)(cols > 0 ? cols : 1));
+  uint8_t* cls = (uint8_t*)malloc((size_t)(cols > 0 ? cols : 1));
+  if (!p || !cls) {
+    free(p);
+    free(cls);
+    return -1;
+  }
+  for (int64_t r = r0; r < r1; ++r) {
+    double* o = out + (r - r0) * d;
+    const int32_t st = softmax_one_row(s, dtype, cols, mk, r, p, cls);
+    if (row_status) row_status[r - r0] = st;
+    if (st != ORACLE_ROW_OK) {
+      for (int64_t k = 0; k < d; ++k) o[k] = st == ORACLE_ROW_POISON ? NAN : 0.0;
+      continue;
+    }
+    const int64_t vbase = (r / rows_per_group) * cols * d;
+    for (int64_t k = 0; k < d; ++k) {
+      nsum acc = {0.0, 0.0};
+      for (int64_t j = 0; j < cols; ++j) {
+        if (cls[j] != ORACLE_LANE_NUMERIC) continue;
+        nsum_add(&acc, p[j] * oracle_decode(v, dtype, vbase + j * d + k));
+      }
+      o[k] = nsum_value(&acc);
+    }
+  }
+  free(p);
+  free(cls);
+  return 0;
+}
+
+int oracle_weighted_chunk_states(const void* s, const void* v, int dtype,
+                                 int64_t rows, int64_t cols, int64_t d,
+                                 int64_t rows_per_group, const oracle_mask* mk,
+                                 int64_t chunk_cols, int64_t r0, int64_t r1,
+                                 double* m, double* l, double* o) {
+  if (d < 0 || rows_per_group <= 0 || rows % rows_per_group != 0) return -1;
+  if (oracle_chunk_stats(s, dtype, rows, cols, mk, chunk_cols, r0, r1, m, l))
+    return -1;
+  const int64_t n_chunks = (cols + chunk_cols - 1) / chunk_cols;
+  for (int64_t r = r0; r < r1; ++r) {
+    const int64_t prefix = oracle_valid_prefix(mk, r, cols);
+    const int64_t vbase = (r / rows_per_group) * cols * d;
+    for (int64_t c = 0; c < n_chunks; ++c) {
+      const int64_t idx = (r - r0) * n_chunks + c;
+      double* oc = o + idx * d;
+      if (isnan(m[idx]) || m[idx] == -INFINITY) {
+        for (int64_t k = 0; k < d; ++k) oc[k] = isnan(m[idx]) ? NAN : 0.0;
+        continue;
+      }
+      const int64_t lo = c * chunk_cols;
+      const int64_t hi = lo + chunk_cols < cols ? lo + chunk_cols : cols;
+      for (int64_t k = 0; k < d; ++k) {
+        nsum acc = {0.0, 0.0};
+        for (int64_t j = lo; j < hi; ++j) {
+          if (!lane_valid(mk, r, j, cols, prefix)) continue;
+          const double x = oracle_decode(s, dtype, r * cols + j);
+          if (x == -INFINITY) continue;
+          nsum_add(&acc, exp(x - m[idx]) * oracle_decode(v, dtype, vbase + j * d + k));
+        }
+        oc[k] = nsum_value(&acc);
+      }
+    }
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* The merge ("Online stable softmax", section "Derive the update for two    */
 /* blocks" and "Reference summary"): m' = max(m, m2),                        */
 /* l' = exp(m - m') l + exp(m2 - m') l2. The side holding the maximum has    */
@@ -289,6 +373,32 @@ void oracle_merge(double m_a, double l_a, double m_b, double l_b,
   const double fb = (m_b == mm) ? 1.0 : exp(m_b - mm);
   *m_out = mm;
   *l_out = fa * l_a + fb * l_b;
+}
+
+/* The weighted numerator takes the same two factors as the sum ("Online
+ * stable softmax", reference summary: o' = exp(m - m') o + exp(m2 - m') o2). */
+void oracle_weighted_merge(double m_a, double l_a, const double* o_a,
+                           double m_b, double l_b, const double* o_b,
+                           int64_t d, double* m_out, double* l_out,
+                           double* o_out) {
+  if (isnan(m_a) || isnan(m_b) || isnan(l_a) || isnan(l_b)) {
+    *m_out = NAN;
+    *l_out = NAN;
+    for (int64_t k = 0; k < d; ++k) o_out[k] = NAN;
+    return;
+  }
+  const double mm = m_a > m_b ? m_a : m_b;
+  if (mm == -INFINITY) {
+    *m_out = -INFINITY;
+    *l_out = 0.0;
+    for (int64_t k = 0; k < d; ++k) o_out[k] = 0.0;
+    return;
+  }
+  const double fa = (m_a == mm) ? 1.0 : exp(m_a - mm);
+  const double fb = (m_b == mm) ? 1.0 : exp(m_b - mm);
+  *m_out = mm;
+  *l_out = fa * l_a + fb * l_b;
+  for (int64_t k = 0; k < d; ++k) o_out[k] = fa * o_a[k] + fb * o_b[k];
 }
 
 void oracle_merge_all(const double* m, const double* l, int64_t n,

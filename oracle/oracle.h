@@ -139,6 +139,40 @@ int oracle_cross_entropy_rows(const void* x, int dtype, int64_t rows,
                               const int32_t* target, int64_t r0, int64_t r1,
                               double* loss, double* dx);
 
+/* Softmax-weighted sum of value vectors ("Online stable softmax", section
+ * on the weighted-value numerator; "Softmax numerics architecture", section
+ * on tiled attention): for rows [r0, r1),
+ *   out[r, k] = sum_j p[r, j] * v[g, j, k],   g = r / rows_per_group,
+ * p the three-pass softmax of row r under the mask. s is [rows, cols], v is
+ * [rows / rows_per_group, cols, d] and shares s's element format; out has
+ * (r1 - r0) * d entries. Policy: a poisoned row gives NaN, an empty row 0.
+ * row_status (may be NULL) has r1 - r0 entries. rows must be a multiple of
+ * rows_per_group.                                                           */
+int oracle_softmax_weighted_rows(const void* s, const void* v, int dtype,
+                                 int64_t rows, int64_t cols, int64_t d,
+                                 int64_t rows_per_group, const oracle_mask* mk,
+                                 int64_t r0, int64_t r1, double* out,
+                                 int32_t* row_status);
+
+/* Per-chunk online states (m, l, o) of rows [r0, r1): chunk c covers
+ * columns [c*chunk_cols, min((c+1)*chunk_cols, cols)); m and l as in
+ * oracle_chunk_stats, o[k] = sum over the chunk's finite valid lanes of
+ * exp(s_j - m) v[g, j, k]. m, l have (r1 - r0) * n_chunks entries, o has
+ * (r1 - r0) * n_chunks * d. Poisoned chunk: (NaN, NaN, NaN...); chunk with
+ * no finite valid lane: (-inf, 0, 0...).                                    */
+int oracle_weighted_chunk_states(const void* s, const void* v, int dtype,
+                                 int64_t rows, int64_t cols, int64_t d,
+                                 int64_t rows_per_group, const oracle_mask* mk,
+                                 int64_t chunk_cols, int64_t r0, int64_t r1,
+                                 double* m, double* l, double* o);
+
+/* The state merge (m_a, l_a, o_a) (+) (m_b, l_b, o_b): the (m, l) rule of
+ * oracle_merge, and o' = f_a o_a + f_b o_b with the same factors.          */
+void oracle_weighted_merge(double m_a, double l_a, const double* o_a,
+                           double m_b, double l_b, const double* o_b,
+                           int64_t d, double* m_out, double* l_out,
+                           double* o_out);
+
 /* Rounding of a double to an element format, to nearest-even with gradual
  * underflow. NaN becomes the canonical quiet NaN (f32 0x7FC00000, f16 0x7E00,
  * bf16 0x7FC0).                                                             */
