@@ -37,6 +37,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores
 MALL_BYTES = 256 * 2 ** 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 KERNEL_SOURCES = {
@@ -58,6 +59,8 @@ def parse():
     ap.add_argument("--next-ops", default="2,4",
                     help="workloads on which the log-softmax, softmax-backward and cross-entropy "
                          "entry points are also timed ('' for none)")
+    ap.add_argument("--no-weighted", dest="weighted", action="store_false",
+                    help="skip the softmax-weighted value sums on the config5 scores")
     ap.add_argument("--no-spread", action="store_true",
                     help="skip the single-launch spread loop (profiling runs)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -91,6 +94,14 @@ def algorithmic_bytes(w, path: str, n_chunks: int = 0) -> int:
     reads = 2 if path == "split" else 1
     summaries = 2 * rows * n_chunks * 8 if path == "split" else 0
     return reads * valid * s + rows * cols * s + mask_bytes + summaries
+
+
+def weighted_flops(w) -> int:
+    """Multiply-adds of softmax(s) @ V counted as 2 flops: one per valid
+    weight and value component (d = 128)."""
+    r = np.arange(w.rows, dtype=np.int64)
+    valid = int(np.clip(r % w.mask.causal_period + 1 + w.mask.causal_offset, 0, w.cols).sum())
+    return 2 * valid * 128
 
 
 def make_workload(k: int):
@@ -148,6 +159,20 @@ def time_workload(w, steps: int, warmup: int, calibrate_copy: bool = False, spre
 
         def call(i):
             smx.softmax_backward_rows(xs[i % copies], xs[(i + 1) % copies], ys[i % copies])
+    elif op == "softmax_weighted_rows":
+        import workloads as W
+
+        # config5's scores weight per group 2048 value vectors of width 128
+        groups = w.rows // w.mask.causal_period
+        vals = to_device(W.config5_values(w.seed, groups, w.cols, 128).reshape(-1, 128), w.dtype)
+        vals = vals.view(groups, w.cols, 128)
+        outs = [torch.empty((w.rows, 128), dtype=x0.dtype, device=x0.device) for _ in range(copies)]
+        nbytes = algorithmic_bytes(w, "wave") - w.rows * w.cols * 2  # the valid scores read, no y
+        nbytes += vals.numel() * 2 + w.rows * 128 * 2  # V read once, out written
+        path = "mfma"
+
+        def call(i):
+            smx.softmax_weighted_rows(xs[i % copies], vals, outs[i % copies], **kw)
     elif op == "softmax_cross_entropy_rows":
         import workloads as W
 
@@ -253,6 +278,7 @@ def main():
     cfgs = [int(c) for c in args.configs.split(",") if c]
     per = {}
     head = None
+    weighted = None
     for k in cfgs:
         w = make_workload(k)
         r = time_workload(w, args.steps, args.warmup, calibrate_copy=args.calibrate_copy and head is None,
@@ -268,6 +294,17 @@ def main():
         per[f"config{k}"] = entry
         print(f"# config{k} {w.name}: path={r['path']} {kgbs:.0f} GB/s per launch "
               f"({r['gpu_ms_per_launch'] * 1e3:.1f} us), {gbs:.0f} GB/s per step", file=sys.stderr, flush=True)
+        if k == 5 and args.weighted:
+            rw = time_workload(w, args.steps, args.warmup, spread=False, op="softmax_weighted_rows")
+            gw = rw["bytes"] / (rw["gpu_ms_per_launch"] * 1e-3) / 1e9
+            flops = weighted_flops(w)
+            tfw = flops / (rw["gpu_ms_per_launch"] * 1e-3) / 1e12
+            weighted = {"workload": w.name + "_values_d128", "path": "mfma", "algorithmic_bytes": rw["bytes"],
+                        "algorithmic_flops": flops, "gpu_ms_per_launch": round(rw["gpu_ms_per_launch"], 5),
+                        "GBps_launch": round(gw, 1), "frac_of_hbm_peak": round(gw / HBM_PEAK_GBS, 4),
+                        "TFLOPs_launch": round(tfw, 1), "frac_of_bf16_mfma_peak": round(tfw / MFMA_BF16_PEAK_TFLOPS, 4)}
+            print(f"# softmax_weighted_rows config5: {gw:.0f} GB/s, {tfw:.0f} TFLOP/s per launch "
+                  f"({rw['gpu_ms_per_launch'] * 1e3:.1f} us)", file=sys.stderr, flush=True)
         if head is None:
             head = (k, w, r, gbs, kgbs)
         else:
@@ -312,6 +349,8 @@ def main():
         "per_config": per,
         "next_ops": next_ops,
     }
+    if weighted is not None:
+        out["next_ops"]["softmax_weighted_rows"] = {"config5": weighted}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, r["bytes"])
     print(json.dumps(out), flush=True)

@@ -200,6 +200,33 @@ SMX_API int softmax_cross_entropy_rows_path(const void* x, const int32_t* target
                                             const smx_mask* valid_len_or_mask, smx_path path, int64_t chunk_cols,
                                             void* stream);
 
+/* softmax_weighted_rows — softmax-weighted sums of value vectors, the
+ * attention output for given scores ("Online stable softmax", section on the
+ * weighted-value numerator: besides m and l each row carries the numerator
+ * o = sum_j exp(s_j - m) V_j, rescaled by the same factor as l when the
+ * maximum moves; "Softmax numerics architecture", tiled attention: the
+ * output is o / l):
+ *   out[r, k] = sum_j softmax(s[r])_j * v[r / rows_per_group, j, k].
+ *   s  : device [rows, cols] scores in dtype (SMX_F16 or SMX_BF16), under
+ *        the mask exactly as softmax_rows; 16-byte aligned, cols % 8 == 0;
+ *   v  : device [rows / rows_per_group, cols, d] values in dtype, one matrix
+ *        per group of rows_per_group consecutive rows; 16-byte aligned;
+ *        expected finite (a non-finite value can reach any row of its group
+ *        whose block of columns covers it);
+ *   out: device [rows, d] in dtype, 8-byte aligned, overlapping neither s
+ *        nor v;
+ *   d  : 32, 64 or 128; rows must be a multiple of rows_per_group.
+ * The running state is fp32. The weights p enter the matrix cores as a
+ * high and a low 16-bit part (about 16 significant bits); the values enter
+ * exactly; products accumulate in fp32.
+ * Policy: a poisoned row (+inf/NaN in a valid lane) gives the canonical NaN
+ * in every component; an empty or fully masked row gives zeros. SMX_F32,
+ * other widths, misalignment and overlap are SMX_EINVAL; rows = 0 is a
+ * no-op. Asynchronous on stream. */
+SMX_API int softmax_weighted_rows(const void* s, const void* v, void* out, int64_t rows, int64_t cols, int64_t d,
+                                  int64_t rows_per_group, smx_dtype dtype, const smx_mask* valid_len_or_mask,
+                                  void* stream);
+
 /* softmax_backward_rows — the vector-Jacobian product of the softmax
  * ("Softmax numerics architecture", section on the Jacobian and the backward
  * pass: J = diag(p) - p p^T is never formed; dx = p * (g - g.p)).

@@ -88,6 +88,8 @@ def lib() -> C.CDLL:
         L.softmax_backward_rows.restype = i32
         L.softmax_backward_rows_path.argtypes = [vp, vp, vp, i64, i64, i32, i32, i64, vp]
         L.softmax_backward_rows_path.restype = i32
+        L.softmax_weighted_rows.argtypes = [vp, vp, vp, i64, i64, i64, i64, i32, mp, vp]
+        L.softmax_weighted_rows.restype = i32
         L.softmax_default_chunk_cols.argtypes = [i64, i64, i32]
         L.softmax_default_chunk_cols.restype = i64
         L.smx_last_error.argtypes = []
@@ -247,6 +249,29 @@ def softmax_cross_entropy_rows(x: torch.Tensor, target: torch.Tensor, loss: Opti
                                                _stream_handle(stream, x.device))
     _check(rc)
     return ls, g
+
+
+def softmax_weighted_rows(s: torch.Tensor, v: torch.Tensor, out: Optional[torch.Tensor] = None, *,
+                          valid_len=None, causal_period=None, causal_offset: int = 0, keep=None,
+                          stream=None) -> torch.Tensor:
+    """out[r] = softmax(s[r]) @ v[r // rows_per_group]: s [rows, cols], v [groups, cols, d]
+    (rows_per_group = rows / groups), out [rows, d], all float16 or all bfloat16."""
+    rows, cols = _rows_cols(s)
+    if v.dim() != 3 or v.shape[1] != cols or v.dtype != s.dtype or not v.is_contiguous():
+        raise ValueError("v must be a contiguous [groups, cols, d] tensor of s's dtype")
+    _on(v, s.device, "v")
+    groups, _, d = v.shape
+    if groups == 0 or rows % groups != 0:
+        raise ValueError("rows must be a multiple of the number of value matrices")
+    o = torch.empty((rows, d), dtype=s.dtype, device=s.device) if out is None else out
+    if o.shape != (rows, d) or o.dtype != s.dtype or not o.is_contiguous():
+        raise ValueError("out must be a contiguous [rows, d] tensor of s's dtype")
+    _on(o, s.device, "out")
+    m, keepalive = make_mask(rows, cols, valid_len, causal_period, causal_offset, keep, s.device)
+    rc = lib().softmax_weighted_rows(s.data_ptr(), v.data_ptr(), o.data_ptr(), rows, cols, d, rows // groups,
+                                     _dtype_code(s), _mask_arg(m), _stream_handle(stream, s.device))
+    _check(rc)
+    return o
 
 
 def softmax_backward_rows(p: torch.Tensor, g: torch.Tensor, out: Optional[torch.Tensor] = None, *,

@@ -345,6 +345,37 @@ int softmax_backward_rows(const void* p, const void* g, void* dx, int64_t rows, 
   return softmax_backward_rows_path(p, g, dx, rows, cols, dtype, SMX_PATH_AUTO, 0, stream);
 }
 
+int softmax_weighted_rows(const void* s, const void* v, void* out, int64_t rows, int64_t cols, int64_t d,
+                          int64_t rows_per_group, smx_dtype dtype, const smx_mask* mask, void* stream) {
+  Call c;
+  if (int rc = check_common(s, nullptr, rows, cols, (int)dtype, mask, false, c)) return rc;
+  if (dtype == SMX_F32)
+    return fail(SMX_EINVAL, "softmax_weighted_rows takes SMX_F16 or SMX_BF16 (16-bit matrix-core operands)");
+  if (!pv_supported_d(d)) return fail(SMX_EINVAL, "d = %lld: the value width must be 32, 64 or 128", (long long)d);
+  if (rows_per_group <= 0 || rows % rows_per_group != 0)
+    return fail(SMX_EINVAL, "rows (%lld) must be a positive multiple of rows_per_group (%lld)", (long long)rows,
+                (long long)rows_per_group);
+  if (cols % 8 != 0) return fail(SMX_EINVAL, "cols (%lld) must be a multiple of 8", (long long)cols);
+  if (rows == 0) return ok();
+  const int64_t groups = rows / rows_per_group;
+  if (cols > 0 && groups > INT64_MAX / cols / d / 2) return fail(SMX_EINVAL, "the size of v overflows int64");
+  if (rows > INT64_MAX / d / 2) return fail(SMX_EINVAL, "the size of out overflows int64");
+  if (out == nullptr || (cols > 0 && v == nullptr)) return fail(SMX_EINVAL, "v and out must not be NULL");
+  if ((uintptr_t)s % 16 != 0 || (uintptr_t)v % 16 != 0 || (uintptr_t)out % 8 != 0)
+    return fail(SMX_EINVAL, "s and v must be 16-byte aligned and out 8-byte aligned");
+  if (c.a.mask.kind == SMX_MASK_KEEP_BYTES && (uintptr_t)c.a.mask.keep % 8 != 0)
+    return fail(SMX_EINVAL, "keep must be 8-byte aligned");
+  const uintptr_t oa = (uintptr_t)out, ob = (uintptr_t)(rows * d * 2);
+  const uintptr_t sa = (uintptr_t)s, sb = (uintptr_t)(rows * cols * 2);
+  const uintptr_t va = (uintptr_t)v, vb = (uintptr_t)(groups * cols * d * 2);
+  if ((sb > 0 && oa < sa + sb && sa < oa + ob) || (vb > 0 && oa < va + vb && va < oa + ob))
+    return fail(SMX_EINVAL, "out overlaps s or v");
+  const hipError_t err = launch_pv((const char*)s, (const char*)v, (char*)out, rows, cols, d, rows_per_group,
+                                   c.dtype, c.a.mask, (hipStream_t)stream);
+  if (err != hipSuccess) return hip_fail(err, "kernel launch");
+  return ok();
+}
+
 const char* smx_last_error(void) { return g_err; }
 
 }  // extern "C"

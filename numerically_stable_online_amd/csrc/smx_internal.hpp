@@ -78,4 +78,9 @@ hipError_t launch_bwd_rows(const char* p, const char* g, char* dx, int64_t rows,
 hipError_t launch_bwd_split(const char* p, const char* g, char* dx, int64_t rows, int64_t cols, int dtype, bool vec,
                             int64_t chunk, int64_t n_chunks, float2* partials, hipStream_t stream);
 
+// --- softmax-weighted value sums on the matrix cores (k_pv.hip) ---
+bool pv_supported_d(int64_t d);
+hipError_t launch_pv(const char* s, const char* v, char* out, int64_t rows, int64_t cols, int64_t d,
+                     int64_t rows_per_group, int dtype, const MaskArgs& mask, hipStream_t stream);
+
 }  // namespace smx

@@ -311,3 +311,57 @@ def check_xent(loss_got, dx_raw, dtype, loss_ref, dx_ref, x_float, target, what=
         out["dx_max_ulp"] = worst
         out["dx_exact_lanes"] = exact_where_clear(bits, dx_ref, dtype, numl, CLEAR_REL * np.abs(dx_ref), what)
     return out
+
+
+# ---------------------------------------------------------------------------
+# Softmax-weighted value sums (out = softmax(s) @ V)
+# ---------------------------------------------------------------------------
+#
+# The kernel's error in fp32, before the final rounding, is bounded by
+# 2^-14 * sum_j p_j |V_jk| + 2^-30 (the weights enter as 16-bit hi + lo
+# pairs, about 2^-17 relative down to 2^-39; fp32 accumulation over up to
+# 2 * cols / 16 matrix-core steps adds at most a few 2^-24 each; the
+# absolute term covers the weights below 2^-39 that fp16 cannot carry), so
+# an output component must be within 1 ulp of the correctly rounded oracle
+# value or within that bound, and exactly the rounded value wherever the
+# reference is clear of a rounding midpoint by more than the bound. Policy:
+# poisoned rows are the canonical NaN in every component, empty rows +0.0.
+
+WEIGHTED_TOL = 2.0 ** -14
+WEIGHTED_FLOOR = 2.0 ** -30
+
+
+def _ordered16(bits: np.ndarray) -> np.ndarray:
+    b = bits.astype(np.int64)
+    return np.where(b & 0x8000, 0x8000 - (b & 0x7FFF), 0x8000 + b)
+
+
+def check_weighted(out_raw, dtype, ref, st, scale, what=""):
+    """out_raw: uint16 [rows, d]; ref, scale: float64 [rows, d] (scale =
+    sum_j p_j |V_jk|); st: row status."""
+    bits = bits_of(out_raw, dtype)
+    pois = st == oracle.ROW_POISON
+    empty = st == oracle.ROW_EMPTY
+    assert (bits[pois] == NAN_BITS[dtype]).all(), f"{what}: poisoned rows must be the canonical NaN"
+    assert (bits[empty] == 0).all(), f"{what}: empty rows must be +0.0"
+    ok = st == oracle.ROW_OK
+    if not ok.any():
+        return {}
+    y = oracle.decode(out_raw[ok], dtype) if out_raw[ok].size < 4096 else (
+        (out_raw[ok].astype(np.uint32) << 16).view(np.float32).astype(np.float64) if dtype == "bf16"
+        else out_raw[ok].view(np.float16).astype(np.float64))
+    r = ref[ok]
+    sc = scale[ok]
+    want = oracle.encode(r, dtype).astype(np.int64)
+    ulps = np.abs(_ordered16(bits[ok]) - _ordered16(want))
+    err = np.abs(y - r)
+    bound = WEIGHTED_TOL * sc + WEIGHTED_FLOOR
+    bad = (ulps > ULP_TOL) & (err > bound)
+    if bad.any():
+        i = tuple(np.argwhere(bad)[0])
+        raise AssertionError(f"{what}: {ulps[i]} ulp and error {err[i]:.3e} > {bound[i]:.3e} at {i} "
+                             f"(got {y[i]!r}, ref {r[i]!r})")
+    sel = np.ones(r.shape, dtype=bool)
+    exact = exact_where_clear(bits[ok], r, dtype, sel, bound, what)
+    return {"max_ulp": int(ulps.max()), "max_err_over_scale": float((err / np.maximum(sc, 1e-300)).max()),
+            "exact_lanes": exact, "lanes": int(r.size)}

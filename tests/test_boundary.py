@@ -37,6 +37,7 @@ def test_header_declares_the_entry_points():
     for n in ("softmax_rows", "softmax_rows_path", "softmax_row_stats", "softmax_merge_normalize",
               "log_softmax_rows", "log_softmax_rows_path", "softmax_backward_rows",
               "softmax_backward_rows_path", "softmax_cross_entropy_rows", "softmax_cross_entropy_rows_path",
+              "softmax_weighted_rows",
               "softmax_default_chunk_cols", "softmax_select_path", "smx_last_error"):
         assert n in names, names
 
@@ -100,6 +101,25 @@ def test_argument_checks_need_no_device(smx):
     assert L.softmax_row_stats(16, 4, 64, 0, None, 16, None, None) == EINVAL
     assert L.softmax_merge_normalize(16, 1 << 20, 4, 64, 0, None, 16, 4096, 3, None) == EINVAL
     assert "n_chunks" in smx.smx_last_error()
+
+
+def test_weighted_rows_argument_checks(smx):
+    L = smx.lib()
+    EINVAL = smx.SMX_EINVAL
+    # (s, v, out, rows, cols, d, rows_per_group, dtype, mask, stream)
+    cases = [
+        ((16, 4096, 1 << 20, 8, 64, 64, 8, 0, None, None), "SMX_F16 or SMX_BF16"),
+        ((16, 4096, 1 << 20, 8, 64, 48, 8, 2, None, None), "value width"),
+        ((16, 4096, 1 << 20, 8, 64, 64, 3, 2, None, None), "multiple of rows_per_group"),
+        ((16, 4096, 1 << 20, 8, 60, 64, 8, 2, None, None), "multiple of 8"),
+        ((18, 4096, 1 << 20, 8, 64, 64, 8, 2, None, None), "aligned"),
+        ((16, 4096, 16, 8, 64, 64, 8, 2, None, None), "overlaps"),
+        ((16, None, 1 << 20, 8, 64, 64, 8, 2, None, None), "NULL"),
+    ]
+    for args, word in cases:
+        assert L.softmax_weighted_rows(*args) == EINVAL, word
+        assert word in smx.smx_last_error(), (word, smx.smx_last_error())
+    assert L.softmax_weighted_rows(None, None, None, 0, 64, 64, 8, 2, None, None) == 0
 
 
 def test_empty_shapes_are_noops(smx):

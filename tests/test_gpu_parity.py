@@ -616,3 +616,121 @@ def test_cross_entropy_in_place():
     loss2, dx2 = run_xent(w.x, "bf16", t, inplace=True)
     assert np.array_equal(loss, loss2) and np.array_equal(dx, dx2)
     check_xent_full(w.x, "bf16", t, w.mask, loss, dx, "xent in place")
+
+
+# ---------------------------------------------------------------------------
+# Softmax-weighted value sums: out[r] = softmax(s[r]) @ V[r // rows_per_group]
+# ---------------------------------------------------------------------------
+
+from smx_compare import check_weighted  # noqa: E402
+
+
+def run_weighted(s_raw, v_raw, dtype, mask=None):
+    rows, cols = s_raw.shape
+    s = to_device(s_raw, dtype)
+    v = to_device(v_raw.reshape(-1, v_raw.shape[-1]), dtype).view(v_raw.shape)
+    out = smx.softmax_weighted_rows(s, v, **mask_kwargs(mask))
+    torch.cuda.synchronize()
+    return to_host(out, dtype)
+
+
+def abs_bits(v_raw, dtype):
+    return (v_raw & np.uint16(0x7FFF)).astype(np.uint16)
+
+
+def weighted_reference(s_raw, v_raw, dtype, rpg, mask, r0=0, r1=None):
+    ref, st = oracle.softmax_weighted_rows(s_raw, v_raw, dtype, rpg, mask, r0, r1)
+    scale, _ = oracle.softmax_weighted_rows(s_raw, abs_bits(v_raw, dtype), dtype, rpg, mask, r0, r1)
+    return ref, st, scale
+
+
+def _weighted_case(rng, dtype, rows_per_group, groups, cols, d, mask_kind):
+    rows = rows_per_group * groups
+    s = W.to_format(3.0 * rng.standard_normal((rows, cols)), dtype)
+    v = W.to_format(rng.standard_normal((groups, cols, d)), dtype)
+    if mask_kind == "none":
+        mask = W.MaskSpec("none")
+    elif mask_kind == "causal":
+        mask = W.MaskSpec("causal", causal_period=rows_per_group, causal_offset=3)
+    elif mask_kind == "valid_len":
+        vl = rng.integers(0, cols + 1, rows).astype(np.int32)
+        vl[:3] = [0, 1, cols]
+        mask = W.MaskSpec("valid_len", valid_len=vl)
+    else:
+        mask = W.MaskSpec("keep", keep=(rng.random((rows, cols)) < 0.7).astype(np.uint8))
+    # policy rows: NaN / +inf in a valid lane, NaN in a masked lane, all -inf
+    W.set_bits(s, 5, 0, dtype, W.QNAN[dtype])
+    W.set_bits(s, 6, 1, dtype, W.POS_INF[dtype])
+    s[7, :] = W.NEG_INF[dtype]
+    return s, v, mask
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("d", [32, 64, 128])
+def test_weighted_rows_small(dtype, d):
+    rng = np.random.default_rng(500 + d)
+    for mask_kind in ("none", "causal", "valid_len", "keep"):
+        # 130 rows per group: a second, two-row tile; 200 columns: three full
+        # blocks of 64 and a ragged one
+        s, v, mask = _weighted_case(rng, dtype, 130, 2, 200, d, mask_kind)
+        what = f"weighted {dtype} d={d} {mask_kind}"
+        banner(what)
+        out = run_weighted(s, v, dtype, mask)
+        ref, st, scale = weighted_reference(s, v, dtype, 130, mask)
+        res = check_weighted(out, dtype, ref, st, scale, what)
+        banner(f"{what}: {res}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_weighted_rows_special_values(dtype):
+    rng = np.random.default_rng(510)
+    rows, cols = 128, 64
+    s = W.to_format(4.0 * rng.standard_normal((rows, cols)), dtype)
+    # one-hot values (V = I): the output is the softmax itself
+    eye = W.to_format(np.eye(cols)[None], dtype)
+    out = run_weighted(s, eye, dtype)
+    p, cls, st = oracle.softmax_rows(s, dtype)
+    ref, st2, scale = weighted_reference(s, eye, dtype, rows, None)
+    assert np.array_equal(st, st2)
+    check_weighted(out, dtype, ref, st2, scale, f"weighted one-hot {dtype}")
+    # constant values: every row returns the constant exactly
+    c = W.to_format(rng.standard_normal(32), dtype)
+    vc = np.broadcast_to(c, (1, cols, 32)).copy()
+    out = run_weighted(s, vc, dtype)
+    assert np.array_equal(out, np.broadcast_to(c, (rows, 32))), f"weighted constant {dtype}"
+    # a single valid lane returns that lane's value row
+    vl = np.full(rows, 1, dtype=np.int32)
+    v = W.to_format(rng.standard_normal((1, cols, 64)), dtype)
+    out = run_weighted(s, v, dtype, W.MaskSpec("valid_len", valid_len=vl))
+    assert np.array_equal(out, np.broadcast_to(v[0, 0], (rows, 64))), f"weighted single lane {dtype}"
+
+
+def test_weighted_rows_config5_full():
+    """The attention workload at full size: 256 groups of 2048 x 2048 causal
+    bf16 scores (config5, with its injected policy rows) and per group 2048
+    value vectors of width 128. Every policy row is checked in every group;
+    numeric rows are checked against the oracle on a sample (the first, the
+    last and 6 random rows of every 8th group)."""
+    banner("weighted config5 generate")
+    w = W.config5()
+    v = W.config5_values()
+    banner("weighted config5 run")
+    out = run_weighted(w.x, v, "bf16", w.mask)
+    n = 2048
+    banner("weighted config5 policy rows")
+    for name, rows in w.special_rows.items():
+        sub = out[rows]
+        if name in ("pos_inf_valid", "nan_valid"):
+            assert (sub == 0x7FC0).all(), name
+        elif name == "all_neg_inf":
+            assert (sub == 0).all(), name
+    banner("weighted config5 sampled rows")
+    rng = np.random.default_rng(520)
+    worst = 0
+    for g in range(0, 256, 8):
+        picks = sorted({g * n, g * n + n - 1, *(g * n + rng.choice(n, 6, replace=False))})
+        for r in picks:
+            ref, st, scale = weighted_reference(w.x, v, "bf16", n, w.mask, r, r + 1)
+            res = check_weighted(out[r:r + 1], "bf16", ref, st, scale, f"weighted config5 row {r}")
+            worst = max(worst, res.get("max_ulp", 0))
+    banner(f"weighted config5: max ulp {worst}")

@@ -229,6 +229,18 @@ def config5(seed: int = 5, groups: int = 256, n: int = 2048, head_dim: int = 128
                     {k: np.asarray(v, dtype=np.int64) for k, v in special.items()})
 
 
+def config5_values(seed: int = 5, groups: int = 256, n: int = 2048, head_dim: int = 128) -> np.ndarray:
+    """Value vectors for config5's score groups (the attention workload that
+    weights them by the scores' softmax): per group an [n, head_dim] matrix
+    of seeded N(0, 1) values rounded to bf16. Returns uint16 bits
+    [groups, n, head_dim]."""
+    v = np.empty((groups, n, head_dim), dtype=np.uint16)
+    for g in range(groups):
+        rng = _rng(seed, g, 11)
+        v[g] = f32_to_bf16_bits(rng.standard_normal((n, head_dim), dtype=np.float32))
+    return v
+
+
 CONFIGS = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}
 
 
