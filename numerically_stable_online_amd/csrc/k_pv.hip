@@ -48,18 +48,30 @@ struct PvArgs {
   MaskArgs mask;
 };
 
-// fp16 weights are raised by 2^15 (p <= 1, so p 2^15 stays below the fp16
-// maximum) so that weights down to 2^-39 keep their precision instead of
-// becoming fp16 subnormals; the factor is divided out with 1 / l
+// A row's exponentials are taken against a reference maximum mr that only
+// moves when a block's maximum exceeds it by more than kSlack (natural log
+// units): weights stay below e^kSlack and the reference cancels in o / l, so
+// most blocks skip rescaling the accumulators. fp16 weights are also raised
+// by 2^12 (p 2^12 <= e^2 2^12 stays below the fp16 maximum) so that weights
+// down to 2^-36 keep their precision instead of becoming fp16 subnormals; the
+// factor is divided out with 1 / l.
 template <int DT>
-constexpr float kWeightScale = DT == kF16 ? 32768.0f : 1.0f;
+constexpr float kSlack = DT == kF16 ? 2.0f : 8.0f;
+template <int DT>
+constexpr float kWeightScale = DT == kF16 ? 4096.0f : 1.0f;
+// rows whose reference exceeds this in magnitude take exp(x - mr) with an
+// explicit subtraction; below it, 2^(x log2e + c) with one constant per row
+constexpr float kBiasedMax = 32768.0f;
 
-// 16-bit pair rounding of an fp32 weight: p = hi + lo to about 16 bits
+// Two fp32 weights as 16-bit hi + lo pairs (p = hi + lo to about 16 bits),
+// packed two to a word: one packed conversion for the high parts, the exact
+// residuals, one packed conversion for the low parts.
 template <int DT>
-__device__ __forceinline__ void split16(float p, uint16_t& hi, uint16_t& lo) {
-  hi = (uint16_t)enc<DT>(p);
-  const float r = p - dec<DT>(hi);  // exact: hi holds p's leading bits
-  lo = (uint16_t)enc<DT>(r);
+__device__ __forceinline__ void split_pair(float p0, float p1, uint32_t& hi, uint32_t& lo) {
+  hi = enc2<DT>(p0, p1);
+  const float r0 = p0 - dec<DT>(hi & 0xFFFFu);  // exact: hi holds p's leading bits
+  const float r1 = p1 - dec<DT>(hi >> 16);
+  lo = enc2<DT>(r0, r1);
 }
 
 template <int DT>
@@ -89,7 +101,7 @@ __device__ __forceinline__ int64_t block_max_i64(int64_t v, int64_t* slot) {
 }
 
 template <int DT, int D, bool KEEP>
-__global__ __launch_bounds__(kThreads) void k_pv(PvArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void k_pv(PvArgs a) {
   constexpr int S = 2;
   constexpr int NT = D / 32;  // 32-wide accumulator tiles along d
   __shared__ __attribute__((aligned(16))) uint16_t vt[D * kVtPitch];
@@ -126,85 +138,123 @@ __global__ __launch_bounds__(kThreads) void k_pv(PvArgs a) {
 #pragma unroll
     for (int i = 0; i < NT; ++i) acc[i] = f32x16{};
 
-    for (int64_t c0 = 0; c0 < extent; c0 += kPvBlock) {
-      // the block of V, transposed into LDS: thread q copies 16-byte chunks
-      // (8 values of one row of V); lane i of a wave takes V row i, so the
-      // LDS stores of a wave fill consecutive positions of one row of vt
-      __syncthreads();  // every wave is done with the previous block
+    // the next block's V chunks and scores, loaded while the current block
+    // is computed. Thread q of the copy takes 16-byte chunks q, q + 256, ...
+    // of the 64 x D block (chunk -> V row q % 64, d block q / 64): lane i of
+    // a wave takes V row i, so a wave's LDS stores fill consecutive
+    // positions of one row of vt.
+    constexpr int CH = kPvBlock * D / 8 / kThreads;
+    Pack<DT, 8> vnext[CH], snext[4];
+    uint64_t knext[4];
+    auto fetch = [&](int64_t c0) {
 #pragma unroll
-      for (int q = tid; q < kPvBlock * D / 8; q += kThreads) {
-        const int vrow = q % kPvBlock;
-        const int dblk = q / kPvBlock;
-        const int64_t j = c0 + vrow;
-        Pack<DT, 8> p;
-        p.fill(0);
-        if (j < cols) p.load(vg + (j * D + 8 * dblk) * S);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) vt[(8 * dblk + e) * kVtPitch + vrow] = (uint16_t)(p.w[e >> 1] >> (16 * (e & 1)));
+      for (int ch = 0; ch < CH; ++ch) {
+        const int q = tid + ch * kThreads;
+        const int64_t j = c0 + q % kPvBlock;
+        vnext[ch].fill(0);
+        if (j < cols) vnext[ch].load(vg + (j * D + 8 * (q / kPvBlock)) * S);
       }
-      __syncthreads();
-
-      // this lane's 32 scores: columns c0 + 32 h .. + 31 of its row
-      float x[32];
-      const int64_t cb = c0 + 32 * h;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const int64_t j0 = cb + 8 * k;
-        const int64_t left = prefix - j0;
-        const int rem = left <= 0 ? 0 : (left >= 8 ? 8 : (int)left);
-        Pack<DT, 8> p;
-        p.fill(0);
-        uint64_t kb = ~0ull;
-        if (rem > 0) {
-          p.template load<true>(srow + j0 * S);
-          if constexpr (KEEP) kb = load_keep<8>(a.mask.keep + row * cols + j0);
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const bool ok = e < rem && (!KEEP || keep_lane(kb, e));
-          x[8 * k + e] = ok ? p.get(e) : -kInf;
+        const int64_t j0 = c0 + 32 * h + 8 * k;
+        snext[k].fill(0);
+        knext[k] = ~0ull;
+        if (j0 < prefix) {
+          snext[k].template load<true>(srow + j0 * S);
+          if constexpr (KEEP) knext[k] = load_keep<8>(a.mask.keep + row * cols + j0);
         }
       }
+    };
+    if (extent > 0) fetch(0);
+
+    for (int64_t c0 = 0; c0 < extent; c0 += kPvBlock) {
+      __syncthreads();  // every wave is done with the previous block's vt
+#pragma unroll
+      for (int ch = 0; ch < CH; ++ch) {
+        const int q = tid + ch * kThreads;
+        const int vrow = q % kPvBlock;
+        const int dblk = q / kPvBlock;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          vt[(8 * dblk + e) * kVtPitch + vrow] = (uint16_t)(vnext[ch].w[e >> 1] >> (16 * (e & 1)));
+      }
+      // this lane's 32 scores: columns c0 + 32 h .. + 31 of its row; lanes
+      // are masked element by element only when some row of the wave ends
+      // inside its half block (or for arbitrary keep masks)
+      float x[32];
+      if (KEEP || __ballot(prefix < c0 + 32 * h + 32) != 0) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int64_t left = prefix - (c0 + 32 * h + 8 * k);
+          const int rem = left <= 0 ? 0 : (left >= 8 ? 8 : (int)left);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const bool ok = e < rem && (!KEEP || keep_lane(knext[k], e));
+            x[8 * k + e] = ok ? snext[k].get(e) : -kInf;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[8 * k + e] = snext[k].get(e);
+      }
+      __syncthreads();
+      if (c0 + kPvBlock < extent) fetch(c0 + kPvBlock);
+
       float bm = -kInf;
 #pragma unroll
       for (int i = 0; i < 32; ++i) bm = vmax(bm, x[i]);
       bm = vmax(bm, __shfl_xor(bm, 32));  // the other half of the row
-      const float m_new = vmax(m, bm);
-      // the old state's factor: exactly 1 when the maximum does not move
-      // (also when both are -inf: no -inf - -inf); 0 for an empty state
-      const float alpha = m == m_new ? 1.0f : __builtin_amdgcn_exp2f((m - m_new) * kLog2e);
+      // the reference moves to the block's maximum when that exceeds it by
+      // more than the slack (or is NaN / +inf, which poisons the row, or the
+      // row was empty so far); the old state then takes the factor
+      // exp(m - m'), exactly 1 when nothing moves
+      const float m_new = (bm <= m + kSlack<DT>) ? m : vmax(m, bm);
+      const bool moved = m_new != m && m != -kInf;  // an empty state holds zeros
+      if (__ballot(moved) != 0) {
+        const float alpha = moved ? __builtin_amdgcn_exp2f((m - m_new) * kLog2e) : 1.0f;
+        l *= alpha;
+#pragma unroll
+        for (int i = 0; i < NT; ++i) acc[i] *= alpha;
+      }
       m = m_new;
-      l *= alpha;
-#pragma unroll
-      for (int i = 0; i < NT; ++i) acc[i] *= alpha;
+      // exp(x - m) as 2^(x log2e + c), c = -m log2e: the rounding of c scales
+      // the row's weights and its l alike and cancels in o / l; a row with no
+      // finite lane yet uses m = 0, so masked lanes (-inf) give 0 without
+      // forming -inf - -inf
+      const float mu = m == -kInf ? 0.0f : m;
 
-      // weights p = exp(x - m) (0 for masked lanes), split into 16-bit pairs
-      u32x4 phi[4], plo[4];
+      // a wave holding a row with a large reference takes exp(x - m) with an
+      // explicit subtraction (rare: scores beyond 2^15)
+      float c = -mu * kLog2e;
+      if (__ballot(!(__builtin_fabsf(mu) < kBiasedMax)) != 0) {
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        uint16_t hi[8], lo[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float xv = x[8 * k + e];
-          const float p = xv == -kInf ? 0.0f : __builtin_amdgcn_exp2f((xv - m) * kLog2e);
-          l += p;
-          split16<DT>(p * kWeightScale<DT>, hi[e], lo[e]);
-        }
-        phi[k] = u32x4{hi[0] | ((uint32_t)hi[1] << 16), hi[2] | ((uint32_t)hi[3] << 16),
-                       hi[4] | ((uint32_t)hi[5] << 16), hi[6] | ((uint32_t)hi[7] << 16)};
-        plo[k] = u32x4{lo[0] | ((uint32_t)lo[1] << 16), lo[2] | ((uint32_t)lo[3] << 16),
-                       lo[4] | ((uint32_t)lo[5] << 16), lo[6] | ((uint32_t)lo[7] << 16)};
+        for (int i = 0; i < 32; ++i) x[i] -= mu;
+        c = 0.0f;
       }
 
-      // o^T += V^T p^T: k-step k pairs this lane's scores 8k .. 8k+7 (columns
-      // cb + 8k ..) with the same columns of V, read from vt
+      // per k-step: the weights p = exp(x - m) of this lane's scores 8k ..
+      // 8k+7 (0 for masked lanes) as 16-bit hi + lo pairs, then o^T += V^T
+      // p^T on the matrix cores with the same columns of V read from vt
+      // (columns c0 + 32 h + 8k ..)
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
+        uint32_t hw[4], lw[4];
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[8 * k + e], kLog2e, c));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[8 * k + e + 1], kLog2e, c));
+          l += p0 + p1;
+          split_pair<DT>(p0 * kWeightScale<DT>, p1 * kWeightScale<DT>, hw[e / 2], lw[e / 2]);
+        }
+        const u32x4 phi{hw[0], hw[1], hw[2], hw[3]};
+        const u32x4 plo{lw[0], lw[1], lw[2], lw[3]};
 #pragma unroll
         for (int i = 0; i < NT; ++i) {
           const u32x4 av = *reinterpret_cast<const u32x4*>(&vt[(32 * i + (lane & 31)) * kVtPitch + 32 * h + 8 * k]);
-          acc[i] = mfma<DT>(av, phi[k], acc[i]);
-          acc[i] = mfma<DT>(av, plo[k], acc[i]);
+          acc[i] = mfma<DT>(av, phi, acc[i]);
+          acc[i] = mfma<DT>(av, plo, acc[i]);
         }
       }
     }
