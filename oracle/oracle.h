@@ -1,6 +1,8 @@
 /*
  * oracle.h — plain, slow, double-precision CPU reference for batched
- * row-wise softmax, chunk summaries and their merge.
+ * row-wise softmax, chunk summaries and their merge, and for the entry
+ * points built on them (log-softmax, softmax backward, cross-entropy,
+ * softmax-weighted value sums).
  *
  * TEST INFRASTRUCTURE. Only the tests, the smoke check and the CPU-baseline
  * leg of the benchmark may load this library. The product path (the HIP
@@ -19,6 +21,12 @@
  *  - "Stable softmax: keep the normalizer consistent as tiles arrive", the
  *    paragraph on masks, and "Online stable softmax", section "Masks, empty
  *    rows, and precision": the mask / empty-row / inf / NaN contract.
+ *  - "Softmax numerics architecture", sections on log-sum-exp and on the
+ *    Jacobian: log-softmax, cross-entropy with logits and its gradient, the
+ *    softmax vector-Jacobian product.
+ *  - "Online stable softmax", section on the weighted-value numerator and
+ *    "Reference summary", and "Softmax numerics architecture", tiled
+ *    attention: the softmax-weighted value sums and their (m, l, o) states.
  *
  * All arithmetic is IEEE double, in the order written, compiled without
  * floating-point contraction. Inputs are decoded exactly; outputs are rounded
