@@ -34,9 +34,11 @@ namespace {
 
 constexpr int kPvRows = 128;    // rows per workgroup (four waves of 32)
 constexpr int kPvBlock = 64;    // columns per block (four matrix-core k-steps of 16)
-constexpr int kPvStages = 2;    // blocks resident in the LDS ring: one computed, one loading
+constexpr int kSStages = 3;     // score blocks in LDS: one read, two loading
+constexpr int kVStages = 2;     // V blocks in LDS: one read, one loading
 constexpr int kPiece = 64 * 16; // bytes one wave's direct global->LDS load moves
-constexpr int kSBytes = kPvRows * kPvBlock * 2;  // one score block: 128 rows of 128 bytes
+constexpr int kSBytes = kPvRows * kPvBlock * 2;        // one score block: 128 rows of 128 bytes
+constexpr int kSPieces = kSBytes / kPiece / kWaves;    // direct score loads per wave per block (4)
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -64,7 +66,7 @@ struct PvArgs {
 template <int DT>
 constexpr float kSlack = DT == kF16 ? 2.0f : 8.0f;
 template <int DT>
-constexpr float kWeightScale = DT == kF16 ? 4096.0f : 1.0f;
+constexpr float kLog2WeightScale = DT == kF16 ? 12.0f : 0.0f;
 // rows whose reference exceeds this in magnitude take exp(x - mr) with an
 // explicit subtraction; below it, 2^(x log2e + c) with one constant per row
 constexpr float kBiasedMax = 32768.0f;
@@ -75,17 +77,25 @@ constexpr float kBiasedMax = 32768.0f;
 constexpr int vmcnt_at_most(int n) { return (n & 0xF) | (((n >> 4) & 3) << 14) | (7 << 4) | (0xF << 8); }
 
 // One wave's direct 16-byte-per-lane global -> LDS load: lane i's 16 bytes
-// land at LDS byte address lds + 16 i (lds must be the same in every lane).
-// Issued as an instruction the compiler does not track, so that it inserts
-// no wait for it before later LDS accesses (which would empty the pipeline);
-// the kernel waits for these loads itself (vmcnt) before its barriers.
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds, bool nt) {
-  if (nt) {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt" : : "v"(g), "s"(lds) : "memory", "m0");
-  } else {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(lds) : "memory", "m0");
-  }
+// land at LDS byte address lds + 16 i (lds must be the same in every lane;
+// it travels in m0, and the load may not read m0 in the instruction right
+// after the write, hence the wait state). Issued as instructions the
+// compiler does not track, so that it inserts no wait for them before later
+// LDS accesses (which would empty the pipeline); the kernel waits for these
+// loads itself (vmcnt) before its barriers.
+__device__ __forceinline__ void dma16_global(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" : : "v"(g), "s"(lds) : "memory");
 }
+// the same from a wave-uniform base plus a 32-bit per-lane offset
+__device__ __forceinline__ void dma16_offset(uint32_t off, const void* base, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(base), "s"(lds) : "memory");
+}
+
+// 16 bytes of -inf in each 16-bit format (fp16, bf16): the source of every
+// score chunk that lies wholly past its row's valid prefix
+__device__ __attribute__((aligned(16))) const uint16_t kNegInfChunk[2][8] = {
+    {0xFC00, 0xFC00, 0xFC00, 0xFC00, 0xFC00, 0xFC00, 0xFC00, 0xFC00},
+    {0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80}};
 
 // A workgroup barrier that orders LDS accesses only: the wave's LDS stores
 // complete before it, but no global load is waited for.
@@ -95,10 +105,10 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// LDS layout of a stage: the score block (128 rows of 128 bytes), then the
-// V block (64 rows of D values, untransposed). Both are stored in 16-byte
-// chunks whose position in their row is XOR-swizzled by the row, so that
-// the reads below spread over the LDS banks.
+// LDS layout: a score block holds 128 rows of 128 bytes (eight 16-byte
+// chunks of 8 scores), a V block 64 rows of D values as they are in memory.
+// Chunks sit at a position XOR-swizzled by the row, so that the reads below
+// spread over the LDS banks.
 __device__ __forceinline__ int s_pos(int row, int chunk) { return chunk ^ (row & 7); }
 template <int D>
 __device__ __forceinline__ int v_pos(int row, int chunk) {
@@ -133,14 +143,14 @@ __device__ __forceinline__ f32x16 mfma(const i16x8& a, const u32x4& b, const f32
 }
 
 // the largest valid prefix among the workgroup's rows (the columns it visits)
-__device__ __forceinline__ int64_t block_max_i64(int64_t v, int64_t* slot) {
+__device__ __forceinline__ int block_max_int(int v, int* slot) {
   for (int off = 32; off > 0; off >>= 1) {
-    const int64_t o = __shfl_xor(v, off);
+    const int o = __shfl_xor(v, off);
     v = o > v ? o : v;
   }
   if ((threadIdx.x & 63) == 0) slot[threadIdx.x >> 6] = v;
   __syncthreads();
-  int64_t r = slot[0];
+  int r = slot[0];
 #pragma unroll
   for (int i = 1; i < kWaves; ++i) r = slot[i] > r ? slot[i] : r;
   __syncthreads();
@@ -150,17 +160,16 @@ __device__ __forceinline__ int64_t block_max_i64(int64_t v, int64_t* slot) {
 template <int DT, int D, bool KEEP>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void k_pv(PvArgs a) {
   constexpr int S = 2;
-  constexpr int NT = D / 32;                          // 32-wide accumulator tiles along d
-  constexpr int kVBytes = kPvBlock * D * S;
-  constexpr int kStage = kSBytes + kVBytes;
-  constexpr int kSPieces = kSBytes / kPiece / kWaves;  // 4 per wave
-  constexpr int kVPieces = kVBytes / kPiece;           // 16, 8 or 4
-  constexpr int kVPerWave = kVPieces / kWaves;         // 4, 2 or 1
-  constexpr int kLoads = kSPieces + kVPerWave;         // direct loads per wave per block
+  constexpr int NT = D / 32;                       // 32-wide accumulator tiles along d
+  constexpr int kVBytes = kPvBlock * D * S;        // one V block
+  constexpr int kVPieces = kVBytes / kPiece;       // 16, 8 or 4
+  constexpr int kVPerWave = kVPieces / kWaves;     // 4, 2 or 1
   constexpr int kVRowsPerPiece = kPiece / (D * S);
   constexpr int kVChunks = D / 8;
-  __shared__ __attribute__((aligned(1024))) char ring[kPvStages * kStage];
-  __shared__ int64_t red64[kWaves];
+  constexpr int kSRing = kSStages * kSBytes;
+  __shared__ __attribute__((aligned(1024))) char ring[kSRing + kVStages * kVBytes];
+  int* const slot = reinterpret_cast<int*>(ring);  // between tiles only, when no load is in flight
+
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int h = lane >> 5;  // which half of the block's columns this lane's scores cover
@@ -171,6 +180,32 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int64_t tiles_per_group = (rpg + kPvRows - 1) / kPvRows;
   const int64_t total = (a.rows / rpg) * tiles_per_group;
   const int64_t per_xcd = total / 8;
+  const void* const ninf = kNegInfChunk[DT == kBF16 ? 1 : 0];
+
+  // Lane constants. This lane's row is r_lds of the tile; of each block it
+  // takes chunks 4h .. 4h+3 (columns 32h .. 32h+31).
+  const int r_lds = wid * 32 + (lane & 31);
+  int s_off[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) s_off[k] = r_lds * 128 + 16 * s_pos(r_lds, 4 * h + k);
+  // Its direct score loads: piece q of wave w is LDS rows 32w + 8q .. + 7;
+  // lane i fills row 32w + 8q + i/8 at position i % 8, which holds chunk
+  // (i % 8) ^ (i / 8).
+  const int cc = 8 * ((lane & 7) ^ (lane >> 3));
+  // Its direct V loads: piece q of wave w is 1 KiB of consecutive V rows
+  const int vrow_in_piece = lane / kVChunks;
+  const uint32_t voff = (uint32_t)((wid * kVPerWave * kVRowsPerPiece + vrow_in_piece) * D * S +
+                                   16 * v_pos<D>(vrow_in_piece, lane % kVChunks));
+  // Its transposing V reads (k-step 0; k-step t adds 8 t rows): within each
+  // 16-lane group, lane 4e + q points at V row 32h + e, columns d0 .. d0+3
+  const int i16 = lane & 15, ee = i16 >> 2, qq = i16 & 3, dh = (lane >> 4) & 1;
+  int tr_off[NT];
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    const int vr = 32 * h + ee;
+    const int d0 = 32 * i + 16 * dh + 4 * qq;
+    tr_off[i] = vr * D * S + v_pos<D>(vr, d0 / 8) * 16 + (d0 % 8) * S;
+  }
 
   for (int64_t b = blockIdx.x; b < total; b += gridDim.x) {
     // XCD-aware order: the eight XCDs take workgroups round-robin, so
@@ -182,44 +217,50 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     const int64_t tile = tiles_per_group - 1 - lb % tiles_per_group;
     const int64_t row0 = g * rpg + tile * kPvRows;
     const int64_t row_end = (row0 + kPvRows < (g + 1) * rpg) ? row0 + kPvRows : (g + 1) * rpg;
-    const int64_t row = row0 + wid * 32 + (lane & 31);
+    const int64_t row = row0 + r_lds;
     const bool row_ok = row < row_end;
-    const int64_t prefix = row_ok ? valid_prefix(a.mask, row, cols) : 0;
-    const int64_t extent = block_max_i64(prefix, red64);
-    const int64_t nblocks = (extent + kPvBlock - 1) / kPvBlock;
-    const char* vg = a.v + g * cols * D * S;
+    const int prefix = row_ok ? (int)valid_prefix(a.mask, row, cols) : 0;
+    const int extent = block_max_int(prefix, slot);
+    const int nb = (extent + kPvBlock - 1) / kPvBlock;
+    const char* const vg = a.v + g * cols * D * S;
 
-    // this lane's share of a block's direct loads. Scores: wave w fills
-    // pieces 4w .. 4w+3 (8 rows each); lane i fills LDS row 8p + i / 8 at
-    // chunk position i % 8 with the chunk that position holds; a chunk past
-    // its row's valid prefix is replaced by the row's first chunk (cached,
-    // never used), so masked scores cost no HBM traffic. V: wave w fills
-    // pieces of kVRowsPerPiece rows; a row past the end is replaced by the
-    // last row (finite, weight 0).
-    const char* ld_base[kSPieces];
-    int64_t ld_prefix[kSPieces];
+    // this lane's score loads: the chunk at c0 + cc of its piece rows, or
+    // the -inf chunk once that chunk lies past the row's valid prefix (so
+    // masked scores cost no HBM traffic and arrive masked)
+    const char* sptr[kSPieces];
+    int slim[kSPieces];
 #pragma unroll
     for (int q = 0; q < kSPieces; ++q) {
-      const int r = 8 * (wid * kSPieces + q) + lane / 8;
-      const bool ok = row0 + r < row_end;
-      ld_base[q] = a.s + (ok ? row0 + r : row0) * cols * S;
-      ld_prefix[q] = ok ? valid_prefix(a.mask, row0 + r, cols) : 0;
+      const int64_t r = row0 + wid * 32 + 8 * q + (lane >> 3);
+      const bool ok = r < row_end;
+      sptr[q] = a.s + ((ok ? r : row0) * cols + cc) * S;
+      slim[q] = ok ? (int)valid_prefix(a.mask, r, cols) - cc : -1;
     }
-    auto issue = [&](int64_t blk) {
-      const uint32_t st = ring_lds + (uint32_t)(blk % kPvStages) * kStage;
-      const int64_t c0 = blk * kPvBlock;
+    auto issue_s = [&](int blk) {
+      const int c0 = blk * kPvBlock;
+      const uint32_t st = ring_lds + (uint32_t)((blk % kSStages) * kSBytes + wid * kSPieces * kPiece);
 #pragma unroll
       for (int q = 0; q < kSPieces; ++q) {
-        const int r = 8 * (wid * kSPieces + q) + lane / 8;
-        const int64_t col = c0 + 8 * s_pos(r, lane % 8);
-        dma16(ld_base[q] + (col < ld_prefix[q] ? col : 0) * S, st + (wid * kSPieces + q) * kPiece, true);
+        const void* src = c0 < slim[q] ? (const void*)(sptr[q] + (int64_t)c0 * S) : ninf;
+        dma16_global(src, st + q * kPiece);
       }
+    };
+    auto issue_v = [&](int blk) {
+      const int c0 = blk * kPvBlock;
+      const uint32_t st = ring_lds + (uint32_t)(kSRing + (blk & 1) * kVBytes + wid * kVPerWave * kPiece);
+      const char* base = vg + (int64_t)c0 * D * S;
+      if (c0 + kPvBlock <= cols) {
 #pragma unroll
-      for (int q = 0; q < kVPerWave; ++q) {
-        const int piece = wid * kVPerWave + q;
-        const int r = piece * kVRowsPerPiece + lane / kVChunks;
-        const int64_t vrow = c0 + r < cols ? c0 + r : cols - 1;
-        dma16(vg + (vrow * D + 8 * v_pos<D>(r, lane % kVChunks)) * S, st + kSBytes + piece * kPiece, false);
+        for (int q = 0; q < kVPerWave; ++q) dma16_offset(voff + q * kPiece, base, st + q * kPiece);
+      } else {
+        // the last block of rows whose length is not a multiple of the
+        // block: V rows past the end re-read the last row (weight 0)
+#pragma unroll
+        for (int q = 0; q < kVPerWave; ++q) {
+          const int r = (wid * kVPerWave + q) * kVRowsPerPiece + vrow_in_piece;
+          const int rr = c0 + r < cols ? r : (int)(cols - 1 - c0);
+          dma16_offset((uint32_t)(rr * D * S + 16 * v_pos<D>(r, lane % kVChunks)), base, st + q * kPiece);
+        }
       }
     };
 
@@ -228,73 +269,99 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
     for (int i = 0; i < NT; ++i) acc[i] = f32x16{};
 
+    // this lane's 32 scores of block blk: x[8k + e] is column c0 + 32h + 8k
+    // + e. Chunks past the valid prefix arrived as -inf; the chunk a row's
+    // prefix ends inside (and keep masks) are masked element by element.
+    auto load_scores = [&](int blk, float (&x)[32]) {
+      const char* st = ring + (blk % kSStages) * kSBytes;
 #pragma unroll
-    for (int pre = 0; pre < kPvStages - 1; ++pre)
-      if (pre < nblocks) issue(pre);
+      for (int k = 0; k < 4; ++k) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(st + s_off[k]);
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[8 * k + 2 * e] = dec<DT>(ws[e] & 0xFFFFu);
+          x[8 * k + 2 * e + 1] = dec<DT>(ws[e] >> 16);
+        }
+      }
+      const int lim = prefix - (blk * kPvBlock + 32 * h);  // valid lanes: i < lim
+      if constexpr (KEEP) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint64_t kb =
+              8 * k < lim ? load_keep<8>(a.mask.keep + row * cols + blk * kPvBlock + 32 * h + 8 * k) : 0;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[8 * k + e] = (8 * k + e < lim && keep_lane(kb, e)) ? x[8 * k + e] : -kInf;
+        }
+      } else if (__ballot(lim > 0 && lim < 32 && (lim & 7) != 0) != 0) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) x[i] = i < lim ? x[i] : -kInf;
+      }
+    };
 
-    for (int64_t blk = 0; blk < nblocks; ++blk) {
-      const int64_t c0 = blk * kPvBlock;
-      // this wave's loads of block blk have landed (at most the later
-      // blocks' are outstanding); after the barrier every wave's have, and
-      // every wave is done with the stage that the next issue refills
-      if (blk + kPvStages - 2 < nblocks && kPvStages > 2) {
-        __builtin_amdgcn_s_waitcnt(vmcnt_at_most(kLoads * (kPvStages - 2)));
+    // the weights of k-step t (x[8t .. 8t+7]) as 16-bit hi + lo pairs
+    auto weights = [&](const float (&x)[32], int t, float c, u32x4& wh, u32x4& wl) {
+      uint32_t hw[4], lw[4];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const float q0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[8 * t + e], kLog2e, c));
+        const float q1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[8 * t + e + 1], kLog2e, c));
+        l += q0 + q1;
+        split_pair<DT>(q0, q1, hw[e / 2], lw[e / 2]);
+      }
+      wh = u32x4{hw[0], hw[1], hw[2], hw[3]};
+      wl = u32x4{lw[0], lw[1], lw[2], lw[3]};
+    };
+
+    // o^T += V^T p^T for k-step t of the V block in stage vst: V's operand
+    // is read transposed (each 16-lane group's read hands lane i rows
+    // k .. k+3 of column i; a second read takes rows k+4 .. k+7)
+    auto products = [&](int vst, int t, const u32x4& wh, const u32x4& wl) {
+      const char* vs = ring + kSRing + vst * kVBytes + t * 8 * D * S;
+      i16x8 av[NT];
+#pragma unroll
+      for (int i = 0; i < NT; ++i) {
+        const i16x4 lo4 =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(vs + tr_off[i]));
+        const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(vs + tr_off[i] + 4 * D * S));
+        av[i] = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+#pragma unroll
+      for (int i = 0; i < NT; ++i) acc[i] = mfma<DT>(av[i], wh, acc[i]);
+#pragma unroll
+      for (int i = 0; i < NT; ++i) acc[i] = mfma<DT>(av[i], wl, acc[i]);
+    };
+
+    // Loads: the scores of block blk are issued two blocks ahead, V one
+    // block ahead; at the top of block blk its scores and V have landed.
+    if (nb > 0) {
+      issue_s(0);
+      issue_v(0);
+      if (nb > 1) issue_s(1);
+    }
+    for (int blk = 0; blk < nb; ++blk) {
+      if (blk + 1 < nb) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_at_most(kSPieces));
       } else {
         __builtin_amdgcn_s_waitcnt(vmcnt_at_most(0));
       }
       lds_barrier();
-      if (blk + kPvStages - 1 < nblocks) issue(blk + kPvStages - 1);
+      if (blk + 1 < nb) issue_v(blk + 1);
+      if (blk + 2 < nb) issue_s(blk + 2);
 
-      const char* st = ring + (int)(blk % kPvStages) * kStage;
-      const char* vs = st + kSBytes;
-      const int r_lds = wid * 32 + (lane & 31);
-
-      // this lane's 32 scores, columns c0 + 32 h .. + 31 of its row; lanes
-      // are masked element by element only when some row of the wave ends
-      // inside its half block (or for arbitrary keep masks)
-      Pack<DT, 8> sp[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const u32x4 w = *reinterpret_cast<const u32x4*>(st + r_lds * 128 + s_pos(r_lds, 4 * h + k) * 16);
-        sp[k].w[0] = w.x;
-        sp[k].w[1] = w.y;
-        sp[k].w[2] = w.z;
-        sp[k].w[3] = w.w;
-      }
       float x[32];
-      if (KEEP || __ballot(prefix < c0 + 32 * h + 32) != 0) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int64_t j0 = c0 + 32 * h + 8 * k;
-          const int64_t left = prefix - j0;
-          const int rem = left <= 0 ? 0 : (left >= 8 ? 8 : (int)left);
-          uint64_t kb = ~0ull;
-          if constexpr (KEEP) {
-            if (rem > 0) kb = load_keep<8>(a.mask.keep + row * cols + j0);
-          }
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const bool ok = e < rem && (!KEEP || keep_lane(kb, e));
-            x[8 * k + e] = ok ? sp[k].get(e) : -kInf;
-          }
-        }
-      } else {
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) x[8 * k + e] = sp[k].get(e);
-      }
-
+      load_scores(blk, x);
+      // The reference moves to the block's maximum when that exceeds it by
+      // more than the slack (or is NaN / +inf, which poisons the row, or
+      // the row was empty so far); the old state then takes exp(m - m'),
+      // exactly 1 when nothing moves.
       float bm = -kInf;
 #pragma unroll
       for (int i = 0; i < 32; ++i) bm = vmax(bm, x[i]);
       bm = vmax(bm, __shfl_xor(bm, 32));  // the other half of the row
-      // the reference moves to the block's maximum when that exceeds it by
-      // more than the slack (or is NaN / +inf, which poisons the row, or the
-      // row was empty so far); the old state then takes the factor
-      // exp(m - m'), exactly 1 when nothing moves
       const float m_new = (bm <= m + kSlack<DT>) ? m : vmax(m, bm);
-      const bool moved = m_new != m && m != -kInf;  // an empty state holds zeros
+      const bool moved = m_new != m && m > -kInf;  // an empty state holds zeros
       if (__ballot(moved) != 0) {
         const float alpha = moved ? __builtin_amdgcn_exp2f((m - m_new) * kLog2e) : 1.0f;
         l *= alpha;
@@ -302,51 +369,28 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         for (int i = 0; i < NT; ++i) acc[i] *= alpha;
       }
       m = m_new;
-      // exp(x - m) as 2^(x log2e + c), c = -m log2e: the rounding of c scales
-      // the row's weights and its l alike and cancels in o / l; a row with no
-      // finite lane yet uses m = 0, so masked lanes (-inf) give 0 without
-      // forming -inf - -inf. A wave holding a row with a large reference
-      // subtracts it explicitly (rare: scores beyond 2^15).
-      const float mu = m == -kInf ? 0.0f : m;
-      float c = -mu * kLog2e;
+      // exp(x - m) as 2^(x log2e + c), c = -m log2e plus the log2 of the
+      // fp16 weight scale: the rounding of c scales the row's weights and
+      // its l alike and cancels in o / l. A row with no finite reference
+      // uses 0, so masked lanes (-inf) give 0 without forming -inf - -inf; a
+      // wave holding a row with a large reference (|m| >= 2^15, rare)
+      // subtracts it explicitly instead.
+      const float mu = __builtin_fabsf(m) < kInf ? m : 0.0f;
+      float c = kLog2WeightScale<DT> - mu * kLog2e;
       if (__ballot(!(__builtin_fabsf(mu) < kBiasedMax)) != 0) {
 #pragma unroll
         for (int i = 0; i < 32; ++i) x[i] -= mu;
-        c = 0.0f;
+        c = kLog2WeightScale<DT>;
       }
 
-      // per k-step t: the weights of this lane's scores 8t .. 8t+7 (columns
-      // c0 + 32 h + 8t ..) as 16-bit hi + lo pairs, then o^T += V^T p^T on
-      // the matrix cores. V's operand is read transposed from the same
-      // columns of the V block: within each 16-lane group, lane 4e + q points
-      // at 4 values of V row (32 h + 8t + e) and the read hands lane i the 4
-      // consecutive rows of column i; a second read takes the next 4 rows.
-      const int i16 = lane & 15, ee = i16 >> 2, qq = i16 & 3, dh = (lane >> 4) & 1;
+      // the products of k-step t run while the weights of k-step t + 1 form
+      const int vst = blk & 1;
+      u32x4 wh[2], wl[2];
+      weights(x, 0, c, wh[0], wl[0]);
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        uint32_t hw[4], lw[4];
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const float q0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[8 * t + e], kLog2e, c));
-          const float q1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[8 * t + e + 1], kLog2e, c));
-          l += q0 + q1;
-          split_pair<DT>(q0 * kWeightScale<DT>, q1 * kWeightScale<DT>, hw[e / 2], lw[e / 2]);
-        }
-        const u32x4 phi{hw[0], hw[1], hw[2], hw[3]};
-        const u32x4 plo{lw[0], lw[1], lw[2], lw[3]};
-        const int vr0 = 32 * h + 8 * t + ee;
-        const int vr1 = vr0 + 4;
-#pragma unroll
-        for (int i = 0; i < NT; ++i) {
-          const int d0 = 32 * i + 16 * dh + 4 * qq;
-          const char* a0 = vs + vr0 * D * S + v_pos<D>(vr0, d0 / 8) * 16 + (d0 % 8) * S;
-          const char* a1 = vs + vr1 * D * S + v_pos<D>(vr1, d0 / 8) * 16 + (d0 % 8) * S;
-          const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)a0);
-          const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)a1);
-          const i16x8 av = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-          acc[i] = mfma<DT>(av, phi, acc[i]);
-          acc[i] = mfma<DT>(av, plo, acc[i]);
-        }
+        if (t < 3) weights(x, t + 1, c, wh[(t + 1) & 1], wl[(t + 1) & 1]);
+        products(vst, t, wh[t & 1], wl[t & 1]);
       }
     }
     lds_barrier();  // every wave is done with the ring before the next tile's loads
@@ -356,7 +400,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     if (!row_ok) continue;
     const bool poisoned = !(m < kInf);
     const bool empty = m == -kInf;
-    const float inv = 1.0f / (l * kWeightScale<DT>);
+    const float inv = 1.0f / l;  // l holds the scaled weights too
     char* orow = a.out + row * D * S;
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
