@@ -107,13 +107,22 @@ __device__ __forceinline__ void lds_barrier() {
 
 // LDS layout: a score block holds 128 rows of 128 bytes (eight 16-byte
 // chunks of 8 scores), a V block 64 rows of D values as they are in memory.
-// Chunks sit at a position XOR-swizzled by the row, so that the reads below
-// spread over the LDS banks.
-__device__ __forceinline__ int s_pos(int row, int chunk) { return chunk ^ (row & 7); }
+// Chunks sit at a position XOR-swizzled by the row so that every read below
+// is free of bank conflicts, whether the LDS serves 128 or 256 bytes a
+// clock: the score reads take one chunk of 16 consecutive rows (position
+// and the row's parity, which selects the 128-byte half, must differ for
+// every row); the transposing V reads take two adjacent chunks of 4
+// consecutive rows for each of two column groups.
+__device__ __forceinline__ int s_pos(int row, int chunk) { return chunk ^ (row & 7) ^ ((row >> 3) & 1); }
 template <int D>
 __device__ __forceinline__ int v_pos(int row, int chunk) {
-  constexpr int kMask = D / 8 - 1 < 7 ? D / 8 - 1 : 7;
-  return chunk ^ ((2 * row) & kMask);
+  if constexpr (D == 128) {
+    return chunk ^ ((row & 1) ? 10 : 0) ^ (((row >> 1) & 1) ? 4 : 0);
+  } else if constexpr (D == 64) {
+    return chunk ^ (2 * (row & 3));
+  } else {
+    return chunk ^ (2 * ((row >> 1) & 1));
+  }
 }
 
 // Two fp32 weights as 16-bit hi + lo pairs (p = hi + lo to about 16 bits),
@@ -190,8 +199,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   for (int k = 0; k < 4; ++k) s_off[k] = r_lds * 128 + 16 * s_pos(r_lds, 4 * h + k);
   // Its direct score loads: piece q of wave w is LDS rows 32w + 8q .. + 7;
   // lane i fills row 32w + 8q + i/8 at position i % 8, which holds chunk
-  // (i % 8) ^ (i / 8).
-  const int cc = 8 * ((lane & 7) ^ (lane >> 3));
+  // (i % 8) ^ (i / 8) ^ (q & 1).
+  int cc[kSPieces];
+#pragma unroll
+  for (int q = 0; q < kSPieces; ++q) cc[q] = 8 * ((lane & 7) ^ (lane >> 3) ^ (q & 1));
   // Its direct V loads: piece q of wave w is 1 KiB of consecutive V rows
   const int vrow_in_piece = lane / kVChunks;
   const uint32_t voff = (uint32_t)((wid * kVPerWave * kVRowsPerPiece + vrow_in_piece) * D * S +
@@ -224,7 +235,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     const int nb = (extent + kPvBlock - 1) / kPvBlock;
     const char* const vg = a.v + g * cols * D * S;
 
-    // this lane's score loads: the chunk at c0 + cc of its piece rows, or
+    // this lane's score loads: the chunk at c0 + cc[q] of its piece rows, or
     // the -inf chunk once that chunk lies past the row's valid prefix (so
     // masked scores cost no HBM traffic and arrive masked)
     const char* sptr[kSPieces];
@@ -233,8 +244,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     for (int q = 0; q < kSPieces; ++q) {
       const int64_t r = row0 + wid * 32 + 8 * q + (lane >> 3);
       const bool ok = r < row_end;
-      sptr[q] = a.s + ((ok ? r : row0) * cols + cc) * S;
-      slim[q] = ok ? (int)valid_prefix(a.mask, r, cols) - cc : -1;
+      sptr[q] = a.s + ((ok ? r : row0) * cols + cc[q]) * S;
+      slim[q] = ok ? (int)valid_prefix(a.mask, r, cols) - cc[q] : -1;
     }
     auto issue_s = [&](int blk) {
       const int c0 = blk * kPvBlock;
