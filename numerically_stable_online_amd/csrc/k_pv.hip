@@ -361,6 +361,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       if (blk + 1 < nb) issue_v(blk + 1);
       if (blk + 2 < nb) issue_s(blk + 2);
 
+      // a block past every row of the wave adds nothing (its weights are
+      // all 0): the wave keeps its loads and barriers but skips the work
+      if (__ballot(prefix > blk * kPvBlock) == 0) continue;
+
       float x[32];
       load_scores(blk, x);
       // The reference moves to the block's maximum when that exceeds it by
