@@ -705,6 +705,33 @@ def test_weighted_rows_special_values(dtype):
     assert np.array_equal(out, np.broadcast_to(v[0, 0], (rows, 64))), f"weighted single lane {dtype}"
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_weighted_rows_reference_paths(dtype):
+    """The slow paths of the running reference, against the oracle: rows whose
+    maximum climbs by 20 at every 64-column block (beyond either slack, so
+    the state is rescaled at every block), rows offset by +40000 and by
+    -40000 (references beyond 2^15 in magnitude are subtracted explicitly),
+    rows whose first third is -inf (the reference starts late); with one
+    row per group, a single ragged block of 8 columns, and several tiles."""
+    rng = np.random.default_rng(530)
+    for rpg, groups, cols, d in ((130, 2, 200, 128), (1, 40, 72, 64), (64, 2, 8, 32)):
+        rows = rpg * groups
+        x = rng.standard_normal((rows, cols))
+        j = np.arange(cols)
+        x[0::4] += 20.0 * (j // 64)
+        x[1::4] = 40000.0 + 100.0 * x[1::4]  # distinct values at the coarse spacing there
+        x[2::4] = -40000.0 + 100.0 * x[2::4]
+        s = W.to_format(x, dtype)
+        s[3::4, : cols // 3] = W.NEG_INF[dtype]
+        v = W.to_format(rng.standard_normal((groups, cols, d)), dtype)
+        what = f"weighted reference paths {dtype} rpg={rpg} cols={cols} d={d}"
+        banner(what)
+        out = run_weighted(s, v, dtype, W.MaskSpec("none"))
+        ref, st, scale = weighted_reference(s, v, dtype, rpg, None)
+        res = check_weighted(out, dtype, ref, st, scale, what)
+        banner(f"{what}: {res}")
+
+
 def test_weighted_rows_config5_full():
     """The attention workload at full size: 256 groups of 2048 x 2048 causal
     bf16 scores (config5, with its injected policy rows) and per group 2048
