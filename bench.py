@@ -61,6 +61,8 @@ def parse():
                          "entry points are also timed ('' for none)")
     ap.add_argument("--no-weighted", dest="weighted", action="store_false",
                     help="skip the softmax-weighted value sums on the config5 scores")
+    ap.add_argument("--no-copy-context", action="store_true",
+                    help="skip timing a plain device copy of the headline input (context only)")
     ap.add_argument("--no-spread", action="store_true",
                     help="skip the single-launch spread loop (profiling runs)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -235,6 +237,35 @@ def time_workload(w, steps: int, warmup: int, calibrate_copy: bool = False, spre
     }
 
 
+def device_copy(w, steps: int, warmup: int):
+    """A plain device-to-device copy of the workload's input (torch copy_,
+    the runtime's copy kernel), rotated through resident copies the same way
+    as the timed kernels: the streaming rate this machine reaches for the same
+    bytes, reported as context beside the roofline."""
+    import torch
+    from smx_compare import to_device
+
+    x0 = to_device(w.x, w.dtype)
+    nbytes = x0.numel() * x0.element_size()
+    copies = max(1, min(64, math.ceil(2 ** 30 / (2 * nbytes))))
+    xs = [x0] + [x0.clone() for _ in range(copies - 1)]
+    ys = [torch.empty_like(x0) for _ in range(copies)]
+    for i in range(warmup):
+        ys[i % copies].copy_(xs[i % copies])
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for i in range(steps):
+        ys[i % copies].copy_(xs[i % copies])
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / steps
+    return {"workload": w.name, "bytes": 2 * nbytes, "ms_per_copy": round(ms, 5),
+            "GBps": round(2 * nbytes / (ms * 1e-3) / 1e9, 1), "buffer_copies": copies}
+
+
 def cpu_baseline(w, nbytes: int):
     import oracle
 
@@ -351,6 +382,11 @@ def main():
     }
     if weighted is not None:
         out["next_ops"]["softmax_weighted_rows"] = {"config5": weighted}
+    if not args.no_copy_context:
+        cp = device_copy(w, args.steps, args.warmup)
+        out["context"] = {"device_copy": cp, "kernel_frac_of_copy": round(kgbs / cp["GBps"], 4)}
+        print(f"# device copy of the same input: {cp['GBps']:.0f} GB/s ({cp['ms_per_copy'] * 1e3:.1f} us); "
+              f"the kernel reaches {kgbs / cp['GBps']:.3f} of it", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, r["bytes"])
     print(json.dumps(out), flush=True)
