@@ -208,7 +208,8 @@ SMX_API int softmax_cross_entropy_rows_path(const void* x, const int32_t* target
  * output is o / l):
  *   out[r, k] = sum_j softmax(s[r])_j * v[r / rows_per_group, j, k].
  *   s  : device [rows, cols] scores in dtype (SMX_F16 or SMX_BF16), under
- *        the mask exactly as softmax_rows; 16-byte aligned, cols % 8 == 0;
+ *        the mask exactly as softmax_rows; 16-byte aligned, cols % 8 == 0,
+ *        cols <= 2^30;
  *   v  : device [rows / rows_per_group, cols, d] values in dtype, one matrix
  *        per group of rows_per_group consecutive rows; 16-byte aligned;
  *        expected finite (a non-finite value can reach any row of its group

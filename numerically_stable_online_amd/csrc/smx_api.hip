@@ -356,6 +356,8 @@ int softmax_weighted_rows(const void* s, const void* v, void* out, int64_t rows,
     return fail(SMX_EINVAL, "rows (%lld) must be a positive multiple of rows_per_group (%lld)", (long long)rows,
                 (long long)rows_per_group);
   if (cols % 8 != 0) return fail(SMX_EINVAL, "cols (%lld) must be a multiple of 8", (long long)cols);
+  if (cols > ((int64_t)1 << 30))
+    return fail(SMX_EINVAL, "cols (%lld) exceeds 2^30, the longest row the weighted sums take", (long long)cols);
   if (rows == 0) return ok();
   const int64_t groups = rows / rows_per_group;
   if (cols > 0 && groups > INT64_MAX / cols / d / 2) return fail(SMX_EINVAL, "the size of v overflows int64");

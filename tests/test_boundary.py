@@ -112,6 +112,7 @@ def test_weighted_rows_argument_checks(smx):
         ((16, 4096, 1 << 20, 8, 64, 48, 8, 2, None, None), "value width"),
         ((16, 4096, 1 << 20, 8, 64, 64, 3, 2, None, None), "multiple of rows_per_group"),
         ((16, 4096, 1 << 20, 8, 60, 64, 8, 2, None, None), "multiple of 8"),
+        ((16, 4096, 1 << 40, 8, (1 << 30) + 8, 64, 8, 2, None, None), "exceeds 2^30"),
         ((18, 4096, 1 << 20, 8, 64, 64, 8, 2, None, None), "aligned"),
         ((16, 4096, 16, 8, 64, 64, 8, 2, None, None), "overlaps"),
         ((16, None, 1 << 20, 8, 64, 64, 8, 2, None, None), "NULL"),
