@@ -9,8 +9,9 @@
 //
 // A workgroup of four waves owns 128 rows of one group; each wave owns 32 of
 // them. Blocks of 64 columns of the scores and of V travel HBM -> LDS by
-// direct loads into a two-stage ring (the next block loads while the
-// current one is computed). Per block:
+// direct loads into a ring (scores three stages deep, issued two blocks
+// ahead; V two stages, one block ahead); score chunks wholly past a row's
+// valid prefix are loaded from a -inf chunk instead of from HBM. Per block:
 //  * each lane takes 32 consecutive scores of its row (lanes l and l + 32
 //    share a row and take one half of the block each), folds them into the
 //    running maximum (NaN-propagating: a NaN or +inf in a valid lane
@@ -23,7 +24,8 @@
 //    accumulator's column is the lane's row, so each lane rescales only its
 //    own row. p enters as a high and a low 16-bit part (p = hi + lo to about
 //    16 bits), so the weights carry nearly fp32 precision into the fp32
-//    accumulation; the value vectors enter exactly.
+//    accumulation; the value vectors enter exactly;
+//  * a wave whose rows all end before the block skips its work.
 // The column order inside a block is permuted consistently between the
 // score operand and the value operand (the contraction does not depend on
 // it), so every lane's scores are 64 contiguous bytes of its row.
@@ -82,7 +84,10 @@ constexpr int vmcnt_at_most(int n) { return (n & 0xF) | (((n >> 4) & 3) << 14) |
 // after the write, hence the wait state). Issued as instructions the
 // compiler does not track, so that it inserts no wait for them before later
 // LDS accesses (which would empty the pipeline); the kernel waits for these
-// loads itself (vmcnt) before its barriers.
+// loads itself (vmcnt) before its barriers. m0 is not declared clobbered
+// (the compiler reserves it and ignores such a declaration): nothing the
+// compiler emits in this file uses m0, whose only writers are these two
+// statements.
 __device__ __forceinline__ void dma16_global(const void* g, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" : : "v"(g), "s"(lds) : "memory");
 }
