@@ -276,10 +276,18 @@ def cpu_baseline(w, nbytes: int):
         _, dt = oracle.softmax_rows_encode_mt(w.x, w.dtype, w.mask, threads)
         times.append(dt)
     med = float(np.median(times))
+    # the same oracle on one thread, as a second reference point
+    times1 = []
+    for _ in range(2):
+        _, dt = oracle.softmax_rows_encode_mt(w.x, w.dtype, w.mask, 1)
+        times1.append(dt)
+    med1 = float(np.median(times1))
     return {"value": nbytes / med / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"the whole {w.name} input ({w.rows}x{w.cols} {w.dtype}), {len(times)} runs, median "
                       f"{med:.3f} s, three-pass double-precision oracle writing {w.dtype}",
-            "seconds": med}
+            "seconds": med,
+            "single_thread": {"value": nbytes / med1 / 1e9, "unit": "GB/s", "cores": 1, "seconds": med1,
+                              "runs": len(times1)}}
 
 
 def load_traffic(path: str, kernel_sha: str, launch_bytes_key: str):
