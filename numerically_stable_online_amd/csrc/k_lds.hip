@@ -54,7 +54,9 @@ __global__ __launch_bounds__(NT) void k_lds(RowArgs a) {
 
     // packs out of LDS; masked lanes become -inf. A pack holds `rem` valid
     // lanes (E inside the prefix, 0 past it), so each lane's test is a 32-bit
-    // compare with a constant.
+    // compare with a constant. The cross-entropy's target lane becomes -inf
+    // too: it stays out of the sum of the others (its logit xt, read below,
+    // joins the maximum and the total), and its gradient is stored apart.
     float v[VPT][E];
     float mx = -kInf;
 #pragma unroll
@@ -75,7 +77,7 @@ __global__ __launch_bounds__(NT) void k_lds(RowArgs a) {
       }
 #pragma unroll
       for (int e = 0; e < E; ++e) {
-        const bool ok = e < rem && (!KEEP || keep_lane(kb, e));
+        const bool ok = e < rem && (!KEEP || keep_lane(kb, e)) && (EPI != kEpiXent || k * E + e != slot);
         v[k][e] = ok ? p.get(e) : -kInf;
       }
 #pragma unroll
@@ -93,6 +95,7 @@ __global__ __launch_bounds__(NT) void k_lds(RowArgs a) {
           xt = dec<DT>(*reinterpret_cast<const uint16_t*>(row_lds + t * S));
         }
       }
+      mx = vmax(mx, xt);  // the target's logit counts toward the maximum and the policy
     }
     // the maximum propagates NaN, so one reduction gives the row's maximum
     // and its policy: NaN or +inf in a valid lane poisons the row
@@ -152,11 +155,7 @@ __global__ __launch_bounds__(NT) void k_lds(RowArgs a) {
         for (int e = 0; e < E; ++e) {
           const float te = exp_acc_b64(v[k][e], mx);
           if constexpr (EPI != kEpiLogSoftmax) v[k][e] = te;
-          if constexpr (EPI == kEpiXent) {
-            ks.add(k * E + e == slot ? 0.0f : te);
-          } else {
-            ks.add(te);
-          }
+          ks.add(te);
         }
       float hi = ks.hi(), lo = ks.lo();
       block_pair_reduce<NW>(hi, lo, red);
@@ -183,11 +182,7 @@ __global__ __launch_bounds__(NT) void k_lds(RowArgs a) {
           for (int e = 0; e < E; ++e) {
             const float te = exp_hw_b64(v[k][e], mx);
             if constexpr (EPI != kEpiLogSoftmax) v[k][e] = te;
-            if constexpr (EPI == kEpiXent) {
-              s += k * E + e == slot ? 0.0f : te;
-            } else {
-              s += te;
-            }
+            s += te;
           }
       }
       total = block_sum<NW>(s, red);
@@ -220,13 +215,18 @@ __global__ __launch_bounds__(NT) void k_lds(RowArgs a) {
           if constexpr (EPI == kEpiLogSoftmax) {
             o[e] = minus_lse(v[k][e], lse);
           } else {
-            o[e] = (EPI == kEpiXent && k * E + e == slot) ? at_t : v[k][e] * inv;
+            o[e] = v[k][e] * inv;  // 0 at the cross-entropy's target, stored apart below
           }
         }
         Pack<DT, E> p;
         p.put_values(o);
         p.template store<true>(yr + j0 * S);
       }
+    }
+    // the cross-entropy's gradient at the target, over the 0 its pack wrote
+    // (the same thread, so the two stores land in order)
+    if constexpr (EPI == kEpiXent) {
+      if (slot >= 0 && a.y != nullptr) store_one<DT>(yr + t * S, at_t);
     }
     // the loss last, once the row's values are no longer live
     if constexpr (EPI == kEpiXent) {

@@ -274,13 +274,18 @@ __global__ __launch_bounds__(kThreads) void k_merge_normalize(RowArgs a, int64_t
             if constexpr (EPI == kEpiLogSoftmax) {
               o[e] = minus_lse(f, lse);
             } else {
-              o[e] = (EPI == kEpiXent && k * E + e == slot) ? at_t : exp_b64<ACC>(f, m) * inv;
+              o[e] = exp_b64<ACC>(f, m) * inv;
             }
           }
           Pack<DT, E> out;
           out.put_values(o);
           out.template store<true>(yr + j0 * S);
         }
+      }
+      // the cross-entropy's gradient at the target, over the value its pack
+      // wrote (the same thread, so the two stores land in order)
+      if constexpr (EPI == kEpiXent) {
+        if (slot >= 0) store_one<DT>(yr + t * S, at_t);
       }
     }
   }

@@ -65,12 +65,22 @@ __global__ __launch_bounds__(kThreads) void k_wave(RowArgs a) {
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         const bool ok = e < rem && (!KEEP || keep_lane(kb, e));
-        v[r][k][e] = ok ? p.get(e) : -kInf;
-        if constexpr (EPI == kEpiXent) xo[r] = k * E + e == slot[r] ? v[r][k][e] : xo[r];
+        const float val = ok ? p.get(e) : -kInf;
+        if constexpr (EPI == kEpiXent) {
+          // the target lane: its logit kept apart, -inf in the row (so it
+          // stays out of the sum of the others; its gradient is stored apart)
+          const bool at = k * E + e == slot[r];
+          xo[r] = at ? val : xo[r];
+          v[r][k][e] = at ? -kInf : val;
+        } else {
+          v[r][k][e] = val;
+        }
       }
 #pragma unroll
       for (int e = 0; e < E; ++e) mx[r] = vmax(mx[r], v[r][k][e]);
     }
+    // the target's logit counts toward the maximum and the policy
+    if constexpr (EPI == kEpiXent) mx[r] = vmax(mx[r], xo[r]);
   }
 
 #pragma unroll
@@ -147,11 +157,7 @@ __global__ __launch_bounds__(kThreads) void k_wave(RowArgs a) {
         for (int e = 0; e < E; ++e) {
           const float te = exp_acc_b64(v[r][k][e], m);
           if constexpr (EPI != kEpiLogSoftmax) v[r][k][e] = te;
-          if constexpr (EPI == kEpiXent) {
-            ks.add(k * E + e == slot[r] ? 0.0f : te);
-          } else {
-            ks.add(te);
-          }
+          ks.add(te);
         }
       float hi = ks.hi(), lo = ks.lo();
       wave_pair_reduce(hi, lo);
@@ -178,11 +184,7 @@ __global__ __launch_bounds__(kThreads) void k_wave(RowArgs a) {
           for (int e = 0; e < E; ++e) {
             const float te = exp_hw_b64(v[r][k][e], m);
             if constexpr (EPI != kEpiLogSoftmax) v[r][k][e] = te;
-            if constexpr (EPI == kEpiXent) {
-              s += k * E + e == slot[r] ? 0.0f : te;
-            } else {
-              s += te;
-            }
+            s += te;
           }
       }
       total = wave_sum(s);
@@ -222,11 +224,16 @@ __global__ __launch_bounds__(kThreads) void k_wave(RowArgs a) {
         if (a.y != nullptr && j0 < cols) {
           float o[E];
 #pragma unroll
-          for (int e = 0; e < E; ++e) o[e] = (EPI == kEpiXent && k * E + e == slot[r]) ? at_t : v[r][k][e] * inv;
+          for (int e = 0; e < E; ++e) o[e] = v[r][k][e] * inv;  // 0 at the cross-entropy's target
           Pack<DT, E> p;
           p.put_values(o);
           p.template store<true>(yr + j0 * S);
         }
+      }
+      // the cross-entropy's gradient at the target, over the 0 its pack wrote
+      // (the same lane, so the two stores land in order)
+      if constexpr (EPI == kEpiXent) {
+        if (slot[r] >= 0 && a.y != nullptr) store_one<DT>(yr + t * S, at_t);
       }
       // the loss last, once the row's values are no longer live
       if constexpr (EPI == kEpiXent) {

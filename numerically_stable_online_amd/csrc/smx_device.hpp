@@ -69,6 +69,16 @@ __device__ __forceinline__ uint32_t enc2(float a, float b) {
   }
 }
 
+// One element rounded as enc does, stored alone (2 or 4 bytes).
+template <int DT>
+__device__ __forceinline__ void store_one(char* p, float f) {
+  if constexpr (DT == kF32) {
+    *reinterpret_cast<uint32_t*>(p) = enc<DT>(f);
+  } else {
+    *reinterpret_cast<uint16_t*>(p) = (uint16_t)enc<DT>(f);
+  }
+}
+
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // E consecutive elements: one 128-bit access (E * S == 16) or one element.
