@@ -282,7 +282,13 @@ def cpu_baseline(w, nbytes: int):
         _, dt = oracle.softmax_rows_encode_mt(w.x, w.dtype, w.mask, 1)
         times1.append(dt)
     med1 = float(np.median(times1))
-    return {"value": nbytes / med / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+    cpu = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
+    return {"value": nbytes / med / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle", "cpu": cpu,
             "sample": f"the whole {w.name} input ({w.rows}x{w.cols} {w.dtype}), {len(times)} runs, median "
                       f"{med:.3f} s, three-pass double-precision oracle writing {w.dtype}",
             "seconds": med,
@@ -397,6 +403,7 @@ def main():
               f"the kernel reaches {kgbs / cp['GBps']:.3f} of it", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, r["bytes"])
+        out["cpu_baseline"]["gpu_over_oracle"] = round(gbs / out["cpu_baseline"]["value"], 1)
     print(json.dumps(out), flush=True)
 
 
