@@ -150,7 +150,7 @@ def test_config5_full():
 # Shapes, alignments, masks and paths
 # ---------------------------------------------------------------------------
 
-ODD_COLS = [1, 3, 7, 8, 63, 64, 65, 255, 511, 513, 1000, 2047, 2048, 2049, 4095, 4096, 4104, 8191, 16385, 33000]
+ODD_COLS = [1, 3, 7, 8, 63, 64, 65, 255, 511, 513, 1000, 2047, 2048, 2049, 4095, 4096, 4104, 8191, 8192, 16384, 16385, 33000]
 
 
 def _masks(rows, cols, rng):
@@ -429,7 +429,7 @@ def test_log_softmax_config5():
 @pytest.mark.parametrize("dtype", W.DTYPES)
 def test_log_softmax_odd_shapes_and_policy(dtype):
     rng = np.random.default_rng(200)
-    for cols in (1, 7, 64, 513, 2049, 5000):
+    for cols in (1, 7, 64, 513, 2048, 2049, 4096, 5000, 8192, 16384):
         rows = 11
         x = W.random_rows(rows, cols, dtype, seed=cols + 1, scale=30.0)
         W.set_bits(x, 2, 0, dtype, W.QNAN[dtype])
@@ -502,7 +502,7 @@ def test_backward_workloads(cfg, path):
 
 @pytest.mark.parametrize("dtype", W.DTYPES)
 def test_backward_odd_shapes(dtype):
-    for cols in (1, 3, 64, 511, 2048, 2049, 9000, 33000):
+    for cols in (1, 3, 64, 511, 512, 2048, 2049, 4096, 8192, 9000, 16384, 33000):
         rows = 9
         x = W.random_rows(rows, cols, dtype, seed=cols + 7, scale=10.0)
         p_raw, g_raw = bwd_inputs(x, dtype, None, seed=cols)
@@ -581,7 +581,7 @@ def test_cross_entropy_workloads(cfg, path):
 @pytest.mark.parametrize("dtype", W.DTYPES)
 def test_cross_entropy_confident_and_policy(dtype):
     rng = np.random.default_rng(301)
-    for cols in (2, 7, 64, 1000, 4096, 20000):
+    for cols in (2, 7, 64, 1000, 2048, 4096, 8192, 16384, 20000):
         rows = 12
         a = rng.standard_normal((rows, cols)) * 3
         t = rng.integers(0, cols, rows).astype(np.int32)
