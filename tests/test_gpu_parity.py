@@ -356,6 +356,93 @@ def test_nondefault_stream():
     check_full(w.x, "f16", w.mask, to_host(y, "f16"), "stream")
 
 
+def _same_bits(a, b):
+    a = a if isinstance(a, tuple) else (a,)
+    b = b if isinstance(b, tuple) else (b,)
+    return len(a) == len(b) and all(
+        torch.equal(u.contiguous().view(torch.uint8), v.contiguous().view(torch.uint8)) for u, v in zip(a, b))
+
+
+def _graph_cases():
+    """(name, inputs(seed) -> tensors, call(*tensors)) for every entry point and
+    path; the split paths allocate their stream-ordered workspace inside."""
+    def rows(r, c, dt, scale):
+        return lambda seed: [to_device(W.random_rows(r, c, dt, seed=seed, scale=scale), dt)]
+
+    vl = torch.from_numpy(np.random.default_rng(3).integers(0, 513, 4096).astype(np.int32)).cuda()
+    tgt = torch.from_numpy(W.class_targets(1024, 4096, 5)).cuda()
+
+    def weighted_inputs(seed):
+        rng = np.random.default_rng(seed)
+        s = to_device(W.to_format(3.0 * rng.standard_normal((256, 200)), "bf16"), "bf16")
+        v = to_device(W.to_format(rng.standard_normal((2 * 200, 64)), "bf16"), "bf16").view(2, 200, 64)
+        return [s, v]
+
+    return [
+        ("softmax, LDS path", rows(1024, 4096, "bf16", 8.0), lambda x: smx.softmax_rows(x)),
+        ("softmax, wave path, valid lengths", rows(4096, 512, "f16", 30.0),
+         lambda x: smx.softmax_rows(x, valid_len=vl)),
+        ("softmax, split path", rows(8, 300000, "f32", 4.0),
+         lambda x: smx.softmax_rows(x, path="split", chunk_cols=4096)),
+        ("log-softmax, LDS path", rows(1024, 4096, "bf16", 8.0), lambda x: smx.log_softmax_rows(x)),
+        ("cross-entropy, LDS path", rows(1024, 4096, "bf16", 8.0),
+         lambda x: smx.softmax_cross_entropy_rows(x, tgt)),
+        ("backward, split path", lambda seed: rows(8, 300000, "f32", 1.0)(seed) + rows(8, 300000, "f32", 1.0)(seed + 50),
+         lambda p, g: smx.softmax_backward_rows(p, g, path="split", chunk_cols=4096)),
+        ("weighted sums, causal", weighted_inputs,
+         lambda s, v: smx.softmax_weighted_rows(s, v, causal_period=128)),
+    ]
+
+
+def test_graph_capture_replays():
+    """Each call captured into a HIP graph and replayed with alternating inputs,
+    with eager work and synchronizations between the replays: every replay
+    equals the eager call on the same input bit for bit (the eager results are
+    the ones the other tests hold to the oracle)."""
+    for name, inputs, call in _graph_cases():
+        banner(f"graph: {name}")
+        a, b = inputs(1), inputs(2)
+        static = [t.clone() for t in a]
+        call(*static)  # warm-up outside the capture
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            out = call(*static)
+        for rep, src in enumerate((a, b, a, b)):
+            for dst, t in zip(static, src):
+                dst.copy_(t)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            ref = call(*[t.clone() for t in src])
+            torch.cuda.synchronize()
+            assert _same_bits(out, ref), f"{name}: replay {rep} differs from the eager call"
+        del g
+
+
+def test_two_streams_at_once():
+    """Split-path calls in flight on two streams at once (each call's workspace
+    is allocated in its own stream's order): every result equals the same call
+    made alone, bit for bit."""
+    xa = to_device(W.random_rows(8, 300000, "f32", seed=11, scale=4.0), "f32")
+    xb = to_device(W.random_rows(8, 300000, "f32", seed=12, scale=4.0), "f32")
+    ref_a = smx.softmax_rows(xa, path="split", chunk_cols=4096)
+    ref_b = smx.log_softmax_rows(xb, path="split", chunk_cols=4096)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    for _ in range(3):
+        with torch.cuda.stream(s1):
+            ya = smx.softmax_rows(xa, path="split", chunk_cols=4096)
+        with torch.cuda.stream(s2):
+            yb = smx.log_softmax_rows(xb, path="split", chunk_cols=4096)
+        outs.append((ya, yb))
+    s1.synchronize()
+    s2.synchronize()
+    for ya, yb in outs:
+        assert _same_bits(ya, ref_a) and _same_bits(yb, ref_b)
+
+
 def test_invalid_arguments_raise():
     x = torch.zeros(4, 8, device="cuda")
     with pytest.raises(smx.SmxError):
