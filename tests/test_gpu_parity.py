@@ -443,6 +443,60 @@ def test_two_streams_at_once():
         assert _same_bits(ya, ref_a) and _same_bits(yb, ref_b)
 
 
+def test_c_program_through_the_abi(tmp_path):
+    """A plain C program (tests/csrc/abi_from_c.c) calls every entry point of
+    include/smx.h on device buffers and a stream of its own, with no Python
+    in between; its results meet the oracle at the same bars as the
+    binding's, and an invalid call is rejected with a message."""
+    import os
+    import subprocess
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    libdir = os.path.dirname(smx.LIB_PATH)
+    exe = tmp_path / "abi_from_c"
+    subprocess.run(["gcc", "-std=c11", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include",
+                    f"-I{root}/include", f"{root}/tests/csrc/abi_from_c.c", "-L/opt/rocm/lib", "-lamdhip64",
+                    f"-L{libdir}", "-lsmx", "-Wl,-rpath,/opt/rocm/lib", f"-Wl,-rpath,{libdir}", "-o", str(exe)],
+                   check=True)
+    rows, cols, wrows, wcols, d, rpg, chunk = 300, 1000, 256, 200, 64, 128, 96
+    rng = np.random.default_rng(40)
+    x = W.random_rows(rows, cols, "f32", seed=41, scale=6.0)
+    vl = rng.integers(-2, cols + 3, rows).astype(np.int32)
+    vl[:3] = [0, 1, cols]
+    xb = W.random_rows(rows, cols, "bf16", seed=42, scale=8.0)
+    tgt = rng.integers(-1, cols + 1, rows).astype(np.int32)
+    g = W.random_rows(rows, cols, "f32", seed=43, scale=1.0)
+    sc = W.to_format(3.0 * rng.standard_normal((wrows, wcols)), "bf16")
+    v = W.to_format(rng.standard_normal((wrows // rpg, wcols, d)), "bf16")
+    inp, outp = tmp_path / "in.bin", tmp_path / "out.bin"
+    with open(inp, "wb") as f:
+        f.write(np.array([rows, cols, wrows, wcols, d, rpg, chunk], dtype=np.int64).tobytes())
+        for a in (x, vl, xb, tgt, g, sc, v):
+            f.write(np.ascontiguousarray(a).tobytes())
+    banner("C program through the ABI")
+    r = subprocess.run([str(exe), str(inp), str(outp)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "rejected:" in r.stdout and r.stdout.strip().endswith("ok"), r.stdout
+    raw = open(outp, "rb").read()
+    parts, off = [], 0
+    for dt, count in ((np.float32, rows * cols), (np.float32, rows * cols), (np.uint16, rows * cols),
+                      (np.float32, rows), (np.float32, rows), (np.uint16, rows * cols), (np.float32, rows * cols),
+                      (np.uint16, wrows * d)):
+        nbytes = count * np.dtype(dt).itemsize
+        parts.append(np.frombuffer(raw[off:off + nbytes], dtype=dt))
+        off += nbytes
+    assert off == len(raw)
+    y, y2, logp, lse, loss, dxb, dx, o = parts
+    mask = W.MaskSpec("valid_len", valid_len=vl)
+    check_full(x, "f32", mask, y.reshape(rows, cols), "C: softmax_rows")
+    check_full(x, "f32", mask, y2.reshape(rows, cols), "C: softmax_row_stats + softmax_merge_normalize")
+    check_log_full(xb, "bf16", mask, logp.reshape(rows, cols), lse, "C: log_softmax_rows")
+    check_xent_full(xb, "bf16", tgt, W.MaskSpec("none"), loss, dxb.reshape(rows, cols), "C: cross-entropy")
+    check_bwd_full(y.reshape(rows, cols), g, "f32", dx.reshape(rows, cols), "C: softmax_backward_rows")
+    ref, st, scale = weighted_reference(sc, v, "bf16", rpg, W.MaskSpec("causal", causal_period=rpg))
+    check_weighted(o.reshape(wrows, d), "bf16", ref, st, scale, "C: softmax_weighted_rows")
+
+
 def test_invalid_arguments_raise():
     x = torch.zeros(4, 8, device="cuda")
     with pytest.raises(smx.SmxError):
