@@ -51,8 +51,8 @@ KERNEL_NAME = {"lds": "k_lds", "wave": "k_wave", "split": "k_merge_normalize+k_s
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--configs", default="2,1,3,4,5",
                     help="workloads to time; the first is the headline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
