@@ -1,6 +1,6 @@
 """Benchmark: row-softmax effective HBM bandwidth on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--configs 1,2,3,4,5]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads spiked,small,masked,long,causal]
 
 One step is one softmax_rows call over one batch of the headline workload,
 8192 x 4096 bf16 rows (logits 8*N(0,1) plus a +30 spike per row), which the
@@ -18,8 +18,8 @@ roofline.achieved = the same bytes / the GPU time per launch: HIP events
 cpu_baseline = the CPU oracle (three-pass, double precision) on the same
          input, on the host cores, writing the element format.
 
-Prints one JSON line. Other workloads (--configs) are reported inside it
-under "per_config".
+Prints one JSON line. Other workloads (--workloads) are reported inside it
+under "per_workload".
 """
 from __future__ import annotations
 
@@ -53,14 +53,14 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--configs", default="2,1,3,4,5",
-                    help="workloads to time; the first is the headline")
+    ap.add_argument("--workloads", default="spiked,small,masked,long,causal",
+                    help="workloads to time (names in workloads.WORKLOADS); the first is the headline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--next-ops", default="2,4",
+    ap.add_argument("--next-ops", default="spiked,long",
                     help="workloads on which the log-softmax, softmax-backward and cross-entropy "
                          "entry points are also timed ('' for none)")
     ap.add_argument("--no-weighted", dest="weighted", action="store_false",
-                    help="skip the softmax-weighted value sums on the config5 scores")
+                    help="skip the softmax-weighted value sums on the causal scores")
     ap.add_argument("--no-copy-context", action="store_true",
                     help="skip timing a plain device copy of the headline input (context only)")
     ap.add_argument("--no-spread", action="store_true",
@@ -106,10 +106,12 @@ def weighted_flops(w) -> int:
     return 2 * valid * 128
 
 
-def make_workload(k: int):
+def make_workload(k: str):
     import workloads as W
 
-    return W.CONFIGS[k]()
+    if k not in W.WORKLOADS:
+        raise SystemExit(f"unknown workload {k!r}; known: {', '.join(W.WORKLOADS)}")
+    return W.WORKLOADS[k]()
 
 
 def time_workload(w, steps: int, warmup: int, calibrate_copy: bool = False, spread: bool = True,
@@ -164,9 +166,9 @@ def time_workload(w, steps: int, warmup: int, calibrate_copy: bool = False, spre
     elif op == "softmax_weighted_rows":
         import workloads as W
 
-        # config5's scores weight per group 2048 value vectors of width 128
+        # the causal scores weight per group 2048 value vectors of width 128
         groups = w.rows // w.mask.causal_period
-        vals = to_device(W.config5_values(w.seed, groups, w.cols, 128).reshape(-1, 128), w.dtype)
+        vals = to_device(W.causal_values(w.seed, groups, w.cols, 128).reshape(-1, 128), w.dtype)
         vals = vals.view(groups, w.cols, 128)
         outs = [torch.empty((w.rows, 128), dtype=x0.dtype, device=x0.device) for _ in range(copies)]
         nbytes = algorithmic_bytes(w, "wave") - w.rows * w.cols * 2  # the valid scores read, no y
@@ -320,11 +322,11 @@ def main():
     import numerically_stable_online_amd as smx
 
     smx.lib()
-    cfgs = [int(c) for c in args.configs.split(",") if c]
+    names = [c for c in args.workloads.split(",") if c]
     per = {}
     head = None
     weighted = None
-    for k in cfgs:
+    for k in names:
         w = make_workload(k)
         r = time_workload(w, args.steps, args.warmup, calibrate_copy=args.calibrate_copy and head is None,
                           spread=not args.no_spread)
@@ -336,10 +338,10 @@ def main():
                  "launch_ms_p10": round(r["launch_ms_p10"], 5), "launch_ms_p90": round(r["launch_ms_p90"], 5),
                  "GBps_step": round(gbs, 1), "GBps_launch": round(kgbs, 1),
                  "frac_of_peak": round(kgbs / HBM_PEAK_GBS, 4), "buffer_copies": r["copies"]}
-        per[f"config{k}"] = entry
-        print(f"# config{k} {w.name}: path={r['path']} {kgbs:.0f} GB/s per launch "
+        per[k] = entry
+        print(f"# {k} {w.name}: path={r['path']} {kgbs:.0f} GB/s per launch "
               f"({r['gpu_ms_per_launch'] * 1e3:.1f} us), {gbs:.0f} GB/s per step", file=sys.stderr, flush=True)
-        if k == 5 and args.weighted:
+        if k == "causal" and args.weighted:
             rw = time_workload(w, args.steps, args.warmup, spread=False, op="softmax_weighted_rows")
             gw = rw["bytes"] / (rw["gpu_ms_per_launch"] * 1e-3) / 1e9
             flops = weighted_flops(w)
@@ -348,7 +350,7 @@ def main():
                         "algorithmic_flops": flops, "gpu_ms_per_launch": round(rw["gpu_ms_per_launch"], 5),
                         "GBps_launch": round(gw, 1), "frac_of_hbm_peak": round(gw / HBM_PEAK_GBS, 4),
                         "TFLOPs_launch": round(tfw, 1), "frac_of_bf16_mfma_peak": round(tfw / MFMA_BF16_PEAK_TFLOPS, 4)}
-            print(f"# softmax_weighted_rows config5: {gw:.0f} GB/s, {tfw:.0f} TFLOP/s per launch "
+            print(f"# softmax_weighted_rows causal: {gw:.0f} GB/s, {tfw:.0f} TFLOP/s per launch "
                   f"({rw['gpu_ms_per_launch'] * 1e3:.1f} us)", file=sys.stderr, flush=True)
         if head is None:
             head = (k, w, r, gbs, kgbs)
@@ -356,22 +358,22 @@ def main():
             del w
 
     next_ops = {}
-    for k2 in [int(c) for c in args.next_ops.split(",") if c]:
+    for k2 in [c for c in args.next_ops.split(",") if c]:
         w2 = make_workload(k2)
         for op in ("log_softmax_rows", "softmax_backward_rows", "softmax_cross_entropy_rows"):
             r2 = time_workload(w2, args.steps, args.warmup, spread=False, op=op)
             g2 = r2["bytes"] / (r2["gpu_ms_per_launch"] * 1e-3) / 1e9
-            next_ops.setdefault(op, {})[f"config{k2}"] = {
+            next_ops.setdefault(op, {})[k2] = {
                 "workload": w2.name, "path": r2["path"], "algorithmic_bytes": r2["bytes"],
                 "gpu_ms_per_launch": round(r2["gpu_ms_per_launch"], 5), "GBps_launch": round(g2, 1),
                 "frac_of_peak": round(g2 / HBM_PEAK_GBS, 4)}
-            print(f"# {op} config{k2}: path={r2['path']} {g2:.0f} GB/s per launch "
+            print(f"# {op} {k2}: path={r2['path']} {g2:.0f} GB/s per launch "
                   f"({r2['gpu_ms_per_launch'] * 1e3:.1f} us)", file=sys.stderr, flush=True)
         del w2
 
     k, w, r, gbs, kgbs = head
     sha = kernel_source_sha(r["path"])
-    traffic = load_traffic(r["path"], sha, f"config{k}")
+    traffic = load_traffic(r["path"], sha, k)
     out = {
         "metric": "row-softmax effective HBM GB/s (read+write bytes/time) and % of MI355X peak",
         "value": round(gbs, 1),
@@ -391,11 +393,11 @@ def main():
         "roofline": {"bound": "hbm", "kernel": KERNEL_NAME[r["path"]], "achieved": round(kgbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(kgbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel_source_sha": sha},
-        "per_config": per,
+        "per_workload": per,
         "next_ops": next_ops,
     }
     if weighted is not None:
-        out["next_ops"]["softmax_weighted_rows"] = {"config5": weighted}
+        out["next_ops"]["softmax_weighted_rows"] = {"causal": weighted}
     if not args.no_copy_context:
         cp = device_copy(w, args.steps, args.warmup)
         out["context"] = {"device_copy": cp, "kernel_frac_of_copy": round(kgbs / cp["GBps"], 4)}

@@ -66,12 +66,12 @@ def test_select_path_for_workloads():
 
 
 @pytest.mark.parametrize("path", ["auto", "wave", "lds", "split"])
-def test_config1(path):
-    w = W.config1()
-    banner(f"config1 {path}")
+def test_small_rows(path):
+    w = W.small_rows()
+    banner(f"small {path}")
     y = run_rows(w.x, "f32", w.mask, path=path, chunk_cols=256 if path == "split" else 0)
-    r = check_full(w.x, "f32", w.mask, y, f"config1/{path}")
-    banner(f"config1 {path}: {r}")
+    r = check_full(w.x, "f32", w.mask, y, f"small/{path}")
+    banner(f"small {path}: {r}")
 
 
 @pytest.mark.parametrize("dtype", W.DTYPES)
@@ -94,56 +94,56 @@ def test_worked_example_printed_values():
 
 
 @pytest.mark.parametrize("path", ["auto", "wave", "split"])
-def test_config2_full(path):
-    w = W.config2()
-    banner(f"config2 {path}")
+def test_spiked_rows_full(path):
+    w = W.spiked_rows()
+    banner(f"spiked {path}")
     y = run_rows(w.x, "bf16", w.mask, path=path)
-    r = check_full(w.x, "bf16", w.mask, y, f"config2/{path}")
-    banner(f"config2 {path}: {r}")
+    r = check_full(w.x, "bf16", w.mask, y, f"spiked/{path}")
+    banner(f"spiked {path}: {r}")
 
 
 @pytest.mark.parametrize("path", ["auto", "lds", "split"])
-def test_config3_full(path):
-    w = W.config3()
-    banner(f"config3 {path}")
+def test_masked_rows_full(path):
+    w = W.masked_rows()
+    banner(f"masked {path}")
     y = run_rows(w.x, "f16", w.mask, path=path)
-    r = check_full(w.x, "f16", w.mask, y, f"config3/{path}")
-    banner(f"config3 {path}: {r}")
+    r = check_full(w.x, "f16", w.mask, y, f"masked/{path}")
+    banner(f"masked {path}: {r}")
 
 
 @pytest.mark.parametrize("chunk", [0, 4096, 100000])
-def test_config4_full(chunk):
-    w = W.config4()
-    banner(f"config4 split chunk={chunk}")
+def test_long_rows_full(chunk):
+    w = W.long_rows()
+    banner(f"long split chunk={chunk}")
     y = run_rows(w.x, "f32", w.mask, path="auto" if chunk == 0 else "split", chunk_cols=chunk)
-    r = check_full(w.x, "f32", w.mask, y, f"config4/chunk{chunk}")
-    banner(f"config4 chunk={chunk}: {r}")
+    r = check_full(w.x, "f32", w.mask, y, f"long/chunk{chunk}")
+    banner(f"long chunk={chunk}: {r}")
 
 
 @pytest.mark.timeout(600)
-def test_config5_full():
-    banner("config5 generate")
-    w = W.config5()
+def test_causal_scores_full():
+    banner("causal generate")
+    w = W.causal_scores()
     x = to_device(w.x, "bf16")
-    banner("config5 run")
+    banner("causal run")
     y = smx.softmax_rows(x, causal_period=w.mask.causal_period)
     torch.cuda.synchronize()
     del x
     y_raw = to_host(y, "bf16")
     del y
-    banner("config5 compare")
+    banner("causal compare")
     n = 2048
     worst = 0
     for g in range(w.rows // n):
         r0, r1 = g * n, (g + 1) * n
         p, cls, st = oracle.softmax_rows(w.x, "bf16", w.mask, r0, r1)
-        r = check(y_raw[r0:r1], "bf16", p, cls, st, f"config5/group{g}")
+        r = check(y_raw[r0:r1], "bf16", p, cls, st, f"causal/group{g}")
         worst = max(worst, r["max_ulp"])
     # the injected rows follow the declared policy
     nanrows = np.concatenate([w.special_rows["pos_inf_valid"], w.special_rows["nan_valid"]])
     assert (y_raw[nanrows] == 0x7FC0).all()
     assert (y_raw[w.special_rows["all_neg_inf"]] == 0).all()
-    banner(f"config5: max ulp {worst}")
+    banner(f"causal: max ulp {worst}")
 
 
 # ---------------------------------------------------------------------------
@@ -319,7 +319,7 @@ def test_merge_normalize_external_summaries_policy():
 # ---------------------------------------------------------------------------
 
 def test_determinism_and_aliasing():
-    w = W.config2(rows=512)
+    w = W.spiked_rows(rows=512)
     x = to_device(w.x, "bf16")
     for path in ("auto", "wave", "split"):
         y1 = smx.softmax_rows(x, path=path)
@@ -345,7 +345,7 @@ def test_no_stray_writes():
 
 
 def test_nondefault_stream():
-    w = W.config3(rows=1024)
+    w = W.masked_rows(rows=1024)
     x = to_device(w.x, "f16")
     vl = torch.from_numpy(w.mask.valid_len).cuda()
     s = torch.cuda.Stream()
@@ -539,28 +539,28 @@ def check_log_full(x_raw, dtype, mask, y, lse, what, r0=0, r1=None):
     return check_log(None if y is None else y[r0:r1], dtype, logp, lse_ref, lse[r0:r1], cls, st, xf, what)
 
 
-@pytest.mark.parametrize("cfg,path", [(1, "auto"), (1, "wave"), (1, "lds"), (1, "split"), (2, "auto"),
-                                      (2, "split"), (3, "auto"), (3, "split"), (4, "auto")])
+@pytest.mark.parametrize("cfg,path", [("small", "auto"), ("small", "wave"), ("small", "lds"), ("small", "split"), ("spiked", "auto"),
+                                      ("spiked", "split"), ("masked", "auto"), ("masked", "split"), ("long", "auto")])
 def test_log_softmax_workloads(cfg, path):
-    w = W.CONFIGS[cfg]()
-    banner(f"log config{cfg} {path}")
+    w = W.WORKLOADS[cfg]()
+    banner(f"log {cfg} {path}")
     y, lse = run_log(w.x, w.dtype, w.mask, path=path)
-    r = check_log_full(w.x, w.dtype, w.mask, y, lse, f"log config{cfg}/{path}")
-    banner(f"log config{cfg} {path}: {r}")
+    r = check_log_full(w.x, w.dtype, w.mask, y, lse, f"log {cfg}/{path}")
+    banner(f"log {cfg} {path}: {r}")
     _, lse_only = run_log(w.x, w.dtype, w.mask, path=path, want_y=False)
     assert np.array_equal(lse_only.view(np.uint32), lse.view(np.uint32))  # LSE-only: the same bits
 
 
 @pytest.mark.timeout(600)
-def test_log_softmax_config5():
-    banner("log config5 generate")
-    w = W.config5()
-    banner("log config5 run")
+def test_log_softmax_causal_scores():
+    banner("log causal generate")
+    w = W.causal_scores()
+    banner("log causal run")
     y, lse = run_log(w.x, "bf16", w.mask)
     n = 2048
     groups = list(range(0, 256, 8))
     for g in groups:
-        check_log_full(w.x, "bf16", w.mask, y, lse, f"log config5/group{g}", g * n, (g + 1) * n)
+        check_log_full(w.x, "bf16", w.mask, y, lse, f"log causal/group{g}", g * n, (g + 1) * n)
     nanrows = np.concatenate([w.special_rows["pos_inf_valid"], w.special_rows["nan_valid"]])
     assert (y[nanrows] == 0x7FC0).all() and np.isnan(lse[nanrows]).all()
     empty = w.special_rows["all_neg_inf"]
@@ -630,15 +630,15 @@ def check_bwd_full(p_raw, g_raw, dtype, dx, what):
                      W.to_float(g_raw, dtype).astype(np.float64), what)
 
 
-@pytest.mark.parametrize("cfg,path", [(1, "auto"), (1, "wave"), (1, "lds"), (1, "split"), (2, "auto"),
-                                      (2, "split"), (3, "auto"), (4, "auto")])
+@pytest.mark.parametrize("cfg,path", [("small", "auto"), ("small", "wave"), ("small", "lds"), ("small", "split"), ("spiked", "auto"),
+                                      ("spiked", "split"), ("masked", "auto"), ("long", "auto")])
 def test_backward_workloads(cfg, path):
-    w = W.CONFIGS[cfg]()
-    p_raw, g_raw = bwd_inputs(w.x, w.dtype, w.mask, seed=100 + cfg)
-    banner(f"backward config{cfg} {path}")
+    w = W.WORKLOADS[cfg]()
+    p_raw, g_raw = bwd_inputs(w.x, w.dtype, w.mask, seed=100 + w.seed)
+    banner(f"backward {cfg} {path}")
     dx = run_bwd(p_raw, g_raw, w.dtype, path=path)
-    r = check_bwd_full(p_raw, g_raw, w.dtype, dx, f"backward config{cfg}/{path}")
-    banner(f"backward config{cfg} {path}: {r}")
+    r = check_bwd_full(p_raw, g_raw, w.dtype, dx, f"backward {cfg}/{path}")
+    banner(f"backward {cfg} {path}: {r}")
 
 
 @pytest.mark.parametrize("dtype", W.DTYPES)
@@ -664,7 +664,7 @@ def test_backward_odd_shapes(dtype):
 
 
 def test_backward_in_place_and_deterministic():
-    w = W.config2(rows=256)
+    w = W.spiked_rows(rows=256)
     p_raw, g_raw = bwd_inputs(w.x, "bf16", w.mask, seed=3)
     a = run_bwd(p_raw, g_raw, "bf16")
     b = run_bwd(p_raw, g_raw, "bf16", inplace=True)
@@ -705,16 +705,16 @@ def check_xent_full(x_raw, dtype, target, mask, loss, dx, what):
     return check_xent(loss, dx, dtype, lr, dref, W.to_float(x_raw, dtype), target, what)
 
 
-@pytest.mark.parametrize("cfg,path", [(1, "auto"), (1, "wave"), (1, "lds"), (1, "split"), (2, "auto"),
-                                      (2, "split"), (3, "auto"), (3, "split"), (4, "auto")])
+@pytest.mark.parametrize("cfg,path", [("small", "auto"), ("small", "wave"), ("small", "lds"), ("small", "split"), ("spiked", "auto"),
+                                      ("spiked", "split"), ("masked", "auto"), ("masked", "split"), ("long", "auto")])
 def test_cross_entropy_workloads(cfg, path):
-    w = W.CONFIGS[cfg]()
-    t = xent_targets(w.rows, w.cols, seed=300 + cfg)
+    w = W.WORKLOADS[cfg]()
+    t = xent_targets(w.rows, w.cols, seed=300 + w.seed)
     t[::17] = -1  # ignored rows
-    banner(f"xent config{cfg} {path}")
+    banner(f"xent {cfg} {path}")
     loss, dx = run_xent(w.x, w.dtype, t, w.mask, path=path)
-    r = check_xent_full(w.x, w.dtype, t, w.mask, loss, dx, f"xent config{cfg}/{path}")
-    banner(f"xent config{cfg} {path}: {r}")
+    r = check_xent_full(w.x, w.dtype, t, w.mask, loss, dx, f"xent {cfg}/{path}")
+    banner(f"xent {cfg} {path}: {r}")
     loss2, _ = run_xent(w.x, w.dtype, t, w.mask, path=path, want_dx=False)
     assert np.array_equal(loss2.view(np.uint32), loss.view(np.uint32))  # loss alone: the same bits
 
@@ -745,13 +745,13 @@ def test_cross_entropy_confident_and_policy(dtype):
 
 
 def test_cross_entropy_in_place():
-    w = W.config4(rows=4, cols=1 << 16)
+    w = W.long_rows(rows=4, cols=1 << 16)
     t = xent_targets(4, 1 << 16, seed=9)
     for path in ("split", "auto"):
         loss, dx = run_xent(w.x, "f32", t, path=path)
         loss2, dx2 = run_xent(w.x, "f32", t, path=path, inplace=True)
         assert np.array_equal(loss, loss2) and np.array_equal(dx, dx2)
-    w = W.config2(rows=64)
+    w = W.spiked_rows(rows=64)
     t = xent_targets(64, 4096, seed=10)
     loss, dx = run_xent(w.x, "bf16", t)
     loss2, dx2 = run_xent(w.x, "bf16", t, inplace=True)
@@ -873,32 +873,32 @@ def test_weighted_rows_reference_paths(dtype):
         banner(f"{what}: {res}")
 
 
-def test_weighted_rows_config5_full():
-    """The attention workload at full size: 256 groups of 2048 x 2048 causal
-    bf16 scores (config5, with its injected policy rows) and per group 2048
+def test_weighted_rows_causal_full():
+    """The attention workload at full size: 256 groups of 2048 x 2048
+    bf16 causal scores (with their injected policy rows) and per group 2048
     value vectors of width 128. Every policy row is checked in every group;
     numeric rows are checked against the oracle on a sample (the first, the
     last and 6 random rows of every 8th group)."""
-    banner("weighted config5 generate")
-    w = W.config5()
-    v = W.config5_values()
-    banner("weighted config5 run")
+    banner("weighted causal generate")
+    w = W.causal_scores()
+    v = W.causal_values()
+    banner("weighted causal run")
     out = run_weighted(w.x, v, "bf16", w.mask)
     n = 2048
-    banner("weighted config5 policy rows")
+    banner("weighted causal policy rows")
     for name, rows in w.special_rows.items():
         sub = out[rows]
         if name in ("pos_inf_valid", "nan_valid"):
             assert (sub == 0x7FC0).all(), name
         elif name == "all_neg_inf":
             assert (sub == 0).all(), name
-    banner("weighted config5 sampled rows")
+    banner("weighted causal sampled rows")
     rng = np.random.default_rng(520)
     worst = 0
     for g in range(0, 256, 8):
         picks = sorted({g * n, g * n + n - 1, *(g * n + rng.choice(n, 6, replace=False))})
         for r in picks:
             ref, st, scale = weighted_reference(w.x, v, "bf16", n, w.mask, r, r + 1)
-            res = check_weighted(out[r:r + 1], "bf16", ref, st, scale, f"weighted config5 row {r}")
+            res = check_weighted(out[r:r + 1], "bf16", ref, st, scale, f"weighted causal row {r}")
             worst = max(worst, res.get("max_ulp", 0))
-    banner(f"weighted config5: max ulp {worst}")
+    banner(f"weighted causal: max ulp {worst}")

@@ -521,12 +521,12 @@ def test_stress_online_vs_three_pass_and_negative_control():
     assert wrong > 500  # the no-rescale version is caught on most rows
 
 
-def test_config_generators_shapes():
-    w = W.config1()
+def test_workload_generators_shapes():
+    w = W.small_rows()
     assert (w.rows, w.cols, w.dtype) == (64, 1024, "f32")
-    w = W.config3(rows=64)
+    w = W.masked_rows(rows=64)
     assert w.mask.kind == "valid_len" and w.mask.valid_len.min() >= 0 and w.mask.valid_len.max() <= 512
-    w = W.config5(groups=2, n=64, head_dim=16)
+    w = W.causal_scores(groups=2, n=64, head_dim=16)
     assert w.rows == 128 and all(len(v) == 2 for v in w.special_rows.values())
     p, cls, st = oracle.softmax_rows(w.x, "bf16", w.mask)
     for name in ("pos_inf_valid", "nan_valid"):

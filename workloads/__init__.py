@@ -9,19 +9,19 @@ masks as plain data.
 The five workload shapes stand in for the "attention-score rows" the source
 pages talk about; no public dataset or suite is involved:
 
-* ``config1`` fp32, 64 x 1024, logits 3*N(0,1); plus the two fixed rows
+* ``small_rows`` fp32, 64 x 1024, logits 3*N(0,1); plus the two fixed rows
   [20, 18, 17, -5] ("Softmax numerics architecture", worked fp16 example) and
   [1000, 999, 997] ("Online stable softmax", opening example).
-* ``config2`` bf16, 8192 x 4096, logits 8*N(0,1) plus +30 at one random
+* ``spiked_rows`` bf16, 8192 x 4096, logits 8*N(0,1) plus +30 at one random
   column per row.
-* ``config3`` fp16, 32768 x 512, logits U(-40, 40), per-row valid length
+* ``masked_rows`` fp16, 32768 x 512, logits U(-40, 40), per-row valid length
   uniform on {0, ..., 512}.
-* ``config4`` fp32, 64 x 1048576, logits 4*N(0,1) plus a ramp 50*j/(cols-1).
-* ``config5`` bf16, 256 groups x 2048 rows x 2048 cols, scores q.k^T/sqrt(128)
+* ``long_rows`` fp32, 64 x 1048576, logits 4*N(0,1) plus a ramp 50*j/(cols-1).
+* ``causal_scores`` bf16, 256 groups x 2048 rows x 2048 cols, scores q.k^T/sqrt(128)
   of N(0,1) q, k with head dimension 128, causal (row i of a group keeps
   columns 0..i), with five injected special rows per group.
 
-Every generator takes a seed (default: the config number) and optional
+Every generator takes a seed (defaults 1 to 5, in the order above) and optional
 smaller shapes, so a test can draw the same distribution at a size the
 oracle finishes in seconds.
 """
@@ -143,10 +143,10 @@ def _rng(seed, *stream) -> np.random.Generator:
 # The five workloads.
 # --------------------------------------------------------------------------
 
-def config1(seed: int = 1, rows: int = 64, cols: int = 1024) -> Workload:
+def small_rows(seed: int = 1, rows: int = 64, cols: int = 1024) -> Workload:
     rng = _rng(seed)
     x = (3.0 * rng.standard_normal((rows, cols))).astype(np.float32)
-    return Workload("config1_f32_64x1024", "f32", x, MaskSpec(), seed)
+    return Workload(f"f32_{rows}x{cols}", "f32", x, MaskSpec(), seed)
 
 
 def fixed_rows() -> List[Workload]:
@@ -157,36 +157,36 @@ def fixed_rows() -> List[Workload]:
             Workload("fixed_1000_999_997", "f32", b, MaskSpec(), 0)]
 
 
-def config2(seed: int = 2, rows: int = 8192, cols: int = 4096) -> Workload:
+def spiked_rows(seed: int = 2, rows: int = 8192, cols: int = 4096) -> Workload:
     rng = _rng(seed)
     x = 8.0 * rng.standard_normal((rows, cols), dtype=np.float32)
     spike = rng.integers(0, cols, size=rows)
     x[np.arange(rows), spike] += np.float32(30.0)
-    return Workload("config2_bf16_8192x4096", "bf16", f32_to_bf16_bits(x), MaskSpec(), seed,
+    return Workload(f"bf16_{rows}x{cols}_spike", "bf16", f32_to_bf16_bits(x), MaskSpec(), seed,
                     {"spike_col": spike})
 
 
-def config3(seed: int = 3, rows: int = 32768, cols: int = 512) -> Workload:
+def masked_rows(seed: int = 3, rows: int = 32768, cols: int = 512) -> Workload:
     rng = _rng(seed)
     x = rng.uniform(-40.0, 40.0, size=(rows, cols))
     valid = rng.integers(0, cols + 1, size=rows).astype(np.int32)  # both ends inclusive
-    return Workload("config3_f16_32768x512_validlen", "f16", f64_to_f16_bits(x),
+    return Workload(f"f16_{rows}x{cols}_validlen", "f16", f64_to_f16_bits(x),
                     MaskSpec("valid_len", valid_len=valid), seed)
 
 
-def config4(seed: int = 4, rows: int = 64, cols: int = 1 << 20) -> Workload:
+def long_rows(seed: int = 4, rows: int = 64, cols: int = 1 << 20) -> Workload:
     rng = _rng(seed)
     x = 4.0 * rng.standard_normal((rows, cols), dtype=np.float32)
     x += (50.0 * np.arange(cols, dtype=np.float64) / max(cols - 1, 1)).astype(np.float32)[None, :]
-    return Workload("config4_f32_64x1048576_ramp", "f32", x, MaskSpec(), seed)
+    return Workload(f"f32_{rows}x{cols}_ramp", "f32", x, MaskSpec(), seed)
 
 
-C5_SPECIALS = ("pos_inf_valid", "nan_valid", "nan_masked", "pos_inf_masked", "all_neg_inf")
+CAUSAL_SPECIALS = ("pos_inf_valid", "nan_valid", "nan_masked", "pos_inf_masked", "all_neg_inf")
 
 
-def config5_group(g: int, seed: int = 5, n: int = 2048, head_dim: int = 128,
-                  inject: bool = True):
-    """One (n x n) causal score block, rows g*n .. g*n+n-1 of config5.
+def causal_score_group(g: int, seed: int = 5, n: int = 2048, head_dim: int = 128,
+                       inject: bool = True):
+    """One (n x n) causal score block, rows g*n .. g*n+n-1 of causal_scores.
 
     Returns (bits uint16 [n, n], {special name: in-group row index}).
     """
@@ -200,7 +200,7 @@ def config5_group(g: int, seed: int = 5, n: int = 2048, head_dim: int = 128,
         srng = _rng(seed, g, 7)
         rows = srng.choice(n - 1, size=5, replace=False)  # row n-1 has no masked lane
         nan_bits = QNAN["bf16"] if g % 2 == 0 else NEG_SNAN["bf16"]
-        for name, i in zip(C5_SPECIALS, rows):
+        for name, i in zip(CAUSAL_SPECIALS, rows):
             i = int(i)
             specials[name] = i
             if name in ("pos_inf_valid", "nan_valid"):
@@ -214,23 +214,23 @@ def config5_group(g: int, seed: int = 5, n: int = 2048, head_dim: int = 128,
     return bits, specials
 
 
-def config5(seed: int = 5, groups: int = 256, n: int = 2048, head_dim: int = 128,
-            out: Optional[np.ndarray] = None) -> Workload:
+def causal_scores(seed: int = 5, groups: int = 256, n: int = 2048, head_dim: int = 128,
+                  out: Optional[np.ndarray] = None) -> Workload:
     rows = groups * n
     x = out if out is not None else np.empty((rows, n), dtype=np.uint16)
-    special = {name: [] for name in C5_SPECIALS}
+    special = {name: [] for name in CAUSAL_SPECIALS}
     for g in range(groups):
-        bits, sp = config5_group(g, seed, n, head_dim)
+        bits, sp = causal_score_group(g, seed, n, head_dim)
         x[g * n:(g + 1) * n] = bits
         for name, i in sp.items():
             special[name].append(g * n + i)
-    return Workload(f"config5_bf16_{groups}x{n}x{n}_causal", "bf16", x,
+    return Workload(f"bf16_{groups}x{n}x{n}_causal", "bf16", x,
                     MaskSpec("causal", causal_period=n), seed,
                     {k: np.asarray(v, dtype=np.int64) for k, v in special.items()})
 
 
-def config5_values(seed: int = 5, groups: int = 256, n: int = 2048, head_dim: int = 128) -> np.ndarray:
-    """Value vectors for config5's score groups (the attention workload that
+def causal_values(seed: int = 5, groups: int = 256, n: int = 2048, head_dim: int = 128) -> np.ndarray:
+    """Value vectors for causal_scores' groups (the attention workload that
     weights them by the scores' softmax): per group an [n, head_dim] matrix
     of seeded N(0, 1) values rounded to bf16. Returns uint16 bits
     [groups, n, head_dim]."""
@@ -241,7 +241,9 @@ def config5_values(seed: int = 5, groups: int = 256, n: int = 2048, head_dim: in
     return v
 
 
-CONFIGS = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}
+# by short name; the first is the benchmark's headline
+WORKLOADS = {"spiked": spiked_rows, "small": small_rows, "masked": masked_rows, "long": long_rows,
+             "causal": causal_scores}
 
 
 def random_rows(rows: int, cols: int, dtype: str, seed: int, scale: float = 4.0,
