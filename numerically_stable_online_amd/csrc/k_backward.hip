@@ -139,9 +139,11 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dot(BwdArgs a, int64_t chunk, 
   }
 }
 
-// pass 2: merge the row's partials (compensated, fixed order), write dx
+// pass 2: merge the row's nsum partials (compensated, fixed order; every
+// chunk's, or the one pair k_bwd_row_sum left), write dx
 template <int DT, int E, int VPT>
-__global__ __launch_bounds__(kThreads) void k_bwd_apply(BwdArgs a, int64_t chunk, int64_t nch, const float2* part) {
+__global__ __launch_bounds__(kThreads) void k_bwd_apply(BwdArgs a, int64_t chunk, int64_t nch, const float2* part,
+                                                        int64_t nsum) {
   constexpr int S = Fmt<DT>::S;
   constexpr int64_t kRound = (int64_t)kThreads * VPT * E;
   __shared__ RedScratch red;
@@ -153,8 +155,8 @@ __global__ __launch_bounds__(kThreads) void k_bwd_apply(BwdArgs a, int64_t chunk
     const int64_t j_hi = j_lo + chunk < a.cols ? j_lo + chunk : a.cols;
     const int64_t base = row * a.cols;
     float hi = 0.0f, lo = 0.0f;
-    for (int64_t i = tid; i < nch; i += kThreads) {
-      const float2 q = part[row * nch + i];
+    for (int64_t i = tid; i < nsum; i += kThreads) {
+      const float2 q = part[row * nsum + i];
       pair_add(hi, lo, q.x, q.y);
     }
     const float s = block_sum_pair<kWaves>(hi, lo, red);
@@ -183,6 +185,37 @@ __global__ __launch_bounds__(kThreads) void k_bwd_apply(BwdArgs a, int64_t chunk
         }
       }
     }
+  }
+}
+
+// Rows with many chunks sum their partials once, here, instead of once in
+// every chunk's workgroup of pass 2: the same per-thread order and the same
+// tree as k_bwd_apply, left as the (hi, lo) pair, which pass 2 then adds to
+// zeros exactly, so dx is bitwise the same. A thread's loads are issued
+// eight at a time, ahead of the dependent additions.
+__global__ __launch_bounds__(kThreads) void k_bwd_row_sum(const float2* part, int64_t rows, int64_t nch,
+                                                          float2* merged) {
+  constexpr int kBatch = 8;
+  __shared__ RedScratch red;
+  const int tid = threadIdx.x;
+  for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
+    const float2* rp = part + row * nch;
+    float hi = 0.0f, lo = 0.0f;
+    for (int64_t i0 = tid; i0 < nch; i0 += (int64_t)kBatch * kThreads) {
+      float2 q[kBatch];
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) {
+        const int64_t i = i0 + (int64_t)k * kThreads;
+        q[k] = i < nch ? rp[i] : make_float2(0.0f, 0.0f);
+      }
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) {
+        if (i0 + (int64_t)k * kThreads >= nch) break;
+        pair_add(hi, lo, q[k].x, q[k].y);
+      }
+    }
+    block_pair_reduce<kWaves>(hi, lo, red);
+    if (tid == 0) merged[row] = make_float2(hi, lo);
   }
 }
 
@@ -221,8 +254,18 @@ hipError_t launch_split_t(const BwdArgs& a, int64_t chunk, int64_t nch, float2* 
   hipLaunchKernelGGL((k_bwd_dot<DT, E, VPT>), dim3(grid), dim3(kThreads), 0, s, a, chunk, nch, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_bwd_apply<DT, E, VPT>), dim3(grid), dim3(kThreads), 0, s, a, chunk, nch,
-                     (const float2*)part);
+  if (nch > kRowMergeMinChunks) {
+    float2* const merged = part + a.rows * nch;
+    const unsigned rgrid = (unsigned)(a.rows < kMaxGrid ? a.rows : kMaxGrid);
+    hipLaunchKernelGGL(k_bwd_row_sum, dim3(rgrid), dim3(kThreads), 0, s, (const float2*)part, a.rows, nch, merged);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_bwd_apply<DT, E, VPT>), dim3(grid), dim3(kThreads), 0, s, a, chunk, nch,
+                       (const float2*)merged, (int64_t)1);
+  } else {
+    hipLaunchKernelGGL((k_bwd_apply<DT, E, VPT>), dim3(grid), dim3(kThreads), 0, s, a, chunk, nch,
+                       (const float2*)part, nch);
+  }
   return hipGetLastError();
 }
 

@@ -154,7 +154,7 @@ __global__ __launch_bounds__(kThreads) void k_stats(RowArgs a, int64_t chunk, in
 
 template <int DT, int E, bool KEEP, int EPI>
 __global__ __launch_bounds__(kThreads) void k_merge_normalize(RowArgs a, int64_t chunk, int64_t nch,
-                                                              const smx_stat* stats) {
+                                                              const smx_stat* stats, int64_t nsum) {
   constexpr int S = Fmt<DT>::S;
   constexpr bool ACC = DT == kF32;
   constexpr int VPT = vpt<DT, E>();
@@ -182,11 +182,12 @@ __global__ __launch_bounds__(kThreads) void k_merge_normalize(RowArgs a, int64_t
     const int64_t t = EPI == kEpiXent ? row_target(a.target, row, a.cols) : -1;
     const float xt_in = EPI == kEpiXent ? a.xt[row] : -kInf;
 
-    // merge this row's summaries
+    // merge this row's nsum summaries (every chunk's, or the one k_row_merge
+    // left)
     float m = -kInf, l = 0.0f;
     bool bad = false;
-    for (int64_t i = tid; i < nch; i += kThreads) {
-      const smx_stat s = stats[row * nch + i];
+    for (int64_t i = tid; i < nsum; i += kThreads) {
+      const smx_stat s = stats[row * nsum + i];
       if (s.m != s.m || s.l != s.l) {
         bad = true;
       } else {
@@ -291,6 +292,47 @@ __global__ __launch_bounds__(kThreads) void k_merge_normalize(RowArgs a, int64_t
   }
 }
 
+// Rows with many chunks merge their summaries once, here, instead of once in
+// every chunk's workgroup of the normalize pass (whose merge reads would grow
+// as chunks squared). Each thread folds the same summaries in the same order
+// and the same tree combines the threads as in k_merge_normalize, so (M, L) is
+// bitwise the one the normalize pass would form; folded again there, (M, L)
+// merged into the empty (-inf, 0) comes out unchanged. The loads of a thread
+// are issued eight at a time, ahead of the dependent folds.
+__global__ __launch_bounds__(kThreads) void k_row_merge(const smx_stat* stats, int64_t rows, int64_t nch,
+                                                        smx_stat* merged) {
+  constexpr int kBatch = 8;
+  __shared__ RedScratch red;
+  const int tid = threadIdx.x;
+  for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
+    const smx_stat* rs = stats + row * nch;
+    float m = -kInf, l = 0.0f;
+    bool bad = false;
+    for (int64_t i0 = tid; i0 < nch; i0 += (int64_t)kBatch * kThreads) {
+      smx_stat q[kBatch];
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) {
+        const int64_t i = i0 + (int64_t)k * kThreads;
+        q[k] = i < nch ? rs[i] : smx_stat{-kInf, 0.0f};
+      }
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) {
+        if (i0 + (int64_t)k * kThreads >= nch) break;
+        if (q[k].m != q[k].m || q[k].l != q[k].l) {
+          bad = true;
+        } else {
+          merge_ml(m, l, q[k].m, q[k].l);
+        }
+      }
+    }
+    const bool poisoned = block_merge_flagged<kWaves>(m, l, bad, red);
+    if (tid == 0) {
+      const float nan = __builtin_nanf("");
+      merged[row] = poisoned ? smx_stat{nan, nan} : smx_stat{m, l};
+    }
+  }
+}
+
 constexpr int64_t kMaxGrid = 1 << 20;
 
 template <int DT, int E>
@@ -315,28 +357,33 @@ hipError_t launch_stats_t(const RowArgs& a, bool xent, int64_t chunk, int64_t nc
 }
 
 template <int DT, int E, int EPI>
-hipError_t launch_mn_t(const RowArgs& a, int64_t chunk, int64_t nch, const smx_stat* stats, hipStream_t s) {
+hipError_t launch_mn_t(const RowArgs& a, int64_t chunk, int64_t nch, const smx_stat* stats, int64_t nsum,
+                       hipStream_t s) {
   const int64_t total = a.rows * nch;
   const unsigned grid = (unsigned)(total < kMaxGrid ? total : kMaxGrid);
   if (a.mask.kind == kMaskKeep) {
-    hipLaunchKernelGGL((k_merge_normalize<DT, E, true, EPI>), dim3(grid), dim3(kThreads), 0, s, a, chunk, nch, stats);
+    hipLaunchKernelGGL((k_merge_normalize<DT, E, true, EPI>), dim3(grid), dim3(kThreads), 0, s, a, chunk, nch, stats,
+                       nsum);
   } else {
-    hipLaunchKernelGGL((k_merge_normalize<DT, E, false, EPI>), dim3(grid), dim3(kThreads), 0, s, a, chunk, nch, stats);
+    hipLaunchKernelGGL((k_merge_normalize<DT, E, false, EPI>), dim3(grid), dim3(kThreads), 0, s, a, chunk, nch, stats,
+                       nsum);
   }
   return hipGetLastError();
 }
 
 template <int EPI>
 hipError_t launch_mn_epi(const RowArgs& a, int dtype, bool vec, int64_t chunk, int64_t nch, const smx_stat* stats,
-                         hipStream_t s) {
+                         int64_t nsum, hipStream_t s) {
   switch (dtype) {
     case kF32:
-      return vec ? launch_mn_t<kF32, 4, EPI>(a, chunk, nch, stats, s) : launch_mn_t<kF32, 1, EPI>(a, chunk, nch, stats, s);
+      return vec ? launch_mn_t<kF32, 4, EPI>(a, chunk, nch, stats, nsum, s)
+                 : launch_mn_t<kF32, 1, EPI>(a, chunk, nch, stats, nsum, s);
     case kF16:
-      return vec ? launch_mn_t<kF16, 8, EPI>(a, chunk, nch, stats, s) : launch_mn_t<kF16, 1, EPI>(a, chunk, nch, stats, s);
+      return vec ? launch_mn_t<kF16, 8, EPI>(a, chunk, nch, stats, nsum, s)
+                 : launch_mn_t<kF16, 1, EPI>(a, chunk, nch, stats, nsum, s);
     default:
-      return vec ? launch_mn_t<kBF16, 8, EPI>(a, chunk, nch, stats, s)
-                 : launch_mn_t<kBF16, 1, EPI>(a, chunk, nch, stats, s);
+      return vec ? launch_mn_t<kBF16, 8, EPI>(a, chunk, nch, stats, nsum, s)
+                 : launch_mn_t<kBF16, 1, EPI>(a, chunk, nch, stats, nsum, s);
   }
 }
 
@@ -363,10 +410,16 @@ hipError_t launch_stats(const RowArgs& a, int dtype, bool vec, bool xent, int64_
 }
 
 hipError_t launch_merge_normalize(const RowArgs& a, int dtype, bool vec, int epi, int64_t chunk, int64_t nch,
-                                  const smx_stat* stats, hipStream_t s) {
-  if (epi == kEpiSoftmax) return launch_mn_epi<kEpiSoftmax>(a, dtype, vec, chunk, nch, stats, s);
-  if (epi == kEpiLogSoftmax) return launch_mn_epi<kEpiLogSoftmax>(a, dtype, vec, chunk, nch, stats, s);
-  return launch_mn_epi<kEpiXent>(a, dtype, vec, chunk, nch, stats, s);
+                                  const smx_stat* stats, int64_t nsum, hipStream_t s) {
+  if (epi == kEpiSoftmax) return launch_mn_epi<kEpiSoftmax>(a, dtype, vec, chunk, nch, stats, nsum, s);
+  if (epi == kEpiLogSoftmax) return launch_mn_epi<kEpiLogSoftmax>(a, dtype, vec, chunk, nch, stats, nsum, s);
+  return launch_mn_epi<kEpiXent>(a, dtype, vec, chunk, nch, stats, nsum, s);
+}
+
+hipError_t launch_row_merge(const smx_stat* stats, int64_t rows, int64_t nch, smx_stat* merged, hipStream_t s) {
+  const unsigned grid = (unsigned)(rows < kMaxGrid ? rows : kMaxGrid);
+  hipLaunchKernelGGL(k_row_merge, dim3(grid), dim3(kThreads), 0, s, stats, rows, nch, merged);
+  return hipGetLastError();
 }
 
 }  // namespace smx

@@ -114,15 +114,24 @@ int run_split(const Call& c0, int64_t chunk, int epi, hipStream_t stream) {
   const int64_t e = vec_elems(c.dtype);
   const bool vec = c.vec && chunk % e == 0;
   const int64_t nch = (c.a.cols + chunk - 1) / chunk;
-  // workspace: the chunk summaries, then (cross-entropy) one target logit per row
+  // workspace: the chunk summaries, then (many chunks per row) one merged
+  // summary per row, then (cross-entropy) one target logit per row
+  const bool row_merge = nch > kRowMergeMinChunks;
   const size_t stat_bytes = (size_t)(c.a.rows * nch) * sizeof(smx_stat);
-  const size_t bytes = stat_bytes + (epi == kEpiXent ? (size_t)c.a.rows * sizeof(float) : 0);
+  const size_t merged_bytes = row_merge ? (size_t)c.a.rows * sizeof(smx_stat) : 0;
+  const size_t bytes = stat_bytes + merged_bytes + (epi == kEpiXent ? (size_t)c.a.rows * sizeof(float) : 0);
   void* ws = nullptr;
   hipError_t err = hipMallocAsync(&ws, bytes, stream);
   if (err != hipSuccess) return hip_fail(err, "hipMallocAsync of the summary workspace");
-  if (epi == kEpiXent) c.a.xt = (float*)((char*)ws + stat_bytes);
-  err = launch_stats(c.a, c.dtype, vec, epi == kEpiXent, chunk, nch, (smx_stat*)ws, stream);
-  if (err == hipSuccess) err = launch_merge_normalize(c.a, c.dtype, vec, epi, chunk, nch, (const smx_stat*)ws, stream);
+  smx_stat* const stats = (smx_stat*)ws;
+  smx_stat* const merged = (smx_stat*)((char*)ws + stat_bytes);
+  if (epi == kEpiXent) c.a.xt = (float*)((char*)ws + stat_bytes + merged_bytes);
+  err = launch_stats(c.a, c.dtype, vec, epi == kEpiXent, chunk, nch, stats, stream);
+  if (err == hipSuccess && row_merge) err = launch_row_merge(stats, c.a.rows, nch, merged, stream);
+  if (err == hipSuccess) {
+    err = row_merge ? launch_merge_normalize(c.a, c.dtype, vec, epi, chunk, nch, merged, 1, stream)
+                    : launch_merge_normalize(c.a, c.dtype, vec, epi, chunk, nch, stats, nch, stream);
+  }
   const hipError_t ferr = hipFreeAsync(ws, stream);
   if (err != hipSuccess) return hip_fail(err, "split-path launch");
   if (ferr != hipSuccess) return hip_fail(ferr, "hipFreeAsync of the summary workspace");
@@ -220,7 +229,8 @@ int softmax_merge_normalize(const void* x, void* y, int64_t rows, int64_t cols, 
   if (rows > 0 && nch > 0 && stats == nullptr) return fail(SMX_EINVAL, "stats is NULL");
   if (rows == 0 || cols == 0) return ok();
   const bool vec = c.vec && chunk_cols % vec_elems(c.dtype) == 0;
-  hipError_t err = launch_merge_normalize(c.a, c.dtype, vec, kEpiSoftmax, chunk_cols, nch, stats, (hipStream_t)stream);
+  hipError_t err = launch_merge_normalize(c.a, c.dtype, vec, kEpiSoftmax, chunk_cols, nch, stats, nch,
+                                         (hipStream_t)stream);
   if (err != hipSuccess) return hip_fail(err, "merge/normalize launch");
   return ok();
 }
@@ -331,7 +341,8 @@ int softmax_backward_rows_path(const void* p, const void* g, void* dx, int64_t r
   const bool cvec = vec && chunk % e == 0;
   const int64_t nch = (cols + chunk - 1) / chunk;
   void* ws = nullptr;
-  err = hipMallocAsync(&ws, (size_t)(rows * nch) * sizeof(float2), st);
+  const size_t part_count = (size_t)(rows * nch) + (nch > kRowMergeMinChunks ? (size_t)rows : 0);
+  err = hipMallocAsync(&ws, part_count * sizeof(float2), st);
   if (err != hipSuccess) return hip_fail(err, "hipMallocAsync of the partial-dot workspace");
   err = launch_bwd_split((const char*)p, (const char*)g, (char*)dx, rows, cols, dt, cvec, chunk, nch, (float2*)ws, st);
   const hipError_t ferr = hipFreeAsync(ws, st);

@@ -67,14 +67,24 @@ int64_t split_round_cols(int dtype, bool vec);
 // written to a.xt
 hipError_t launch_stats(const RowArgs& a, int dtype, bool vec, bool xent, int64_t chunk_cols, int64_t n_chunks,
                         smx_stat* stats, hipStream_t stream);
+// stats holds n_summaries summaries per row: every chunk's (n_chunks), or the
+// single one launch_row_merge left
 hipError_t launch_merge_normalize(const RowArgs& a, int dtype, bool vec, int epi, int64_t chunk_cols,
-                                  int64_t n_chunks, const smx_stat* stats, hipStream_t stream);
+                                  int64_t n_chunks, const smx_stat* stats, int64_t n_summaries, hipStream_t stream);
+// each row's n_chunks summaries merged into merged[row], bitwise as the
+// normalize pass would merge them
+hipError_t launch_row_merge(const smx_stat* stats, int64_t rows, int64_t n_chunks, smx_stat* merged,
+                            hipStream_t stream);
+// more chunks per row than this: the summaries are merged once per row first
+constexpr int64_t kRowMergeMinChunks = 1024;
 
 // --- softmax backward (k_backward.hip) ---
 int64_t bwd_wave_max_cols(int dtype, bool vec);
 int64_t bwd_block_max_cols(int dtype, bool vec);
 hipError_t launch_bwd_rows(const char* p, const char* g, char* dx, int64_t rows, int64_t cols, int dtype,
                            bool vec, bool wave, hipStream_t stream);
+// partials holds rows * n_chunks partial dot products, then (when n_chunks
+// exceeds kRowMergeMinChunks) room for one merged pair per row
 hipError_t launch_bwd_split(const char* p, const char* g, char* dx, int64_t rows, int64_t cols, int dtype, bool vec,
                             int64_t chunk, int64_t n_chunks, float2* partials, hipStream_t stream);
 

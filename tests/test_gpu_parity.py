@@ -162,6 +162,41 @@ def test_very_long_rows_split():
     banner(f"very long rows: {r}")
 
 
+def test_row_merge_matches_direct_merge():
+    """Beyond 1024 chunks per row the split path merges each row's summaries
+    once before normalizing. Its output is bitwise the one the normalize pass
+    gives when each of its workgroups merges every summary itself (the
+    public softmax_row_stats + softmax_merge_normalize pair), and it meets
+    the oracle; log-softmax, cross-entropy and the backward take the same
+    two-level merge and meet the oracle too. Rows: full, a valid length
+    ending inside a chunk, empty, and NaN in a valid lane."""
+    rows, cols, chunk = 4, 1 << 22, 2048  # 2048 chunks per row
+    x = W.random_rows(rows, cols, "f32", seed=91, scale=5.0)
+    x[3, 777_777] = np.float32("nan")
+    vl = np.array([cols, cols - 1000, 0, cols], dtype=np.int32)
+    mask = W.MaskSpec("valid_len", valid_len=vl)
+    xd = to_device(x, "f32")
+    kw = mask_kwargs(mask)
+    banner("row merge: softmax")
+    y_two = smx.softmax_rows(xd, path="split", chunk_cols=chunk, **kw)
+    st = smx.softmax_row_stats(xd, chunk, **kw)
+    y_direct = smx.softmax_merge_normalize(xd, st, chunk, **kw)
+    torch.cuda.synchronize()
+    assert _same_bits(y_two, y_direct)
+    check_full(x, "f32", mask, to_host(y_two, "f32"), "row merge softmax")
+    banner("row merge: log-softmax")
+    y, lse = run_log(x, "f32", mask, path="split", chunk_cols=chunk)
+    check_log_full(x, "f32", mask, y, lse, "row merge log-softmax")
+    banner("row merge: cross-entropy")
+    t = xent_targets(rows, cols, seed=93)
+    loss, dx = run_xent(x, "f32", t, mask, path="split", chunk_cols=chunk)
+    check_xent_full(x, "f32", t, mask, loss, dx, "row merge cross-entropy")
+    banner("row merge: backward")
+    p_raw, g_raw = bwd_inputs(x[:2], "f32", W.MaskSpec("valid_len", valid_len=vl[:2]), seed=92)
+    dxb = run_bwd(p_raw, g_raw, "f32", path="split", chunk_cols=chunk)
+    check_bwd_full(p_raw, g_raw, "f32", dxb, "row merge backward")
+
+
 # ---------------------------------------------------------------------------
 # Shapes, alignments, masks and paths
 # ---------------------------------------------------------------------------
