@@ -115,8 +115,9 @@ typedef enum {
  *   valid_len_or_mask : host pointer to a mask descriptor, or NULL.
  *   stream: hipStream_t.
  * Long rows go through the split path, which takes its summary workspace
- * (rows * ceil(cols / chunk) * 8 bytes) with a stream-ordered allocation and
- * frees it on the same stream. */
+ * (rows * ceil(cols / chunk) * 8 bytes, plus 8 bytes per row when a row has
+ * more than 1024 chunks and its summaries are merged once per row first)
+ * with a stream-ordered allocation and frees it on the same stream. */
 SMX_API int softmax_rows(const void* x, void* y, int64_t rows, int64_t cols,
                  smx_dtype dtype, const smx_mask* valid_len_or_mask,
                  void* stream);
@@ -148,7 +149,10 @@ SMX_API int softmax_row_stats(const void* x, int64_t rows, int64_t cols,
  * Any (NaN, NaN) summary makes a NaN row; all-empty summaries a zero row.
  *   stats: device [rows][n_chunks], as written by softmax_row_stats or by the
  *          caller (e.g. summaries exchanged between devices);
- *   n_chunks must equal ceil(cols / chunk_cols). */
+ *   n_chunks must equal ceil(cols / chunk_cols).
+ * Every chunk's workgroup merges all n_chunks summaries of its row itself
+ * (no workspace), so its summary reads grow as n_chunks squared: prefer
+ * chunks large enough to keep n_chunks to about a thousand or fewer. */
 SMX_API int softmax_merge_normalize(const void* x, void* y, int64_t rows, int64_t cols,
                             smx_dtype dtype, const smx_mask* valid_len_or_mask,
                             int64_t chunk_cols, const smx_stat* stats,
@@ -238,7 +242,8 @@ SMX_API int softmax_weighted_rows(const void* s, const void* v, void* out, int64
  * may equal p or g exactly (in place); partial overlap is SMX_EINVAL. A NaN
  * in a row's p or g makes that row's dx the canonical NaN. Long rows take two
  * passes (per-chunk partial dot products in a stream-ordered workspace of
- * rows * ceil(cols / chunk) * 8 bytes). */
+ * rows * ceil(cols / chunk) * 8 bytes, plus 8 bytes per row when a row has
+ * more than 1024 chunks and its partials are summed once per row first). */
 SMX_API int softmax_backward_rows(const void* p, const void* g, void* dx, int64_t rows, int64_t cols,
                                   smx_dtype dtype, void* stream);
 
