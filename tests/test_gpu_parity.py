@@ -197,6 +197,49 @@ def test_row_merge_matches_direct_merge():
     check_bwd_full(p_raw, g_raw, "f32", dxb, "row merge backward")
 
 
+def test_beyond_2_31_elements():
+    """Tensors of more than 2^31 elements, so element offsets pass 2^31 on
+    every path (64-bit addressing): 2^20 + 512 rows of 2048 bf16 lanes
+    through the wave, LDS and split paths, and the weighted sums over 520
+    groups of 2048 x 2048 causal scores. Rows at both ends and on each side
+    of element 2^31 are checked against the oracle."""
+    rows, cols = (1 << 20) + 512, 2048
+    g = torch.Generator(device="cuda")
+    g.manual_seed(123)
+    x = torch.empty(rows, cols, dtype=torch.bfloat16, device="cuda")
+    for r in range(0, rows, 1 << 18):
+        x[r:r + (1 << 18)] = (6.0 * torch.randn(min(1 << 18, rows - r), cols, device="cuda", generator=g)).to(torch.bfloat16)
+    edge = (1 << 31) // cols
+    sample = [0, 1, rows // 2, edge - 1, edge, edge + 1, rows - 2, rows - 1]
+    xs = to_host(x[sample].contiguous(), "bf16")
+    p, cls, st = oracle.softmax_rows(xs, "bf16", W.MaskSpec("none"))
+    for path, chunk in (("wave", 0), ("lds", 0), ("split", 512)):
+        banner(f"2^31+: softmax {path}")
+        y = smx.softmax_rows(x, path=path, chunk_cols=chunk)
+        torch.cuda.synchronize()
+        check(to_host(y[sample].contiguous(), "bf16"), "bf16", p, cls, st, f"2^31+ {path}")
+        del y
+    del x
+    groups, n, d = 520, 2048, 128
+    banner("2^31+: weighted sums")
+    sc = torch.empty(groups * n, n, dtype=torch.bfloat16, device="cuda")
+    for gi in range(0, groups, 64):
+        k = min(64, groups - gi)
+        sc[gi * n:(gi + k) * n] = (3.0 * torch.randn(k * n, n, device="cuda", generator=g)).to(torch.bfloat16)
+    v = torch.randn(groups, n, d, device="cuda", generator=g).to(torch.bfloat16)
+    out = smx.softmax_weighted_rows(sc, v, causal_period=n)
+    torch.cuda.synchronize()
+    mask = W.MaskSpec("causal", causal_period=n)
+    for gi in (0, edge // n, edge // n + 1, groups - 1):
+        s_g = to_host(sc[gi * n:(gi + 1) * n].contiguous(), "bf16")
+        v_g = to_host(v[gi:gi + 1].contiguous().view(n, d), "bf16").reshape(1, n, d)
+        rows_g = [0, 1, 777, n - 1]
+        for r in rows_g:
+            ref, st_w, scale = weighted_reference(s_g, v_g, "bf16", n, mask, r, r + 1)
+            got = to_host(out[gi * n + r:gi * n + r + 1].contiguous(), "bf16")
+            check_weighted(got, "bf16", ref, st_w, scale, f"2^31+ weighted group {gi} row {r}")
+
+
 # ---------------------------------------------------------------------------
 # Shapes, alignments, masks and paths
 # ---------------------------------------------------------------------------
