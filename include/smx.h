@@ -223,7 +223,9 @@ SMX_API int softmax_cross_entropy_rows_path(const void* x, const int32_t* target
  *   d  : 32, 64 or 128; rows must be a multiple of rows_per_group.
  * The running state is fp32. The weights p enter the matrix cores as a
  * high and a low 16-bit part (about 16 significant bits); the values enter
- * exactly; products accumulate in fp32.
+ * exactly; products accumulate in fp32. Groups of at most 8 rows take the
+ * key split of softmax_weighted_states and softmax_weighted_merge instead
+ * (fp32 on the vector ALUs), with a stream-ordered workspace.
  * Policy: a poisoned row (+inf/NaN in a valid lane) gives the canonical NaN
  * in every component; an empty or fully masked row gives zeros. SMX_F32,
  * other widths, misalignment and overlap are SMX_EINVAL; rows = 0 is a
@@ -231,6 +233,42 @@ SMX_API int softmax_cross_entropy_rows_path(const void* x, const int32_t* target
 SMX_API int softmax_weighted_rows(const void* s, const void* v, void* out, int64_t rows, int64_t cols, int64_t d,
                                   int64_t rows_per_group, smx_dtype dtype, const smx_mask* valid_len_or_mask,
                                   void* stream);
+
+/* softmax_weighted_states — the weighted sums split along the keys: one
+ * online state per (row, chunk of keys) ("Online stable softmax", section on
+ * the weighted numerator: a block carries (m, l, o) with
+ * o = sum_j exp(s_j - m) V_j; "Softmax numerics architecture", tiled
+ * attention, where blocks of keys are visited in turn).
+ *   s, v, rows, cols, d, rows_per_group, dtype, mask: as softmax_weighted_rows;
+ *   chunk_cols: in [1, 2048]; chunk c covers keys [c*chunk_cols,
+ *               min((c+1)*chunk_cols, cols)), n_chunks = ceil(cols / chunk_cols);
+ *   ml: device float [rows][n_chunks][2]: m, the chunk's maximum over valid
+ *       finite scores (exact), and l = sum exp(s_j - m) over them;
+ *   o:  device float [rows][n_chunks][d]: sum exp(s_j - m) v[r / rows_per_group, j, k].
+ * An empty chunk is m = -inf, l = 0, o = 0; a chunk with +inf or NaN in a
+ * valid lane is NaN in m, l and o. The state is fp32 and computed on the
+ * vector ALUs (this split serves groups of few rows and many keys). ml and o
+ * must overlap neither each other nor s or v. Asynchronous on stream. */
+SMX_API int softmax_weighted_states(const void* s, const void* v, int64_t rows, int64_t cols, int64_t d,
+                                    int64_t rows_per_group, smx_dtype dtype, const smx_mask* valid_len_or_mask,
+                                    int64_t chunk_cols, float* ml, float* o, void* stream);
+
+/* softmax_weighted_merge — folds each row's n_chunks states by the merge
+ * rule ("Online stable softmax", derive the update for two blocks and the
+ * weighted numerator: M = max m_c; l and o take the same factor
+ * exp(m_c - M), exactly 1 on the side holding the maximum, so an empty state
+ * is an identity) and writes out[r, k] = O_k / L in dtype (SMX_F16 or
+ * SMX_BF16), rounded to nearest even.
+ *   ml, o: as softmax_weighted_states wrote them (or any states of that
+ *          layout, e.g. gathered from several devices);
+ *   out:   device [rows, d]; n_chunks <= 16384.
+ * A NaN state (or m = +inf) makes the row the canonical NaN; a row whose
+ * states are all empty is +0.0. Chunks are folded in order, so results are
+ * deterministic. softmax_weighted_rows takes this split (states in a
+ * stream-ordered workspace of rows * n_chunks * (d + 2) * 4 bytes, then this
+ * merge) when rows_per_group <= 8. */
+SMX_API int softmax_weighted_merge(const float* ml, const float* o, int64_t rows, int64_t n_chunks, int64_t d,
+                                   smx_dtype dtype, void* out, void* stream);
 
 /* softmax_backward_rows — the vector-Jacobian product of the softmax
  * ("Softmax numerics architecture", section on the Jacobian and the backward

@@ -90,6 +90,10 @@ def lib() -> C.CDLL:
         L.softmax_backward_rows_path.restype = i32
         L.softmax_weighted_rows.argtypes = [vp, vp, vp, i64, i64, i64, i64, i32, mp, vp]
         L.softmax_weighted_rows.restype = i32
+        L.softmax_weighted_states.argtypes = [vp, vp, i64, i64, i64, i64, i32, mp, i64, vp, vp, vp]
+        L.softmax_weighted_states.restype = i32
+        L.softmax_weighted_merge.argtypes = [vp, vp, i64, i64, i64, i32, vp, vp]
+        L.softmax_weighted_merge.restype = i32
         L.softmax_default_chunk_cols.argtypes = [i64, i64, i32]
         L.softmax_default_chunk_cols.restype = i64
         L.smx_last_error.argtypes = []
@@ -272,6 +276,55 @@ def softmax_weighted_rows(s: torch.Tensor, v: torch.Tensor, out: Optional[torch.
                                      _dtype_code(s), _mask_arg(m), _stream_handle(stream, s.device))
     _check(rc)
     return o
+
+
+def softmax_weighted_states(s: torch.Tensor, v: torch.Tensor, chunk_cols: int, ml: Optional[torch.Tensor] = None,
+                            o: Optional[torch.Tensor] = None, *, valid_len=None, causal_period=None,
+                            causal_offset: int = 0, keep=None, stream=None):
+    """Per-(row, key chunk) states of softmax(s) @ v: ml float32 [rows, n_chunks, 2] (the chunk
+    maximum m and l = sum exp(s - m)) and o float32 [rows, n_chunks, d] (sum exp(s - m) v).
+    Returns (ml, o)."""
+    rows, cols = _rows_cols(s)
+    if v.dim() != 3 or v.shape[1] != cols or v.dtype != s.dtype or not v.is_contiguous():
+        raise ValueError("v must be a contiguous [groups, cols, d] tensor of s's dtype")
+    _on(v, s.device, "v")
+    groups, _, d = v.shape
+    if groups == 0 or rows % groups != 0:
+        raise ValueError("rows must be a multiple of the number of value matrices")
+    nch = -(-cols // chunk_cols) if chunk_cols > 0 else 0
+    ml = torch.empty((rows, nch, 2), dtype=torch.float32, device=s.device) if ml is None else ml
+    o = torch.empty((rows, nch, d), dtype=torch.float32, device=s.device) if o is None else o
+    for t, shape, name in ((ml, (rows, nch, 2), "ml"), (o, (rows, nch, d), "o")):
+        if t.shape != shape or t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous float32 tensor {list(shape)}")
+        _on(t, s.device, name)
+    m, keepalive = make_mask(rows, cols, valid_len, causal_period, causal_offset, keep, s.device)
+    rc = lib().softmax_weighted_states(s.data_ptr(), v.data_ptr(), rows, cols, d, rows // groups, _dtype_code(s),
+                                       _mask_arg(m), int(chunk_cols), ml.data_ptr(), o.data_ptr(),
+                                       _stream_handle(stream, s.device))
+    _check(rc)
+    return ml, o
+
+
+def softmax_weighted_merge(ml: torch.Tensor, o: torch.Tensor, dtype: torch.dtype, out: Optional[torch.Tensor] = None,
+                           *, stream=None) -> torch.Tensor:
+    """Fold each row's chunk states (as softmax_weighted_states writes them) and write
+    O / L in dtype (torch.float16 or torch.bfloat16): out [rows, d]."""
+    if ml.dim() != 3 or ml.shape[2] != 2 or ml.dtype != torch.float32 or not ml.is_contiguous():
+        raise ValueError("ml must be a contiguous float32 tensor [rows, n_chunks, 2]")
+    rows, nch, _ = ml.shape
+    if o.dim() != 3 or o.shape[:2] != (rows, nch) or o.dtype != torch.float32 or not o.is_contiguous():
+        raise ValueError("o must be a contiguous float32 tensor [rows, n_chunks, d]")
+    _on(o, ml.device, "o")
+    d = o.shape[2]
+    y = torch.empty((rows, d), dtype=dtype, device=ml.device) if out is None else out
+    if y.shape != (rows, d) or y.dtype != dtype or not y.is_contiguous():
+        raise ValueError("out must be a contiguous [rows, d] tensor of the given dtype")
+    _on(y, ml.device, "out")
+    rc = lib().softmax_weighted_merge(ml.data_ptr(), o.data_ptr(), rows, nch, d, DTYPE[dtype], y.data_ptr(),
+                                      _stream_handle(stream, ml.device))
+    _check(rc)
+    return y
 
 
 def softmax_backward_rows(p: torch.Tensor, g: torch.Tensor, out: Optional[torch.Tensor] = None, *,

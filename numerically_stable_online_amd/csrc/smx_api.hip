@@ -169,6 +169,47 @@ int run_rows(const Call& c, smx_path path, int64_t chunk_cols, int epi, hipStrea
   return ok();
 }
 
+// whether [a, a + na) and [b, b + nb) share a byte
+bool overlaps(const void* a, uintptr_t na, const void* b, uintptr_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return na > 0 && nb > 0 && x < y + nb && y < x + na;
+}
+
+// The checks shared by the weighted-sum calls: scores s [rows, cols] under
+// the mask, values v [rows / rows_per_group, cols, d], 16-bit, aligned.
+int check_weighted(const char* name, const void* s, const void* v, int64_t rows, int64_t cols, int64_t d,
+                   int64_t rows_per_group, smx_dtype dtype, const smx_mask* mask, Call& c) {
+  if (int rc = check_common(s, nullptr, rows, cols, (int)dtype, mask, false, c)) return rc;
+  if (dtype == SMX_F32) return fail(SMX_EINVAL, "%s takes SMX_F16 or SMX_BF16", name);
+  if (!pv_supported_d(d)) return fail(SMX_EINVAL, "d = %lld: the value width must be 32, 64 or 128", (long long)d);
+  if (rows_per_group <= 0 || rows % rows_per_group != 0)
+    return fail(SMX_EINVAL, "rows (%lld) must be a positive multiple of rows_per_group (%lld)", (long long)rows,
+                (long long)rows_per_group);
+  if (cols % 8 != 0) return fail(SMX_EINVAL, "cols (%lld) must be a multiple of 8", (long long)cols);
+  if (cols > ((int64_t)1 << 30))
+    return fail(SMX_EINVAL, "cols (%lld) exceeds 2^30, the longest row the weighted sums take", (long long)cols);
+  const int64_t groups = rows / rows_per_group;
+  if (cols > 0 && groups > INT64_MAX / cols / d / 2) return fail(SMX_EINVAL, "the size of v overflows int64");
+  if (rows > INT64_MAX / d / 2) return fail(SMX_EINVAL, "the size of out overflows int64");
+  if (rows > 0 && cols > 0 && v == nullptr) return fail(SMX_EINVAL, "v must not be NULL");
+  if ((uintptr_t)s % 16 != 0 || (uintptr_t)v % 16 != 0) return fail(SMX_EINVAL, "s and v must be 16-byte aligned");
+  if (c.a.mask.kind == SMX_MASK_KEEP_BYTES && (uintptr_t)c.a.mask.keep % 8 != 0)
+    return fail(SMX_EINVAL, "keep must be 8-byte aligned");
+  return SMX_OK;
+}
+
+// groups of at most this many score rows take the key-split path in
+// softmax_weighted_rows (the matrix-core tiles hold 128 rows)
+constexpr int64_t kWeightedSplitMaxRows = 8;
+
+// the key chunk of that path: 512, halved (down to 128) while the grid has
+// fewer than 2048 workgroups
+int64_t weighted_split_chunk(int64_t groups, int64_t cols) {
+  int64_t chunk = 512;
+  while (chunk > 128 && groups * ((cols + chunk - 1) / chunk) < 2048) chunk /= 2;
+  return chunk;
+}
+
 }  // namespace
 }  // namespace smx
 
@@ -359,32 +400,83 @@ int softmax_backward_rows(const void* p, const void* g, void* dx, int64_t rows, 
 int softmax_weighted_rows(const void* s, const void* v, void* out, int64_t rows, int64_t cols, int64_t d,
                           int64_t rows_per_group, smx_dtype dtype, const smx_mask* mask, void* stream) {
   Call c;
-  if (int rc = check_common(s, nullptr, rows, cols, (int)dtype, mask, false, c)) return rc;
-  if (dtype == SMX_F32)
-    return fail(SMX_EINVAL, "softmax_weighted_rows takes SMX_F16 or SMX_BF16 (16-bit matrix-core operands)");
-  if (!pv_supported_d(d)) return fail(SMX_EINVAL, "d = %lld: the value width must be 32, 64 or 128", (long long)d);
-  if (rows_per_group <= 0 || rows % rows_per_group != 0)
-    return fail(SMX_EINVAL, "rows (%lld) must be a positive multiple of rows_per_group (%lld)", (long long)rows,
-                (long long)rows_per_group);
-  if (cols % 8 != 0) return fail(SMX_EINVAL, "cols (%lld) must be a multiple of 8", (long long)cols);
-  if (cols > ((int64_t)1 << 30))
-    return fail(SMX_EINVAL, "cols (%lld) exceeds 2^30, the longest row the weighted sums take", (long long)cols);
+  if (int rc = check_weighted("softmax_weighted_rows", s, v, rows, cols, d, rows_per_group, dtype, mask, c)) return rc;
   if (rows == 0) return ok();
+  if (out == nullptr) return fail(SMX_EINVAL, "out must not be NULL");
+  if ((uintptr_t)out % 8 != 0) return fail(SMX_EINVAL, "out must be 8-byte aligned");
   const int64_t groups = rows / rows_per_group;
-  if (cols > 0 && groups > INT64_MAX / cols / d / 2) return fail(SMX_EINVAL, "the size of v overflows int64");
-  if (rows > INT64_MAX / d / 2) return fail(SMX_EINVAL, "the size of out overflows int64");
-  if (out == nullptr || (cols > 0 && v == nullptr)) return fail(SMX_EINVAL, "v and out must not be NULL");
-  if ((uintptr_t)s % 16 != 0 || (uintptr_t)v % 16 != 0 || (uintptr_t)out % 8 != 0)
-    return fail(SMX_EINVAL, "s and v must be 16-byte aligned and out 8-byte aligned");
-  if (c.a.mask.kind == SMX_MASK_KEEP_BYTES && (uintptr_t)c.a.mask.keep % 8 != 0)
-    return fail(SMX_EINVAL, "keep must be 8-byte aligned");
-  const uintptr_t oa = (uintptr_t)out, ob = (uintptr_t)(rows * d * 2);
-  const uintptr_t sa = (uintptr_t)s, sb = (uintptr_t)(rows * cols * 2);
-  const uintptr_t va = (uintptr_t)v, vb = (uintptr_t)(groups * cols * d * 2);
-  if ((sb > 0 && oa < sa + sb && sa < oa + ob) || (vb > 0 && oa < va + vb && va < oa + ob))
+  const uintptr_t ob = (uintptr_t)(rows * d * 2);
+  if (overlaps(out, ob, s, (uintptr_t)(rows * cols * 2)) || overlaps(out, ob, v, (uintptr_t)(groups * cols * d * 2)))
     return fail(SMX_EINVAL, "out overlaps s or v");
-  const hipError_t err = launch_pv((const char*)s, (const char*)v, (char*)out, rows, cols, d, rows_per_group,
-                                   c.dtype, c.a.mask, (hipStream_t)stream);
+  const hipStream_t st = (hipStream_t)stream;
+  if (rows_per_group > kWeightedSplitMaxRows || cols == 0) {
+    const hipError_t err = launch_pv((const char*)s, (const char*)v, (char*)out, rows, cols, d, rows_per_group,
+                                     c.dtype, c.a.mask, st);
+    if (err != hipSuccess) return hip_fail(err, "kernel launch");
+    return ok();
+  }
+  // few rows per group: per-chunk states in a stream-ordered workspace, merged
+  const int64_t chunk = weighted_split_chunk(groups, cols);
+  const int64_t nch = (cols + chunk - 1) / chunk;
+  const size_t ml_bytes = (size_t)(rows * nch) * 2 * sizeof(float);
+  const size_t bytes = ml_bytes + (size_t)(rows * nch * d) * sizeof(float);
+  void* ws = nullptr;
+  hipError_t err = hipMallocAsync(&ws, bytes, st);
+  if (err != hipSuccess) return hip_fail(err, "hipMallocAsync of the state workspace");
+  float* const ml = (float*)ws;
+  float* const o = (float*)((char*)ws + ml_bytes);
+  err = launch_wstates((const char*)s, (const char*)v, rows, cols, d, rows_per_group, c.dtype, c.a.mask, chunk, nch,
+                       ml, o, st);
+  if (err == hipSuccess) err = launch_wmerge(ml, o, rows, nch, d, c.dtype, (char*)out, st);
+  const hipError_t ferr = hipFreeAsync(ws, st);
+  if (err != hipSuccess) return hip_fail(err, "kernel launch");
+  if (ferr != hipSuccess) return hip_fail(ferr, "hipFreeAsync of the state workspace");
+  return ok();
+}
+
+int softmax_weighted_states(const void* s, const void* v, int64_t rows, int64_t cols, int64_t d,
+                            int64_t rows_per_group, smx_dtype dtype, const smx_mask* mask, int64_t chunk_cols,
+                            float* ml, float* o, void* stream) {
+  Call c;
+  if (int rc = check_weighted("softmax_weighted_states", s, v, rows, cols, d, rows_per_group, dtype, mask, c))
+    return rc;
+  if (chunk_cols <= 0 || chunk_cols > kMaxWChunk)
+    return fail(SMX_EINVAL, "chunk_cols (%lld) must be in [1, %d]", (long long)chunk_cols, kMaxWChunk);
+  const int64_t nch = (cols + chunk_cols - 1) / chunk_cols;
+  if (rows == 0 || nch == 0) return ok();
+  if (ml == nullptr || o == nullptr) return fail(SMX_EINVAL, "ml and o must not be NULL");
+  if ((uintptr_t)ml % 4 != 0 || (uintptr_t)o % 4 != 0) return fail(SMX_EINVAL, "ml and o must be 4-byte aligned");
+  if (rows * nch > INT64_MAX / d / 4) return fail(SMX_EINVAL, "the size of o overflows int64");
+  const int64_t groups = rows / rows_per_group;
+  const uintptr_t mlb = (uintptr_t)(rows * nch * 8), obb = (uintptr_t)(rows * nch * d * 4);
+  const uintptr_t sb = (uintptr_t)(rows * cols * 2), vb = (uintptr_t)(groups * cols * d * 2);
+  if (overlaps(ml, mlb, o, obb) || overlaps(ml, mlb, s, sb) || overlaps(ml, mlb, v, vb) || overlaps(o, obb, s, sb) ||
+      overlaps(o, obb, v, vb))
+    return fail(SMX_EINVAL, "ml and o must overlap neither each other nor s or v");
+  const hipError_t err = launch_wstates((const char*)s, (const char*)v, rows, cols, d, rows_per_group, c.dtype,
+                                        c.a.mask, chunk_cols, nch, ml, o, (hipStream_t)stream);
+  if (err != hipSuccess) return hip_fail(err, "kernel launch");
+  return ok();
+}
+
+int softmax_weighted_merge(const float* ml, const float* o, int64_t rows, int64_t n_chunks, int64_t d,
+                           smx_dtype dtype, void* out, void* stream) {
+  if (dtype != SMX_F16 && dtype != SMX_BF16)
+    return fail(SMX_EINVAL, "softmax_weighted_merge writes SMX_F16 or SMX_BF16");
+  if (!pv_supported_d(d)) return fail(SMX_EINVAL, "d = %lld: the value width must be 32, 64 or 128", (long long)d);
+  if (rows < 0 || n_chunks < 0) return fail(SMX_EINVAL, "rows and n_chunks must be >= 0");
+  if (n_chunks > kMaxWMergeChunks)
+    return fail(SMX_EINVAL, "n_chunks (%lld) exceeds %lld", (long long)n_chunks, (long long)kMaxWMergeChunks);
+  if (rows == 0) return ok();
+  if (rows > INT64_MAX / (n_chunks + 1) / d / 4) return fail(SMX_EINVAL, "the size of o overflows int64");
+  if (out == nullptr || (n_chunks > 0 && (ml == nullptr || o == nullptr)))
+    return fail(SMX_EINVAL, "ml, o and out must not be NULL");
+  if ((uintptr_t)out % 2 != 0 || (uintptr_t)ml % 4 != 0 || (uintptr_t)o % 4 != 0)
+    return fail(SMX_EINVAL, "out must be 2-byte aligned, ml and o 4-byte aligned");
+  const uintptr_t ob = (uintptr_t)(rows * d * 2);
+  if (overlaps(out, ob, ml, (uintptr_t)(rows * n_chunks * 8)) || overlaps(out, ob, o, (uintptr_t)(rows * n_chunks * d * 4)))
+    return fail(SMX_EINVAL, "out overlaps ml or o");
+  const hipError_t err = launch_wmerge(ml, o, rows, n_chunks, d, (int)dtype, (char*)out, (hipStream_t)stream);
   if (err != hipSuccess) return hip_fail(err, "kernel launch");
   return ok();
 }

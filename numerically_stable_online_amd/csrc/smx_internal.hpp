@@ -88,6 +88,18 @@ hipError_t launch_bwd_rows(const char* p, const char* g, char* dx, int64_t rows,
 hipError_t launch_bwd_split(const char* p, const char* g, char* dx, int64_t rows, int64_t cols, int dtype, bool vec,
                             int64_t chunk, int64_t n_chunks, float2* partials, hipStream_t stream);
 
+// --- softmax-weighted value sums split along the keys (k_wsplit.hip) ---
+// the longest key chunk of one state (its weights sit in LDS)
+constexpr int kMaxWChunk = 2048;
+// the most chunk states one row's merge takes (their factors sit in LDS)
+constexpr int64_t kMaxWMergeChunks = 16384;
+// per (row, chunk): ml = (m, l), o[d]; v 16-byte aligned
+hipError_t launch_wstates(const char* s, const char* v, int64_t rows, int64_t cols, int64_t d, int64_t rows_per_group,
+                          int dtype, const MaskArgs& mask, int64_t chunk, int64_t n_chunks, float* ml, float* o,
+                          hipStream_t stream);
+hipError_t launch_wmerge(const float* ml, const float* o, int64_t rows, int64_t n_chunks, int64_t d, int dtype,
+                         char* out, hipStream_t stream);
+
 // --- softmax-weighted value sums on the matrix cores (k_pv.hip) ---
 bool pv_supported_d(int64_t d);
 hipError_t launch_pv(const char* s, const char* v, char* out, int64_t rows, int64_t cols, int64_t d,

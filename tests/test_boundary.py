@@ -37,7 +37,7 @@ def test_header_declares_the_entry_points():
     for n in ("softmax_rows", "softmax_rows_path", "softmax_row_stats", "softmax_merge_normalize",
               "log_softmax_rows", "log_softmax_rows_path", "softmax_backward_rows",
               "softmax_backward_rows_path", "softmax_cross_entropy_rows", "softmax_cross_entropy_rows_path",
-              "softmax_weighted_rows",
+              "softmax_weighted_rows", "softmax_weighted_states", "softmax_weighted_merge",
               "softmax_default_chunk_cols", "softmax_select_path", "smx_last_error"):
         assert n in names, names
 
@@ -121,6 +121,46 @@ def test_weighted_rows_argument_checks(smx):
         assert L.softmax_weighted_rows(*args) == EINVAL, word
         assert word in smx.smx_last_error(), (word, smx.smx_last_error())
     assert L.softmax_weighted_rows(None, None, None, 0, 64, 64, 8, 2, None, None) == 0
+
+
+def test_weighted_split_argument_checks(smx):
+    """The key-split states and their merge validate like the fused call, plus
+    the chunk width (1 .. 2048), the state buffers and the merge's chunk count;
+    the failing calls enqueue nothing."""
+    lib = smx.lib()
+    fake = 1 << 20
+    ml, o = fake * 64, fake * 128
+
+    def states(**kw):
+        a = dict(s=fake, v=fake * 8, rows=16, cols=4096, d=128, rpg=1, dtype=2, chunk=512, ml=ml, o=o)
+        a.update(kw)
+        return lib.softmax_weighted_states(a["s"], a["v"], a["rows"], a["cols"], a["d"], a["rpg"], a["dtype"], None,
+                                           a["chunk"], a["ml"], a["o"], None)
+
+    assert states(dtype=0) == smx.SMX_EINVAL            # f32
+    assert states(d=96) == smx.SMX_EINVAL               # width
+    assert states(chunk=0) == smx.SMX_EINVAL
+    assert states(chunk=4096) == smx.SMX_EINVAL         # above 2048
+    assert states(ml=0) == smx.SMX_EINVAL
+    assert states(o=0) == smx.SMX_EINVAL
+    assert states(ml=o) == smx.SMX_EINVAL               # ml overlaps o
+    assert states(o=fake) == smx.SMX_EINVAL             # o overlaps s
+    assert states(rpg=3) == smx.SMX_EINVAL              # rows not a multiple
+    assert states(rows=0) == smx.SMX_OK                 # nothing to do
+
+    def merge(**kw):
+        a = dict(ml=ml, o=o, rows=16, nch=8, d=128, dtype=2, out=fake)
+        a.update(kw)
+        return lib.softmax_weighted_merge(a["ml"], a["o"], a["rows"], a["nch"], a["d"], a["dtype"], a["out"], None)
+
+    assert merge(dtype=0) == smx.SMX_EINVAL
+    assert merge(d=16) == smx.SMX_EINVAL
+    assert merge(nch=16385) == smx.SMX_EINVAL
+    assert merge(nch=-1) == smx.SMX_EINVAL
+    assert merge(out=0) == smx.SMX_EINVAL
+    assert merge(out=fake + 1) == smx.SMX_EINVAL        # odd address
+    assert merge(out=ml) == smx.SMX_EINVAL              # out overlaps ml
+    assert merge(rows=0) == smx.SMX_OK
 
 
 def test_empty_shapes_are_noops(smx):

@@ -916,6 +916,102 @@ def test_weighted_rows_small(dtype, d):
         banner(f"{what}: {res}")
 
 
+# Key-split weighted sums: per-(row, chunk) states (m, l, o) and their merge.
+STATE_TOL = 4e-6  # relative, on l and (against sum |w v|) on o; derived in DESIGN
+
+
+def _split_case(rng, dtype, rpg, groups, cols, d, mask_kind):
+    rows = rpg * groups
+    s = W.to_format(3.0 * rng.standard_normal((rows, cols)), dtype)
+    v = W.to_format(rng.standard_normal((groups, cols, d)), dtype)
+    if mask_kind == "none":
+        mask = W.MaskSpec("none")
+    elif mask_kind == "causal":
+        mask = W.MaskSpec("causal", causal_period=rpg, causal_offset=cols // 2)
+    elif mask_kind == "valid_len":
+        vl = rng.integers(0, cols + 1, rows).astype(np.int32)
+        vl[0] = 0
+        mask = W.MaskSpec("valid_len", valid_len=vl)
+    else:
+        mask = W.MaskSpec("keep", keep=(rng.random((rows, cols)) < 0.7).astype(np.uint8))
+    if rows >= 4:  # policy rows: NaN and +inf in a valid lane, all -inf
+        W.set_bits(s, 1, 5, dtype, W.QNAN[dtype])
+        W.set_bits(s, 2, cols - 1, dtype, W.POS_INF[dtype])
+        s[3, :] = W.NEG_INF[dtype]
+    return s, v, mask
+
+
+def _check_states(ml, o, s, v, dtype, rpg, chunk, mask, what):
+    m_ref, l_ref, o_ref = oracle.weighted_chunk_states(s, v, dtype, rpg, chunk, mask)
+    _, _, o_abs = oracle.weighted_chunk_states(s, abs_bits(v, dtype), dtype, rpg, chunk, mask)
+    m_g = ml[..., 0].astype(np.float64)
+    l_g = ml[..., 1].astype(np.float64)
+    o_g = o.astype(np.float64)
+    pois = np.isnan(m_ref)
+    empty = m_ref == -np.inf
+    live = ~pois & ~empty
+    assert np.isnan(m_g[pois]).all() and np.isnan(l_g[pois]).all() and np.isnan(o_g[pois]).all(), what
+    assert (m_g[empty] == -np.inf).all() and (l_g[empty] == 0).all() and (o_g[empty] == 0).all(), what
+    assert np.array_equal(m_g[live], m_ref[live]), f"{what}: m is the exact chunk maximum"
+    rel = np.abs(l_g[live] - l_ref[live]) / l_ref[live]
+    assert rel.max(initial=0) <= STATE_TOL, f"{what}: l off by {rel.max():.3e}"
+    err = np.abs(o_g[live] - o_ref[live])
+    bound = STATE_TOL * o_abs[live] + 1e-30
+    assert (err <= bound).all(), f"{what}: o off by {(err / bound).max():.3f} of the bound"
+    return int(live.sum())
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("d", [32, 64, 128])
+def test_weighted_states_and_merge(dtype, d):
+    """States against the oracle's chunk states, then the merge of the GPU
+    states and of the oracle's (rounded to fp32) against the oracle's direct
+    weighted sums, over ragged chunks, every mask kind and policy rows."""
+    rng = np.random.default_rng(700 + d)
+    for rpg, groups, cols, chunk in ((1, 9, 2056, 512), (3, 3, 200, 64), (8, 2, 4096, 2048), (4, 2, 1000, 300)):
+        for mask_kind in ("none", "causal", "valid_len", "keep"):
+            s, v, mask = _split_case(rng, dtype, rpg, groups, cols, d, mask_kind)
+            what = f"states {dtype} d={d} rpg={rpg} cols={cols} chunk={chunk} {mask_kind}"
+            banner(what)
+            sd = to_device(s, dtype)
+            vd = to_device(v.reshape(-1, d), dtype).view(groups, cols, d)
+            ml, o = smx.softmax_weighted_states(sd, vd, chunk, **mask_kwargs(mask))
+            torch.cuda.synchronize()
+            _check_states(ml.cpu().numpy(), o.cpu().numpy(), s, v, dtype, rpg, chunk, mask, what)
+            ref, st, scale = weighted_reference(s, v, dtype, rpg, mask)
+            out = smx.softmax_weighted_merge(ml, o, TORCH_DTYPE[dtype])
+            torch.cuda.synchronize()
+            check_weighted(to_host(out, dtype), dtype, ref, st, scale, what + " merged")
+            # the merge alone, fed with the oracle's states
+            m_ref, l_ref, o_ref = oracle.weighted_chunk_states(s, v, dtype, rpg, chunk, mask)
+            ml_o = torch.from_numpy(np.stack([m_ref, l_ref], -1).astype(np.float32)).cuda()
+            o_o = torch.from_numpy(o_ref.astype(np.float32)).cuda()
+            out2 = smx.softmax_weighted_merge(ml_o, o_o, TORCH_DTYPE[dtype])
+            torch.cuda.synchronize()
+            check_weighted(to_host(out2, dtype), dtype, ref, st, scale, what + " merge of oracle states")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_weighted_rows_few_rows_per_group(dtype):
+    """Groups of at most 8 rows take the key split inside softmax_weighted_rows
+    (states in a workspace, then the merge): the fused call meets the oracle
+    for 1, 3 and 8 rows per group; constant values come back exactly."""
+    rng = np.random.default_rng(720)
+    for rpg, groups, cols, d in ((1, 40, 2048, 128), (3, 7, 200, 64), (8, 5, 4104, 32)):
+        for mask_kind in ("none", "causal", "valid_len", "keep"):
+            s, v, mask = _split_case(rng, dtype, rpg, groups, cols, d, mask_kind)
+            what = f"weighted split {dtype} rpg={rpg} cols={cols} d={d} {mask_kind}"
+            banner(what)
+            out = run_weighted(s, v, dtype, mask)
+            ref, st, scale = weighted_reference(s, v, dtype, rpg, mask)
+            check_weighted(out, dtype, ref, st, scale, what)
+    s = W.to_format(4.0 * rng.standard_normal((6, 512)), dtype)
+    c = W.to_format(rng.standard_normal(64), dtype)
+    vc = np.broadcast_to(c, (2, 512, 64)).copy()
+    out = run_weighted(s, vc, dtype)
+    assert np.array_equal(out, np.broadcast_to(c, (6, 64))), f"weighted split constant {dtype}"
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 def test_weighted_rows_special_values(dtype):
     rng = np.random.default_rng(510)
