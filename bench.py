@@ -61,6 +61,8 @@ def parse():
                          "entry points are also timed ('' for none)")
     ap.add_argument("--no-weighted", dest="weighted", action="store_false",
                     help="skip the softmax-weighted value sums on the causal scores")
+    ap.add_argument("--no-decode", dest="decode", action="store_false",
+                    help="skip the softmax-weighted value sums on the decode-shaped input")
     ap.add_argument("--no-copy-context", action="store_true",
                     help="skip timing a plain device copy of the headline input (context only)")
     ap.add_argument("--no-spread", action="store_true",
@@ -268,6 +270,41 @@ def device_copy(w, steps: int, warmup: int):
             "GBps": round(2 * nbytes / (ms * 1e-3) / 1e9, 1), "buffer_copies": copies}
 
 
+def decode_weighted(steps: int, warmup: int, groups: int = 256, keys: int = 32768, d: int = 128):
+    """softmax_weighted_rows on a decode-shaped input: one score row per
+    group (one query per head) over many keys, the attention workload's
+    value width and element type. The seeded synthetic input is drawn on the
+    device (timing only; the parity tests check this path on smaller shapes).
+    Two copies rotate so V (2 GiB each) streams from HBM. Algorithmic bytes:
+    the scores and V read once, the output written."""
+    import torch
+
+    import numerically_stable_online_amd as smx
+
+    g = torch.Generator(device="cuda")
+    g.manual_seed(6)
+    ss = [(3.0 * torch.randn(groups, keys, device="cuda", generator=g)).to(torch.bfloat16) for _ in range(2)]
+    vs = [torch.randn(groups, keys, d, device="cuda", generator=g).to(torch.bfloat16) for _ in range(2)]
+    out = torch.empty(groups, d, dtype=torch.bfloat16, device="cuda")
+    nbytes = groups * keys * 2 + groups * keys * d * 2 + groups * d * 2
+    for i in range(warmup):
+        smx.softmax_weighted_rows(ss[i % 2], vs[i % 2], out)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for i in range(steps):
+        smx.softmax_weighted_rows(ss[i % 2], vs[i % 2], out)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / steps
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": f"bf16_decode_{groups}x1x{keys}_values_d{d}", "path": "key split (states + merge)",
+            "algorithmic_bytes": nbytes, "gpu_ms_per_launch": round(ms, 5), "GBps_launch": round(gbs, 1),
+            "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 def cpu_baseline(w, nbytes: int):
     import oracle
 
@@ -398,6 +435,11 @@ def main():
     }
     if weighted is not None:
         out["next_ops"]["softmax_weighted_rows"] = {"causal": weighted}
+    if args.decode:
+        dec = decode_weighted(args.steps, args.warmup)
+        out["next_ops"].setdefault("softmax_weighted_rows", {})["decode"] = dec
+        print(f"# softmax_weighted_rows decode: {dec['GBps_launch']:.0f} GB/s per launch "
+              f"({dec['gpu_ms_per_launch'] * 1e3:.1f} us)", file=sys.stderr, flush=True)
     if not args.no_copy_context:
         cp = device_copy(w, args.steps, args.warmup)
         out["context"] = {"device_copy": cp, "kernel_frac_of_copy": round(kgbs / cp["GBps"], 4)}

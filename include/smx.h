@@ -223,9 +223,10 @@ SMX_API int softmax_cross_entropy_rows_path(const void* x, const int32_t* target
  *   d  : 32, 64 or 128; rows must be a multiple of rows_per_group.
  * The running state is fp32. The weights p enter the matrix cores as a
  * high and a low 16-bit part (about 16 significant bits); the values enter
- * exactly; products accumulate in fp32. Groups of at most 8 rows take the
- * key split of softmax_weighted_states and softmax_weighted_merge instead
- * (fp32 on the vector ALUs), with a stream-ordered workspace.
+ * exactly; products accumulate in fp32. Groups of at most 4 rows (or of at
+ * most 8 when there are fewer than 256 groups) take the key split of
+ * softmax_weighted_states and softmax_weighted_merge instead (fp32 on the
+ * vector ALUs), with a stream-ordered workspace.
  * Policy: a poisoned row (+inf/NaN in a valid lane) gives the canonical NaN
  * in every component; an empty or fully masked row gives zeros. SMX_F32,
  * other widths, misalignment and overlap are SMX_EINVAL; rows = 0 is a
@@ -266,7 +267,7 @@ SMX_API int softmax_weighted_states(const void* s, const void* v, int64_t rows, 
  * states are all empty is +0.0. Chunks are folded in order, so results are
  * deterministic. softmax_weighted_rows takes this split (states in a
  * stream-ordered workspace of rows * n_chunks * (d + 2) * 4 bytes, then this
- * merge) when rows_per_group <= 8. */
+ * merge) for groups of few rows. */
 SMX_API int softmax_weighted_merge(const float* ml, const float* o, int64_t rows, int64_t n_chunks, int64_t d,
                                    smx_dtype dtype, void* out, void* stream);
 

@@ -14,10 +14,10 @@
 // the vector ALUs.
 //
 // k_wstates: one workgroup per (group, chunk). Rows of the group are taken
-// four at a time: their scores for the chunk become weights in LDS (the chunk
-// maximum found first, so m is exact), then each thread streams 16-byte
-// slices of V rows (8 value components) and accumulates those components for
-// the four rows. The threads sharing components are reduced with shuffles
+// four (or eight) at a time: their scores for the chunk become weights in LDS
+// (the chunk maximum found first, so m is exact), then each thread streams
+// 16-byte slices of V rows (8 value components), four loads ahead, and
+// accumulates those components for each of the rows. The threads sharing components are reduced with shuffles
 // inside a wave and through LDS across waves.
 //
 // k_wmerge: one workgroup per row; the states are folded by the merge rule
@@ -28,17 +28,18 @@
 namespace smx {
 namespace {
 
-constexpr int kRowsPerPass = 4;  // score rows whose weights are in LDS at once
-
-template <int DT, int D, bool KEEP>
+// RP: score rows whose weights sit in LDS at once (4, or 8 for larger groups)
+template <int DT, int D, int RP, bool KEEP>
 __global__ __launch_bounds__(kThreads) void k_wstates(const char* __restrict__ s, const char* __restrict__ v,
                                                       int64_t rows, int64_t cols, int64_t rpg, MaskArgs mask,
                                                       int64_t chunk, int64_t nch, float* __restrict__ ml,
                                                       float* __restrict__ o) {
   constexpr int S = 2;
+  constexpr int kRowsPerPass = RP;
   constexpr int KL = D / 8;             // threads covering one V row (8 components each)
   constexpr int JR = kThreads / KL;     // V rows in flight per step across the workgroup
-  __shared__ float w[kRowsPerPass][kMaxWChunk];
+  constexpr int kUnroll = 4;            // V loads of a thread issued ahead of their products
+  extern __shared__ float wbuf[];       // RP x chunk weights
   __shared__ float part[kWaves][kRowsPerPass][D];
   __shared__ RedScratch red;
   const int tid = threadIdx.x;
@@ -79,7 +80,7 @@ __global__ __launch_bounds__(kThreads) void k_wstates(const char* __restrict__ s
           if (j < lim && (!KEEP || mask.keep[r * cols + j0 + j] != 0)) {
             x = dec<DT>(*reinterpret_cast<const uint16_t*>(sr + j * S));
           }
-          w[q][j] = x;
+          wbuf[q * chunk + j] = x;
           mx = vmax(mx, x);
         }
         mx = block_max<kWaves>(mx, red);
@@ -89,8 +90,8 @@ __global__ __launch_bounds__(kThreads) void k_wstates(const char* __restrict__ s
         float sum = 0.0f;
         if (live[q]) {
           for (int j = tid; j < n; j += kThreads) {
-            const float e = __builtin_amdgcn_exp2f((w[q][j] - mx) * kLog2e);  // -inf lanes give 0
-            w[q][j] = e;
+            const float e = __builtin_amdgcn_exp2f((wbuf[q * chunk + j] - mx) * kLog2e);  // -inf lanes give 0
+            wbuf[q * chunk + j] = e;
             sum += e;
           }
           sum = block_sum<kWaves>(sum, red);
@@ -106,21 +107,32 @@ __global__ __launch_bounds__(kThreads) void k_wstates(const char* __restrict__ s
       for (int q = 0; q < kRowsPerPass; ++q)
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[q][e] = 0.0f;
-      for (int j = jr; j < n; j += JR) {
-        const u32x4 raw = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vg + ((int64_t)j * D + kq * 8) * S));
-        const uint32_t ws[4] = {raw.x, raw.y, raw.z, raw.w};
-        float vv[8];
+      for (int j0u = jr; j0u < n; j0u += kUnroll * JR) {
+        u32x4 raw[kUnroll];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          vv[2 * e] = dec<DT>(ws[e] & 0xFFFFu);
-          vv[2 * e + 1] = dec<DT>(ws[e] >> 16);
+        for (int u = 0; u < kUnroll; ++u) {
+          const int j = j0u + u * JR;
+          raw[u] = j < n ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vg + ((int64_t)j * D + kq * 8) * S))
+                         : u32x4{0u, 0u, 0u, 0u};
         }
 #pragma unroll
-        for (int q = 0; q < kRowsPerPass; ++q) {
-          if (!live[q]) continue;  // uniform
-          const float wj = w[q][j];
+        for (int u = 0; u < kUnroll; ++u) {
+          const int j = j0u + u * JR;
+          if (j >= n) break;
+          const uint32_t ws[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+          float vv[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[q][e] = __builtin_fmaf(wj, vv[e], acc[q][e]);
+          for (int e = 0; e < 4; ++e) {
+            vv[2 * e] = dec<DT>(ws[e] & 0xFFFFu);
+            vv[2 * e + 1] = dec<DT>(ws[e] >> 16);
+          }
+#pragma unroll
+          for (int q = 0; q < kRowsPerPass; ++q) {
+            if (!live[q]) continue;  // uniform
+            const float wj = wbuf[q * chunk + j];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[q][e] = __builtin_fmaf(wj, vv[e], acc[q][e]);
+          }
         }
       }
       // the wave's V rows sharing a component: lanes kq, kq + KL, ...
@@ -217,19 +229,27 @@ __global__ __launch_bounds__(kThreads) void k_wmerge(const float* __restrict__ m
 
 constexpr int64_t kMaxGrid = 1 << 20;
 
+template <int DT, int D, int RP>
+hipError_t launch_states_rp(const char* s, const char* v, int64_t rows, int64_t cols, int64_t rpg,
+                            const MaskArgs& mask, int64_t chunk, int64_t nch, float* ml, float* o, hipStream_t st) {
+  const int64_t total = rows / rpg * nch;
+  const unsigned grid = (unsigned)(total < kMaxGrid ? total : kMaxGrid);
+  const size_t lds = (size_t)RP * (size_t)chunk * sizeof(float);
+  if (mask.kind == kMaskKeep) {
+    hipLaunchKernelGGL((k_wstates<DT, D, RP, true>), dim3(grid), dim3(kThreads), lds, st, s, v, rows, cols, rpg,
+                       mask, chunk, nch, ml, o);
+  } else {
+    hipLaunchKernelGGL((k_wstates<DT, D, RP, false>), dim3(grid), dim3(kThreads), lds, st, s, v, rows, cols, rpg,
+                       mask, chunk, nch, ml, o);
+  }
+  return hipGetLastError();
+}
+
 template <int DT, int D>
 hipError_t launch_states_d(const char* s, const char* v, int64_t rows, int64_t cols, int64_t rpg,
                            const MaskArgs& mask, int64_t chunk, int64_t nch, float* ml, float* o, hipStream_t st) {
-  const int64_t total = rows / rpg * nch;
-  const unsigned grid = (unsigned)(total < kMaxGrid ? total : kMaxGrid);
-  if (mask.kind == kMaskKeep) {
-    hipLaunchKernelGGL((k_wstates<DT, D, true>), dim3(grid), dim3(kThreads), 0, st, s, v, rows, cols, rpg, mask,
-                       chunk, nch, ml, o);
-  } else {
-    hipLaunchKernelGGL((k_wstates<DT, D, false>), dim3(grid), dim3(kThreads), 0, st, s, v, rows, cols, rpg, mask,
-                       chunk, nch, ml, o);
-  }
-  return hipGetLastError();
+  if (rpg > 4) return launch_states_rp<DT, D, 8>(s, v, rows, cols, rpg, mask, chunk, nch, ml, o, st);
+  return launch_states_rp<DT, D, 4>(s, v, rows, cols, rpg, mask, chunk, nch, ml, o, st);
 }
 
 template <int DT>

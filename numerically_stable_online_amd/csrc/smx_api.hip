@@ -198,9 +198,14 @@ int check_weighted(const char* name, const void* s, const void* v, int64_t rows,
   return SMX_OK;
 }
 
-// groups of at most this many score rows take the key-split path in
-// softmax_weighted_rows (the matrix-core tiles hold 128 rows)
-constexpr int64_t kWeightedSplitMaxRows = 8;
+// softmax_weighted_rows takes the key-split path for groups of at most 4
+// score rows, and of at most 8 when there are too few groups (under 256) for
+// the matrix-core kernel's one workgroup per 128-row tile to fill the chip;
+// larger groups keep the matrix cores, whose products the vector ALUs cannot
+// match (measured: 256 groups of 8 rows, 8192 keys: 163 us there, 300 us split)
+bool weighted_split(int64_t rows_per_group, int64_t groups) {
+  return rows_per_group <= 4 || (rows_per_group <= 8 && groups < 256);
+}
 
 // the key chunk of that path: 512, halved (down to 128) while the grid has
 // fewer than 2048 workgroups
@@ -409,7 +414,7 @@ int softmax_weighted_rows(const void* s, const void* v, void* out, int64_t rows,
   if (overlaps(out, ob, s, (uintptr_t)(rows * cols * 2)) || overlaps(out, ob, v, (uintptr_t)(groups * cols * d * 2)))
     return fail(SMX_EINVAL, "out overlaps s or v");
   const hipStream_t st = (hipStream_t)stream;
-  if (rows_per_group > kWeightedSplitMaxRows || cols == 0) {
+  if (!weighted_split(rows_per_group, groups) || cols == 0) {
     const hipError_t err = launch_pv((const char*)s, (const char*)v, (char*)out, rows, cols, d, rows_per_group,
                                      c.dtype, c.a.mask, st);
     if (err != hipSuccess) return hip_fail(err, "kernel launch");

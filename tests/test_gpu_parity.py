@@ -993,9 +993,10 @@ def test_weighted_states_and_merge(dtype, d):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 def test_weighted_rows_few_rows_per_group(dtype):
-    """Groups of at most 8 rows take the key split inside softmax_weighted_rows
-    (states in a workspace, then the merge): the fused call meets the oracle
-    for 1, 3 and 8 rows per group; constant values come back exactly."""
+    """Groups of at most 4 rows (8 when there are few groups) take the key
+    split inside softmax_weighted_rows (states in a workspace, then the
+    merge): the fused call meets the oracle for 1, 3 and 8 rows per group;
+    constant values come back exactly."""
     rng = np.random.default_rng(720)
     for rpg, groups, cols, d in ((1, 40, 2048, 128), (3, 7, 200, 64), (8, 5, 4104, 32)):
         for mask_kind in ("none", "causal", "valid_len", "keep"):
