@@ -466,6 +466,14 @@ def _graph_cases():
     vl = torch.from_numpy(np.random.default_rng(3).integers(0, 513, 4096).astype(np.int32)).cuda()
     tgt = torch.from_numpy(W.class_targets(1024, 4096, 5)).cuda()
 
+    vl40 = torch.from_numpy(np.random.default_rng(4).integers(0, 2049, 40).astype(np.int32)).cuda()
+
+    def split_inputs(seed):
+        rng = np.random.default_rng(seed)
+        s = to_device(W.to_format(3.0 * rng.standard_normal((40, 2048)), "bf16"), "bf16")
+        v = to_device(W.to_format(rng.standard_normal((40 * 2048, 128)), "bf16"), "bf16").view(40, 2048, 128)
+        return [s, v]
+
     def weighted_inputs(seed):
         rng = np.random.default_rng(seed)
         s = to_device(W.to_format(3.0 * rng.standard_normal((256, 200)), "bf16"), "bf16")
@@ -485,6 +493,8 @@ def _graph_cases():
          lambda p, g: smx.softmax_backward_rows(p, g, path="split", chunk_cols=4096)),
         ("weighted sums, causal", weighted_inputs,
          lambda s, v: smx.softmax_weighted_rows(s, v, causal_period=128)),
+        ("weighted sums, key split (one row per group)", split_inputs,
+         lambda s, v: smx.softmax_weighted_rows(s, v, valid_len=vl40)),
     ]
 
 
