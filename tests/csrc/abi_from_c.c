@@ -23,6 +23,8 @@
  *   uint16 dxb[rows*cols]
  *   float  dx[rows*cols]         softmax_backward_rows(y, g)
  *   uint16 o[wrows*d]            softmax_weighted_rows(s, v), causal per group
+ *   uint16 o2[wrows*d]           softmax_weighted_states (chunks of 64 keys) +
+ *                                softmax_weighted_merge, the same sums
  * Exit status 0 only if every call returned SMX_OK and an invalid call was
  * rejected with SMX_EINVAL and a message.
  */
@@ -118,6 +120,10 @@ int main(int argc, char** argv) {
   void* dxb = device_buffer(n * 2);
   void* dx = device_buffer(n * 4);
   void* o = device_buffer((size_t)(wrows * d) * 2);
+  const int64_t wchunk = 64, wnch = (wcols + wchunk - 1) / wchunk;
+  float* wml = (float*)device_buffer((size_t)(wrows * wnch) * 2 * sizeof(float));
+  float* wo = (float*)device_buffer((size_t)(wrows * wnch * d) * sizeof(float));
+  void* o2 = device_buffer((size_t)(wrows * d) * 2);
 
   hipStream_t st;
   hip_check(hipStreamCreate(&st), "hipStreamCreate");
@@ -139,6 +145,9 @@ int main(int argc, char** argv) {
             "softmax_cross_entropy_rows");
   smx_check(softmax_backward_rows(y, g, dx, rows, cols, SMX_F32, st), "softmax_backward_rows");
   smx_check(softmax_weighted_rows(s, v, o, wrows, wcols, d, rpg, SMX_BF16, &causal, st), "softmax_weighted_rows");
+  smx_check(softmax_weighted_states(s, v, wrows, wcols, d, rpg, SMX_BF16, &causal, wchunk, wml, wo, st),
+            "softmax_weighted_states");
+  smx_check(softmax_weighted_merge(wml, wo, wrows, wnch, d, SMX_BF16, o2, st), "softmax_weighted_merge");
 
   /* an invalid element type is rejected before anything is enqueued */
   const int bad = softmax_rows(x, y, rows, cols, (smx_dtype)7, NULL, st);
@@ -156,9 +165,10 @@ int main(int argc, char** argv) {
   write_back(out, dxb, n * 2);
   write_back(out, dx, n * 4);
   write_back(out, o, (size_t)(wrows * d) * 2);
+  write_back(out, o2, (size_t)(wrows * d) * 2);
   fclose(out);
   hip_check(hipStreamDestroy(st), "hipStreamDestroy");
-  void* bufs[] = {x, vl, xb, tgt, g, s, v, y, y2, stats, logp, lse, loss, dxb, dx, o};
+  void* bufs[] = {x, vl, xb, tgt, g, s, v, y, y2, stats, logp, lse, loss, dxb, dx, o, wml, wo, o2};
   for (size_t i = 0; i < sizeof bufs / sizeof bufs[0]; ++i) hip_check(hipFree(bufs[i]), "hipFree");
   free(h_x);
   free(h_vl);

@@ -585,12 +585,12 @@ def test_c_program_through_the_abi(tmp_path):
     parts, off = [], 0
     for dt, count in ((np.float32, rows * cols), (np.float32, rows * cols), (np.uint16, rows * cols),
                       (np.float32, rows), (np.float32, rows), (np.uint16, rows * cols), (np.float32, rows * cols),
-                      (np.uint16, wrows * d)):
+                      (np.uint16, wrows * d), (np.uint16, wrows * d)):
         nbytes = count * np.dtype(dt).itemsize
         parts.append(np.frombuffer(raw[off:off + nbytes], dtype=dt))
         off += nbytes
     assert off == len(raw)
-    y, y2, logp, lse, loss, dxb, dx, o = parts
+    y, y2, logp, lse, loss, dxb, dx, o, o2 = parts
     mask = W.MaskSpec("valid_len", valid_len=vl)
     check_full(x, "f32", mask, y.reshape(rows, cols), "C: softmax_rows")
     check_full(x, "f32", mask, y2.reshape(rows, cols), "C: softmax_row_stats + softmax_merge_normalize")
@@ -599,6 +599,7 @@ def test_c_program_through_the_abi(tmp_path):
     check_bwd_full(y.reshape(rows, cols), g, "f32", dx.reshape(rows, cols), "C: softmax_backward_rows")
     ref, st, scale = weighted_reference(sc, v, "bf16", rpg, W.MaskSpec("causal", causal_period=rpg))
     check_weighted(o.reshape(wrows, d), "bf16", ref, st, scale, "C: softmax_weighted_rows")
+    check_weighted(o2.reshape(wrows, d), "bf16", ref, st, scale, "C: softmax_weighted_states + softmax_weighted_merge")
 
 
 def test_invalid_arguments_raise():
