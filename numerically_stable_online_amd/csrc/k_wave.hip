@@ -17,19 +17,23 @@
 namespace smx {
 namespace {
 
-template <int DT, int E, int VPT, int RPW, bool KEEP, int EPI>
-__global__ __launch_bounds__(kThreads) void k_wave(RowArgs a) {
+// MK: the mask class, fixed at compile time: kMaskNone (the whole row),
+// kMaskValidLen (a valid prefix: valid lengths or causal) or kMaskKeep.
+template <int DT, int E, int VPT, int RPW, int MK, int EPI>
+__global__ __launch_bounds__(kThreads) void k_wave(RowArgs a, int64_t rbase) {
+  constexpr bool KEEP = MK == kMaskKeep;
   constexpr int S = Fmt<DT>::S;
   constexpr bool ACC = DT == kF32;
   const int lane = threadIdx.x & 63;
-  const int64_t row0 = ((int64_t)blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) * RPW;
+  const int64_t row0 = rbase + ((int64_t)blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) * RPW;
   if (row0 >= a.rows) return;  // wave-uniform
   const int64_t cols = a.cols;
 
   // load, mask and lane-wise max for every row of the wave
   float v[RPW][VPT][E];
   float mx[RPW];
-  int64_t prefix[RPW];
+  const int icols = (int)cols;  // rows on this path hold at most 4096 lanes
+  int prefix[RPW];
   // cross-entropy: each row's target lane (-1: ignored row), read before the
   // row so its latency overlaps the row's loads, and the target's logit as
   // this lane holds it (-inf in every other lane)
@@ -39,7 +43,7 @@ __global__ __launch_bounds__(kThreads) void k_wave(RowArgs a) {
 #pragma unroll
   for (int r = 0; r < RPW; ++r) {
     const int64_t row = row0 + r;
-    prefix[r] = row < a.rows ? valid_prefix(a.mask, row, cols) : 0;
+    prefix[r] = row < a.rows ? (MK == kMaskValidLen ? (int)valid_prefix(a.mask, row, cols) : icols) : 0;
     mx[r] = -kInf;
     tgt[r] = (EPI == kEpiXent && row < a.rows) ? row_target(a.target, row, cols) : -1;
     slot[r] = target_slot<64, E>(tgt[r], lane);
@@ -52,9 +56,9 @@ __global__ __launch_bounds__(kThreads) void k_wave(RowArgs a) {
     for (int k = 0; k < VPT; ++k) {
       // the pack's valid lanes: E inside the prefix, 0 past it, so each
       // lane's test is a 32-bit compare with a constant
-      const int64_t j0 = (int64_t)(k * 64 + lane) * E;
-      const int64_t left = prefix[r] - j0;
-      const int rem = left <= 0 ? 0 : (left >= E ? E : (int)left);
+      const int j0 = (k * 64 + lane) * E;
+      const int left = prefix[r] - j0;
+      const int rem = left <= 0 ? 0 : (left >= E ? E : left);
       Pack<DT, E> p;
       p.fill(0);
       uint64_t kb = ~0ull;
@@ -105,8 +109,8 @@ __global__ __launch_bounds__(kThreads) void k_wave(RowArgs a) {
           z.fill(0u);
 #pragma unroll
           for (int k = 0; k < VPT; ++k) {
-            const int64_t j0 = (int64_t)(k * 64 + lane) * E;
-            if (j0 < cols) z.template store<true>(yr + j0 * S);
+            const int j0 = (k * 64 + lane) * E;
+            if (j0 < icols) z.template store<true>(yr + j0 * S);
           }
         }
         continue;
@@ -129,8 +133,8 @@ __global__ __launch_bounds__(kThreads) void k_wave(RowArgs a) {
         const uint32_t fill = poisoned ? Fmt<DT>::kNaN : (EPI == kEpiLogSoftmax ? Fmt<DT>::kNegInf : 0u);
 #pragma unroll
         for (int k = 0; k < VPT; ++k) {
-          const int64_t j0 = (int64_t)(k * 64 + lane) * E;
-          if (j0 < cols) {
+          const int j0 = (k * 64 + lane) * E;
+          if (j0 < icols) {
             uint32_t h[E];
 #pragma unroll
             for (int e = 0; e < E; ++e) h[e] = (!poisoned && k * E + e == slot[r]) ? enc<DT>(-1.0f) : fill;
@@ -202,8 +206,8 @@ __global__ __launch_bounds__(kThreads) void k_wave(RowArgs a) {
       if (a.y != nullptr) {
 #pragma unroll
         for (int k = 0; k < VPT; ++k) {
-          const int64_t j0 = (int64_t)(k * 64 + lane) * E;
-          if (j0 < cols) {
+          const int j0 = (k * 64 + lane) * E;
+          if (j0 < icols) {
             float o[E];
 #pragma unroll
             for (int e = 0; e < E; ++e) o[e] = minus_lse(v[r][k][e], lse);
@@ -220,8 +224,8 @@ __global__ __launch_bounds__(kThreads) void k_wave(RowArgs a) {
       const float at_t = (0.0f - others) / total;
 #pragma unroll
       for (int k = 0; k < VPT; ++k) {
-        const int64_t j0 = (int64_t)(k * 64 + lane) * E;
-        if (a.y != nullptr && j0 < cols) {
+        const int j0 = (k * 64 + lane) * E;
+        if (a.y != nullptr && j0 < icols) {
           float o[E];
 #pragma unroll
           for (int e = 0; e < E; ++e) o[e] = v[r][k][e] * inv;  // 0 at the cross-entropy's target
@@ -247,15 +251,24 @@ __global__ __launch_bounds__(kThreads) void k_wave(RowArgs a) {
 
 template <int DT, int E, int VPT, int RPW, int EPI>
 hipError_t launch_vpt(const RowArgs& a, hipStream_t stream) {
+  // slices of at most 2^20 workgroups, so a launch's work-items stay below 2^32
+  constexpr int64_t kMaxBlocks = (int64_t)1 << 20;
   const int64_t rows_per_block = (int64_t)kWaves * RPW;
   const int64_t blocks = (a.rows + rows_per_block - 1) / rows_per_block;
-  if (blocks > (int64_t)INT32_MAX) return hipErrorInvalidValue;
-  if (a.mask.kind == kMaskKeep) {
-    hipLaunchKernelGGL((k_wave<DT, E, VPT, RPW, true, EPI>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
-  } else {
-    hipLaunchKernelGGL((k_wave<DT, E, VPT, RPW, false, EPI>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+  for (int64_t b0 = 0; b0 < blocks; b0 += kMaxBlocks) {
+    const dim3 grid((unsigned)(blocks - b0 < kMaxBlocks ? blocks - b0 : kMaxBlocks));
+    const int64_t rbase = b0 * rows_per_block;
+    if (a.mask.kind == kMaskKeep) {
+      hipLaunchKernelGGL((k_wave<DT, E, VPT, RPW, kMaskKeep, EPI>), grid, dim3(kThreads), 0, stream, a, rbase);
+    } else if (a.mask.kind == kMaskNone) {
+      hipLaunchKernelGGL((k_wave<DT, E, VPT, RPW, kMaskNone, EPI>), grid, dim3(kThreads), 0, stream, a, rbase);
+    } else {
+      hipLaunchKernelGGL((k_wave<DT, E, VPT, RPW, kMaskValidLen, EPI>), grid, dim3(kThreads), 0, stream, a, rbase);
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 // the smallest register budget that holds the row; short rows go several to

@@ -188,7 +188,11 @@ __device__ __forceinline__ int64_t valid_prefix(const MaskArgs& mk, int64_t r, i
   if (mk.kind == kMaskValidLen) {
     v = mk.valid_len[r];
   } else if (mk.kind == kMaskCausal) {
-    v = r % mk.period + 1 + mk.offset;
+    // r % period: a short 32-bit sequence when both fit, else the 64-bit one
+    const int64_t q = (((uint64_t)r | (uint64_t)mk.period) >> 32) != 0
+                          ? r % mk.period
+                          : (int64_t)((uint32_t)r % (uint32_t)mk.period);
+    v = q + 1 + mk.offset;
   }
   return v < 0 ? 0 : (v > cols ? cols : v);
 }

@@ -240,6 +240,54 @@ def test_beyond_2_31_elements():
             check_weighted(got, "bf16", ref, st_w, scale, f"2^31+ weighted group {gi} row {r}")
 
 
+def test_row_slices_past_2_20_workgroups():
+    """Launches split into slices of at most 2^20 workgroups: a causal mask's
+    row index and the NaN policy must carry across the slice boundary.
+    (1) 2^24 + 37 one-lane fp32 rows on the wave path (16 rows per
+    workgroup: 2^20 + 3 workgroups, two slices); causal period 5, offset -1
+    leaves rows r = 0 (mod 5) empty and every other row one valid lane, so
+    every output is +0.0 or exactly 1.0 (the one-valid-lane special case),
+    NaN rows aside. (2) 2^20 + 300 causal bf16 rows of 256 lanes on the LDS
+    path (two slices), sampled rows on both sides of row 2^20 held to the
+    oracle under their global row index."""
+    banner("slices: wave path, 2^24 + 37 one-lane rows")
+    rows = (1 << 24) + 37
+    b = 1 << 24  # first row of the second slice
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    x = (4.0 * torch.randn(rows, 1, device="cuda", generator=g)).contiguous()
+    nan_rows = [b - 2, b - 1, b, b + 1, b + 4, b + 5, rows - 1]  # b = 1 (mod 5): b - 1 and b + 4 are empty, their NaN masked
+    x[nan_rows, 0] = float("nan")
+    x[b + 2, 0] = float("inf")
+    y = smx.softmax_rows(x, causal_period=5, causal_offset=-1, path="wave")
+    torch.cuda.synchronize()
+    got = y.view(torch.int32).cpu().numpy().reshape(-1).view(np.uint32)
+    r = np.arange(rows)
+    want = np.where(r % 5 == 0, np.uint32(0), np.uint32(0x3F800000))
+    for q in nan_rows + [b + 2]:
+        if q % 5 != 0:
+            want[q] = 0x7FC00000
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, f"{bad.size} rows differ, first {bad[:8]}: got {got[bad[:8]]}, want {want[bad[:8]]}"
+    del x, y
+
+    banner("slices: LDS path, 2^20 + 500 causal rows")
+    rows, cols, period = (1 << 20) + 500, 256, 1000
+    b = 1 << 20  # r mod 1000 = 576 at r = b: rows b - 2 ... b + 423 keep all 256 lanes
+    x = (6.0 * torch.randn(rows, cols, device="cuda", generator=g)).to(torch.bfloat16)
+    x[b - 1, 3] = float("nan")    # valid lane: NaN row
+    x[b, 200] = float("nan")      # valid lane: NaN row
+    x[b + 1, 5] = float("inf")    # valid lane: NaN row
+    x[b + 424, 100] = float("nan")  # r mod 1000 = 0, one valid lane: the NaN is masked, p = (1, 0, ...)
+    y = smx.softmax_rows(x, causal_period=period, path="lds")
+    torch.cuda.synchronize()
+    sample = [0, 1, 999, 1000, b - 3, b - 2, b - 1, b, b + 1, b + 2, b + 424, b + 425, rows - 2, rows - 1]
+    vl = np.clip(np.array(sample) % period + 1, 0, cols).astype(np.int32)
+    xs = to_host(x[sample].contiguous(), "bf16")
+    p, cls, st = oracle.softmax_rows(xs, "bf16", W.MaskSpec("valid_len", valid_len=vl))
+    check(to_host(y[sample].contiguous(), "bf16"), "bf16", p, cls, st, "LDS slices, causal")
+    assert list(st[6:9]) == [oracle.ROW_POISON] * 3 and st[10] == oracle.ROW_OK
+
 # ---------------------------------------------------------------------------
 # Shapes, alignments, masks and paths
 # ---------------------------------------------------------------------------
