@@ -7,7 +7,10 @@ One step is one softmax_rows call over one batch of the headline workload,
 library runs on its LDS-staged workgroup-per-row kernel. The batch rotates
 through enough resident copies of x and y (>= 1 GiB in all) that every step
 streams from HBM instead of hitting the 256 MB Infinity Cache left warm by
-the previous step.
+the previous step. Each timed loop follows its W warm-up calls and, if those
+took less than 0.25 s, more untimed calls until 0.25 s has passed (the GPU's
+clocks settle after the idle gap of input generation); per_workload reports
+how many warm-up calls ran.
 
 value  = algorithmic bytes per step / mean step time, in GB/s (1e9 B/s);
          algorithmic bytes = valid input lanes read (twice on the split path),
@@ -37,6 +40,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
+# Warm-up floor: after its W warm-up steps each timed loop keeps calling until
+# this much wall time has passed, so the GPU's clocks have left the state an
+# idle gap (input generation on the host) puts them in; 20-200 calls of a
+# 23 us kernel measured 3-5 % slower than the sustained rate.
+MIN_WARMUP_S = 0.25
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores
 MALL_BYTES = 256 * 2 ** 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
@@ -106,6 +114,25 @@ def weighted_flops(w) -> int:
     r = np.arange(w.rows, dtype=np.int64)
     valid = int(np.clip(r % w.mask.causal_period + 1 + w.mask.causal_offset, 0, w.cols).sum())
     return 2 * valid * 128
+
+
+def warm_up(call, warmup: int) -> int:
+    """W untimed calls, then more until MIN_WARMUP_S has passed; returns
+    how many ran."""
+    import torch
+
+    t0 = time.perf_counter()
+    n = 0
+    for _ in range(warmup):
+        call(n)
+        n += 1
+    torch.cuda.synchronize()
+    while time.perf_counter() - t0 < MIN_WARMUP_S:
+        for _ in range(20):
+            call(n)
+            n += 1
+        torch.cuda.synchronize()
+    return n
 
 
 def make_workload(k: str):
@@ -198,9 +225,7 @@ def time_workload(w, steps: int, warmup: int, calibrate_copy: bool = False, spre
         c.copy_(x0)
         torch.cuda.synchronize()
 
-    for i in range(warmup):
-        call(i)
-    torch.cuda.synchronize()
+    warm = warm_up(call, warmup)
 
     # the timed region: K back-to-back calls, bracketed by synchronizations;
     # HIP events on the stream the kernels run on give the GPU time per launch
@@ -232,6 +257,7 @@ def time_workload(w, steps: int, warmup: int, calibrate_copy: bool = False, spre
         "bytes": nbytes,
         "copies": copies,
         "n_chunks": n_chunks,
+        "warmup_steps_run": warm,
         "ms_per_step": wall * 1e3 / steps,
         "gpu_ms_per_launch": gpu_ms,
         "launch_ms_mean": float(launch_ms.mean()),
@@ -254,9 +280,10 @@ def device_copy(w, steps: int, warmup: int):
     copies = max(1, min(64, math.ceil(2 ** 30 / (2 * nbytes))))
     xs = [x0] + [x0.clone() for _ in range(copies - 1)]
     ys = [torch.empty_like(x0) for _ in range(copies)]
-    for i in range(warmup):
+    def call(i):
         ys[i % copies].copy_(xs[i % copies])
-    torch.cuda.synchronize()
+
+    warm_up(call, warmup)
     stream = torch.cuda.current_stream()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
@@ -287,9 +314,10 @@ def decode_weighted(steps: int, warmup: int, groups: int = 256, keys: int = 3276
     vs = [torch.randn(groups, keys, d, device="cuda", generator=g).to(torch.bfloat16) for _ in range(2)]
     out = torch.empty(groups, d, dtype=torch.bfloat16, device="cuda")
     nbytes = groups * keys * 2 + groups * keys * d * 2 + groups * d * 2
-    for i in range(warmup):
+    def call(i):
         smx.softmax_weighted_rows(ss[i % 2], vs[i % 2], out)
-    torch.cuda.synchronize()
+
+    warm_up(call, warmup)
     stream = torch.cuda.current_stream()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
@@ -374,7 +402,8 @@ def main():
                  "single_launch_ms_mean": round(r["launch_ms_mean"], 5),
                  "launch_ms_p10": round(r["launch_ms_p10"], 5), "launch_ms_p90": round(r["launch_ms_p90"], 5),
                  "GBps_step": round(gbs, 1), "GBps_launch": round(kgbs, 1),
-                 "frac_of_peak": round(kgbs / HBM_PEAK_GBS, 4), "buffer_copies": r["copies"]}
+                 "frac_of_peak": round(kgbs / HBM_PEAK_GBS, 4), "buffer_copies": r["copies"],
+                 "warmup_steps_run": r["warmup_steps_run"]}
         per[k] = entry
         print(f"# {k} {w.name}: path={r['path']} {kgbs:.0f} GB/s per launch "
               f"({r['gpu_ms_per_launch'] * 1e3:.1f} us), {gbs:.0f} GB/s per step", file=sys.stderr, flush=True)
