@@ -295,6 +295,14 @@ SMX_API int softmax_backward_rows_path(const void* p, const void* g, void* dx, i
 SMX_API int64_t softmax_default_chunk_cols(int64_t rows, int64_t cols,
                                    smx_dtype dtype);
 
+/* A plain streaming copy of `bytes` bytes from x to y (device pointers, both
+ * 16-byte aligned, bytes a multiple of 16, the two ranges disjoint), with
+ * nontemporal 16-byte accesses. It is no step of the softmax: it measures the
+ * HBM rate a bare copy reaches on a footprint, the reference against which
+ * the row kernels' effective bandwidth is read. SMX_EINVAL on a bad size,
+ * alignment, NULL pointer or overlap; bytes = 0 is a no-op. */
+SMX_API int smx_stream_copy(const void* x, void* y, int64_t bytes, void* stream);
+
 /* Message for the last nonzero status on this thread ("" if none). */
 SMX_API const char* smx_last_error(void);
 

@@ -15,6 +15,7 @@ Functions keep the C names:
   softmax_cross_entropy_rows(x, t)  -> (loss, dx)
   softmax_default_chunk_cols(rows, cols, dtype)
   softmax_select_path(rows, cols, dtype)
+  stream_copy(x, y)                 (a plain copy: the bandwidth reference, no softmax step)
   smx_last_error()
 """
 from __future__ import annotations
@@ -96,6 +97,8 @@ def lib() -> C.CDLL:
         L.softmax_weighted_merge.restype = i32
         L.softmax_default_chunk_cols.argtypes = [i64, i64, i32]
         L.softmax_default_chunk_cols.restype = i64
+        L.smx_stream_copy.argtypes = [vp, vp, i64, vp]
+        L.smx_stream_copy.restype = i32
         L.smx_last_error.argtypes = []
         L.smx_last_error.restype = C.c_char_p
         _lib = L
@@ -180,6 +183,20 @@ def make_mask(rows: int, cols: int, valid_len: Optional[torch.Tensor] = None,
 
 def _mask_arg(m):
     return None if m is None else C.byref(m)
+
+
+def stream_copy(x: torch.Tensor, y: torch.Tensor, stream=None) -> torch.Tensor:
+    """smx_stream_copy: y[:] = x through the library's streaming copy (the
+    bandwidth reference; x and y contiguous device tensors of equal byte size,
+    16-byte aligned, disjoint)."""
+    nbytes = x.numel() * x.element_size()
+    if not (x.is_contiguous() and y.is_contiguous()) or y.numel() * y.element_size() != nbytes:
+        raise ValueError("x and y must be contiguous and of the same byte size")
+    if x.device.type != "cuda":
+        raise ValueError("x must be a device tensor")
+    _on(y, x.device, "y")
+    _check(lib().smx_stream_copy(x.data_ptr(), y.data_ptr(), nbytes, _stream_handle(stream, x.device)))
+    return y
 
 
 def softmax_rows(x: torch.Tensor, out: Optional[torch.Tensor] = None, *, valid_len=None,

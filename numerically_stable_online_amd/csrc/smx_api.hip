@@ -486,6 +486,17 @@ int softmax_weighted_merge(const float* ml, const float* o, int64_t rows, int64_
   return ok();
 }
 
+int smx_stream_copy(const void* x, void* y, int64_t bytes, void* stream) {
+  if (bytes < 0 || bytes % 16 != 0) return fail(SMX_EINVAL, "bytes (%lld) must be a non-negative multiple of 16", (long long)bytes);
+  if (bytes == 0) return ok();
+  if (x == nullptr || y == nullptr) return fail(SMX_EINVAL, "x and y must not be NULL");
+  if ((uintptr_t)x % 16 != 0 || (uintptr_t)y % 16 != 0) return fail(SMX_EINVAL, "x and y must be 16-byte aligned");
+  if (overlaps(x, (uintptr_t)bytes, y, (uintptr_t)bytes)) return fail(SMX_EINVAL, "x and y overlap");
+  const hipError_t err = launch_stream_copy(x, y, bytes / 16, (hipStream_t)stream);
+  if (err != hipSuccess) return hip_fail(err, "kernel launch");
+  return ok();
+}
+
 const char* smx_last_error(void) { return g_err; }
 
 }  // extern "C"

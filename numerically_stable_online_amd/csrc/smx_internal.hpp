@@ -105,4 +105,8 @@ bool pv_supported_d(int64_t d);
 hipError_t launch_pv(const char* s, const char* v, char* out, int64_t rows, int64_t cols, int64_t d,
                      int64_t rows_per_group, int dtype, const MaskArgs& mask, hipStream_t stream);
 
+// --- the streaming copy used as a bandwidth reference (k_copy.hip) ---
+// n16 16-byte packs from x to y; both 16-byte aligned, not overlapping
+hipError_t launch_stream_copy(const void* x, void* y, int64_t n16, hipStream_t stream);
+
 }  // namespace smx

@@ -103,6 +103,28 @@ def test_argument_checks_need_no_device(smx):
     assert "n_chunks" in smx.smx_last_error()
 
 
+def test_stream_copy_argument_checks(smx):
+    """The bandwidth reference copy rejects bad sizes, NULL, misaligned and
+    overlapping buffers before any launch (the pointers here are never
+    dereferenced)."""
+    L = smx.lib()
+    EINVAL = smx.SMX_EINVAL
+    cases = [
+        ((4096, 1 << 20, -16, None), "bytes"),
+        ((4096, 1 << 20, 24, None), "bytes"),
+        ((None, 1 << 20, 64, None), "NULL"),
+        ((4096, None, 64, None), "NULL"),
+        ((4104, 1 << 20, 64, None), "aligned"),
+        ((4096, 1 << 20 | 8, 64, None), "aligned"),
+        ((4096, 4096 + 32, 64, None), "overlap"),
+        ((4096, 4096, 64, None), "overlap"),
+    ]
+    for args, word in cases:
+        assert L.smx_stream_copy(*args) == EINVAL, word
+        assert word in smx.smx_last_error(), (word, smx.smx_last_error())
+    assert L.smx_stream_copy(None, None, 0, None) == smx.SMX_OK
+
+
 def test_weighted_rows_argument_checks(smx):
     L = smx.lib()
     EINVAL = smx.SMX_EINVAL

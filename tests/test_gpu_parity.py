@@ -288,6 +288,31 @@ def test_row_slices_past_2_20_workgroups():
     check(to_host(y[sample].contiguous(), "bf16"), "bf16", p, cls, st, "LDS slices, causal")
     assert list(st[6:9]) == [oracle.ROW_POISON] * 3 and st[10] == oracle.ROW_OK
 
+def test_stream_copy_is_exact():
+    """The bandwidth reference copy moves every byte: sizes from one 16-byte
+    pack through ragged multiples to the headline footprint, on the default
+    and on a separate stream."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(11)
+    for nbytes in (16, 48, 4096 + 16, 1 << 20, (1 << 26) + 4080, 8192 * 4096 * 2):
+        banner(f"stream copy {nbytes} B")
+        x = torch.randint(-2 ** 31, 2 ** 31 - 1, (nbytes // 4,), dtype=torch.int32, device="cuda", generator=g)
+        y = torch.full_like(x, 0x5A5A5A5A)
+        guard = torch.full((1024,), 0x3C3C3C3C, dtype=torch.int32, device="cuda")
+        yy = torch.cat([y, guard])  # a guard zone after y: the copy writes nothing past its bytes
+        smx.stream_copy(x, yy[:x.numel()])
+        torch.cuda.synchronize()
+        assert torch.equal(yy[:x.numel()], x)
+        assert torch.equal(yy[x.numel():], guard)
+    s = torch.cuda.Stream()
+    x = torch.arange(1 << 20, dtype=torch.int32, device="cuda")
+    y = torch.empty_like(x)
+    with torch.cuda.stream(s):
+        smx.stream_copy(x, y)
+    s.synchronize()
+    assert torch.equal(x, y)
+
+
 # ---------------------------------------------------------------------------
 # Shapes, alignments, masks and paths
 # ---------------------------------------------------------------------------
