@@ -1,7 +1,7 @@
 /*
  * abi_from_c.c — drives the library through include/smx.h from plain C, the
  * way a caller with no Python would: device buffers from hipMalloc, one
- * non-default stream, every entry point once, results copied back.
+ * non-default stream, every entry point, results copied back.
  *
  * usage: abi_from_c <inputs.bin> <outputs.bin>
  *
@@ -25,8 +25,11 @@
  *   uint16 o[wrows*d]            softmax_weighted_rows(s, v), causal per group
  *   uint16 o2[wrows*d]           softmax_weighted_states (chunks of 64 keys) +
  *                                softmax_weighted_merge, the same sums
- * Exit status 0 only if every call returned SMX_OK and an invalid call was
- * rejected with SMX_EINVAL and a message.
+ * The _path variants (with SMX_PATH_AUTO) are checked here to equal their
+ * plain calls bit for bit, smx_stream_copy to reproduce its input exactly,
+ * and the two host helpers to return a path and a chunk width.
+ * Exit status 0 only if every call returned SMX_OK, every check held and an
+ * invalid call was rejected with SMX_EINVAL and a message.
  */
 #include <hip/hip_runtime_api.h>
 #include <stdio.h>
@@ -72,6 +75,23 @@ static void* device_buffer(size_t bytes) {
   void* d = NULL;
   hip_check(hipMalloc(&d, bytes ? bytes : 16), "hipMalloc");
   return d;
+}
+
+/* the device buffers a and b hold the same bytes */
+static void same_bytes(const void* a, const void* b, size_t bytes, const char* what) {
+  unsigned char* ha = (unsigned char*)malloc(bytes ? bytes : 1);
+  unsigned char* hb = (unsigned char*)malloc(bytes ? bytes : 1);
+  if (ha == NULL || hb == NULL) die("out of host memory");
+  if (bytes) {
+    hip_check(hipMemcpy(ha, a, bytes, hipMemcpyDeviceToHost), "hipMemcpy to host");
+    hip_check(hipMemcpy(hb, b, bytes, hipMemcpyDeviceToHost), "hipMemcpy to host");
+  }
+  if (memcmp(ha, hb, bytes) != 0) {
+    fprintf(stderr, "abi_from_c: %s differ\n", what);
+    exit(1);
+  }
+  free(ha);
+  free(hb);
 }
 
 static void write_back(FILE* f, const void* d, size_t bytes) {
@@ -149,6 +169,36 @@ int main(int argc, char** argv) {
             "softmax_weighted_states");
   smx_check(softmax_weighted_merge(wml, wo, wrows, wnch, d, SMX_BF16, o2, st), "softmax_weighted_merge");
 
+  /* the _path variants with the automatic path: the same dispatch, bit for bit */
+  void* ya = device_buffer(n * 4);
+  void* logpa = device_buffer(n * 2);
+  float* lsea = (float*)device_buffer((size_t)rows * 4);
+  float* lossa = (float*)device_buffer((size_t)rows * 4);
+  void* dxba = device_buffer(n * 2);
+  void* dxa = device_buffer(n * 4);
+  smx_check(softmax_rows_path(x, ya, rows, cols, SMX_F32, &by_len, SMX_PATH_AUTO, 0, st), "softmax_rows_path");
+  smx_check(log_softmax_rows_path(xb, logpa, lsea, rows, cols, SMX_BF16, &by_len, SMX_PATH_AUTO, 0, st),
+            "log_softmax_rows_path");
+  smx_check(softmax_cross_entropy_rows_path(xb, tgt, lossa, dxba, rows, cols, SMX_BF16, NULL, SMX_PATH_AUTO, 0, st),
+            "softmax_cross_entropy_rows_path");
+  smx_check(softmax_backward_rows_path(y, g, dxa, rows, cols, SMX_F32, SMX_PATH_AUTO, 0, st),
+            "softmax_backward_rows_path");
+  /* the streaming copy (the bandwidth reference) of the bf16 logits' whole 16-byte packs */
+  const size_t cbytes = (n * 2) / 16 * 16;
+  void* xc = device_buffer(n * 2);
+  smx_check(smx_stream_copy(xb, xc, (int64_t)cbytes, st), "smx_stream_copy");
+  const smx_path pth = softmax_select_path(rows, cols, SMX_F32);
+  if (pth != SMX_PATH_WAVE && pth != SMX_PATH_LDS && pth != SMX_PATH_SPLIT) die("softmax_select_path");
+  if (softmax_default_chunk_cols(rows, cols, SMX_F32) <= 0) die("softmax_default_chunk_cols");
+  hip_check(hipStreamSynchronize(st), "hipStreamSynchronize");
+  same_bytes(y, ya, n * 4, "softmax_rows and softmax_rows_path");
+  same_bytes(logp, logpa, n * 2, "log_softmax_rows and log_softmax_rows_path (y)");
+  same_bytes(lse, lsea, (size_t)rows * 4, "log_softmax_rows and log_softmax_rows_path (lse)");
+  same_bytes(loss, lossa, (size_t)rows * 4, "the cross-entropy losses");
+  same_bytes(dxb, dxba, n * 2, "the cross-entropy gradients");
+  same_bytes(dx, dxa, n * 4, "softmax_backward_rows and softmax_backward_rows_path");
+  same_bytes(xb, xc, cbytes, "smx_stream_copy's input and output");
+
   /* an invalid element type is rejected before anything is enqueued */
   const int bad = softmax_rows(x, y, rows, cols, (smx_dtype)7, NULL, st);
   if (bad != SMX_EINVAL || smx_last_error()[0] == '\0') die("an invalid dtype was not rejected");
@@ -168,7 +218,8 @@ int main(int argc, char** argv) {
   write_back(out, o2, (size_t)(wrows * d) * 2);
   fclose(out);
   hip_check(hipStreamDestroy(st), "hipStreamDestroy");
-  void* bufs[] = {x, vl, xb, tgt, g, s, v, y, y2, stats, logp, lse, loss, dxb, dx, o, wml, wo, o2};
+  void* bufs[] = {x, vl, xb, tgt, g, s, v, y, y2, stats, logp, lse, loss, dxb, dx, o, wml, wo, o2,
+                  ya, logpa, lsea, lossa, dxba, dxa, xc};
   for (size_t i = 0; i < sizeof bufs / sizeof bufs[0]; ++i) hip_check(hipFree(bufs[i]), "hipFree");
   free(h_x);
   free(h_vl);
