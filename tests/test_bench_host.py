@@ -2,7 +2,8 @@
 message, and its byte and flop accounting reproduces the totals worked out
 by hand for the workloads (a read of the valid lanes, a write of whole rows,
 a second read and the chunk summaries on the split path, 4 bytes of mask per
-row for valid lengths; 2 flops per valid weight and value component)."""
+row for valid lengths; 2 flops per valid weight and value component), and its
+warm-up runs W calls and then fills a time floor."""
 import os
 import subprocess
 import sys
@@ -52,3 +53,34 @@ def test_weighted_flops_of_the_attention_workload():
     # 2 flops x 128 components x the valid weights, 256 x (1 + 2 + ... + 2048)
     assert bench.weighted_flops(_w(524_288, 2048, "bf16", causal)) == 2 * 128 * 256 * (2048 * 2049 // 2)
     assert bench.weighted_flops(_w(524_288, 2048, "bf16", causal)) == 137_506_062_336
+
+
+def test_warm_up_runs_w_calls_then_fills_the_time_floor(monkeypatch):
+    """warm_up makes its W calls, then keeps calling (20 at a time, each
+    batch ended by a device sync) until MIN_WARMUP_S has passed, and returns
+    the number of calls; slow calls end it right after the W."""
+    import torch
+
+    syncs = []
+    monkeypatch.setattr(torch.cuda, "synchronize", lambda *a, **k: syncs.append(1))
+    clock = [0.0]
+    monkeypatch.setattr(bench.time, "perf_counter", lambda: clock[0])
+    seen = []
+
+    def fast(i):
+        seen.append(i)
+        clock[0] += 0.001  # 1 ms a call: the floor needs 250 of them
+
+    n = bench.warm_up(fast, 7)
+    assert n == len(seen) and seen == list(range(n))
+    assert n >= 250 and (n - 7) % 20 == 0 and n - 20 < 250
+    assert len(syncs) == 1 + (n - 7) // 20
+
+    seen.clear()
+    clock[0] = 0.0
+
+    def slow(i):
+        seen.append(i)
+        clock[0] += 0.1  # 100 ms a call: W = 3 already passes the floor
+
+    assert bench.warm_up(slow, 3) == 3 and seen == [0, 1, 2]
