@@ -457,30 +457,55 @@ def _tree_shapes(items):
                 yield oracle.merge(*a, *b)
 
 
+def _brute_force_rows(n, rows):
+    """For every row: the chunk summary of the whole row against the
+    definition, then every contiguous split, every merge order of up to four
+    chunks as a left fold (one order beyond), and every bracketing of the
+    chunks, each held to the three-pass summary. Returns the folds checked."""
+    checked = 0
+    for row in rows:
+        x = np.array([row], dtype=np.float32)
+        M, L = oracle.chunk_stats(x, "f32", n)
+        M, L = M[0, 0], L[0, 0]
+        finite = [v for v in row if v != -np.inf]
+        if not finite:
+            assert (M, L) == (-np.inf, 0.0)
+        else:
+            assert M == max(finite) and 1.0 <= L <= len(finite)
+        for cuts in itertools.product((0, 1), repeat=n - 1):
+            bounds = [0] + [i + 1 for i, c in enumerate(cuts) if c] + [n]
+            stats = [_segment_stats(row, a, b) for a, b in zip(bounds[:-1], bounds[1:])]
+            orders = itertools.permutations(stats) if len(stats) <= 4 else [stats]
+            for perm in orders:
+                m, l = _fold(perm)
+                assert m == M
+                assert abs(l - L) <= 8 * n * 2.0 ** -53 * max(L, 1.0)
+                checked += 1
+            for m, l in _tree_shapes(stats):
+                assert m == M and abs(l - L) <= 8 * n * 2.0 ** -53 * max(L, 1.0)
+    return checked
+
+
 def test_brute_force_every_split_and_merge_order():
     checked = 0
     for n in range(1, 5):
-        for row in itertools.product(VALUE_SET, repeat=n):
-            x = np.array([row], dtype=np.float32)
-            M, L = oracle.chunk_stats(x, "f32", n)
-            M, L = M[0, 0], L[0, 0]
-            finite = [v for v in row if v != -np.inf]
-            if not finite:
-                assert (M, L) == (-np.inf, 0.0)
-            else:
-                assert M == max(finite) and 1.0 <= L <= len(finite)
-            for cuts in itertools.product((0, 1), repeat=n - 1):
-                bounds = [0] + [i + 1 for i, c in enumerate(cuts) if c] + [n]
-                stats = [_segment_stats(row, a, b) for a, b in zip(bounds[:-1], bounds[1:])]
-                orders = itertools.permutations(stats) if len(stats) <= 4 else [stats]
-                for perm in orders:
-                    m, l = _fold(perm)
-                    assert m == M
-                    assert abs(l - L) <= 8 * n * 2.0 ** -53 * max(L, 1.0)
-                    checked += 1
-                for m, l in _tree_shapes(stats):
-                    assert m == M and abs(l - L) <= 8 * n * 2.0 ** -53 * max(L, 1.0)
+        checked += _brute_force_rows(n, itertools.product(VALUE_SET, repeat=n))
     assert checked > 100000
+
+
+@pytest.mark.slow
+def test_brute_force_rows_of_five_exhaustive():
+    """The slow tier: every row of five values from the set."""
+    assert _brute_force_rows(5, itertools.product(VALUE_SET, repeat=5)) > 1000000
+
+
+@pytest.mark.slow
+def test_brute_force_rows_of_six_sampled():
+    """The slow tier at length six: 3000 seeded rows of the set (the full
+    8^6 rows would take the better part of an hour here)."""
+    rng = np.random.default_rng(66)
+    rows = [tuple(VALUE_SET[i] for i in rng.integers(0, len(VALUE_SET), 6)) for _ in range(3000)]
+    assert _brute_force_rows(6, rows) > 100000
 
 
 def test_split_path_oracle_equals_three_pass():
