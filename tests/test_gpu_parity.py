@@ -339,6 +339,27 @@ def _paths(dtype, cols, misalign):
     return paths
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_large_maxima_switch_the_exponential(dtype):
+    """16-bit rows whose maximum reaches 2^15 in magnitude: the wave and LDS
+    kernels fold the row's shift into one constant below that and subtract it
+    explicitly at and above it; both sides of the switch, and rows around
+    +-40000, on every path, held to the oracle."""
+    rng = np.random.default_rng(77)
+    rows, cols = 12, 1024
+    a = np.empty((rows, cols))
+    a[0::4] = 40000.0 + 100.0 * rng.standard_normal((3, cols))
+    a[1::4] = -40000.0 + 100.0 * rng.standard_normal((3, cols))
+    a[2::4] = 32768.0 - 16.0 * rng.integers(0, 4, (3, cols))  # maximum 2^15: explicit subtraction
+    a[3::4] = 32752.0 - 16.0 * rng.integers(0, 4, (3, cols))  # maximum below 2^15 (f16): one constant
+    x = W.to_format(a, dtype)
+    p, cls, st = oracle.softmax_rows(x, dtype, W.MaskSpec())
+    for path in ("wave", "lds", "split"):
+        banner(f"{dtype} large maxima path={path}")
+        y = run_rows(x, dtype, W.MaskSpec(), path=path, chunk_cols=256 if path == "split" else 0)
+        check(y, dtype, p, cls, st, f"{dtype} large maxima path={path}")
+
+
 @pytest.mark.parametrize("dtype", W.DTYPES)
 def test_odd_shapes_masks_paths(dtype):
     rng = np.random.default_rng(100)
