@@ -68,7 +68,10 @@ __global__ __launch_bounds__(kThreads) void k_stats(RowArgs a, int64_t chunk, in
       tbad = !(xt < kInf);
     }
 
-    // one round's loads into registers
+    // one round's loads into registers. These are ordinary loads, not
+    // nontemporal ones: part of x then stays in the Infinity Cache for the
+    // normalize pass's reread (nontemporal loads here made the two passes
+    // 12-14 % slower end to end)
     auto fetch = [&](int64_t base, Pack<DT, E>(&p)[VPT], uint64_t(&kb)[VPT]) {
 #pragma unroll
       for (int k = 0; k < VPT; ++k) {
