@@ -150,9 +150,11 @@ SMX_API int softmax_row_stats(const void* x, int64_t rows, int64_t cols,
  *   stats: device [rows][n_chunks], as written by softmax_row_stats or by the
  *          caller (e.g. summaries exchanged between devices);
  *   n_chunks must equal ceil(cols / chunk_cols).
- * Every chunk's workgroup merges all n_chunks summaries of its row itself
- * (no workspace), so its summary reads grow as n_chunks squared: prefer
- * chunks large enough to keep n_chunks to about a thousand or fewer. */
+ * Up to 1024 chunks per row, every chunk's workgroup merges its row's
+ * summaries itself (no workspace). Beyond that each row's summaries are first
+ * merged once, bitwise as the workgroups would merge them, into a
+ * stream-ordered workspace of rows * 8 bytes, so the summary reads grow
+ * linearly with n_chunks. */
 SMX_API int softmax_merge_normalize(const void* x, void* y, int64_t rows, int64_t cols,
                             smx_dtype dtype, const smx_mask* valid_len_or_mask,
                             int64_t chunk_cols, const smx_stat* stats,
@@ -226,7 +228,9 @@ SMX_API int softmax_cross_entropy_rows_path(const void* x, const int32_t* target
  * exactly; products accumulate in fp32. Groups of at most 4 rows (or of at
  * most 8 when there are fewer than 256 groups) take the key split of
  * softmax_weighted_states and softmax_weighted_merge instead (fp32 on the
- * vector ALUs), with a stream-ordered workspace.
+ * vector ALUs), with a stream-ordered workspace; its key chunk grows (up to
+ * 2048 keys) until a row has at most 16384 chunk states, and rows of more
+ * than 2^25 keys stay on the matrix cores.
  * Policy: a poisoned row (+inf/NaN in a valid lane) gives the canonical NaN
  * in every component; an empty or fully masked row gives zeros. SMX_F32,
  * other widths, misalignment and overlap are SMX_EINVAL; rows = 0 is a

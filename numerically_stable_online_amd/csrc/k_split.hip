@@ -248,9 +248,12 @@ __global__ __launch_bounds__(kThreads) void k_merge_normalize(RowArgs a, int64_t
     const float at_t = (0.0f - others) / l;  // cross-entropy target lane: -(others / L)
 
     for (int64_t base = j_lo; base < j_hi; base += kRound) {
-      // cross-entropy: the target's place in this round's registers (-1: not here)
-      const int slot = EPI == kEpiXent ? target_slot<kThreads, E>(t >= base && t - base < kRound ? t - base : -1, tid)
-                                       : -1;
+      // cross-entropy: the target's place in this round's registers (-1: not
+      // here). A round may reach past the chunk (chunk < kRound), so the target
+      // must also lie inside this chunk: its lane belongs to one workgroup only
+      const int slot = EPI == kEpiXent
+                           ? target_slot<kThreads, E>(t >= base && t < j_hi && t - base < kRound ? t - base : -1, tid)
+                           : -1;
       Pack<DT, E> in[VPT];
       uint64_t kb[VPT];
 #pragma unroll

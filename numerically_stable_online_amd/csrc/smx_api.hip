@@ -208,11 +208,16 @@ bool weighted_split(int64_t rows_per_group, int64_t groups) {
 }
 
 // the key chunk of that path: 512, halved (down to 128) while the grid has
-// fewer than 2048 workgroups
+// fewer than 2048 workgroups, doubled (up to kMaxWChunk) while a row would
+// leave more chunk states than one merge folds (kMaxWMergeChunks: their
+// factors sit in LDS); 0 when even the longest chunk leaves too many, and
+// those rows (more than kMaxWChunk * kMaxWMergeChunks = 2^25 keys) take the
+// matrix-core kernel instead
 int64_t weighted_split_chunk(int64_t groups, int64_t cols) {
   int64_t chunk = 512;
   while (chunk > 128 && groups * ((cols + chunk - 1) / chunk) < 2048) chunk /= 2;
-  return chunk;
+  while (chunk < kMaxWChunk && (cols + chunk - 1) / chunk > kMaxWMergeChunks) chunk *= 2;
+  return (cols + chunk - 1) / chunk > kMaxWMergeChunks ? 0 : chunk;
 }
 
 }  // namespace
@@ -275,9 +280,24 @@ int softmax_merge_normalize(const void* x, void* y, int64_t rows, int64_t cols, 
   if (rows > 0 && nch > 0 && stats == nullptr) return fail(SMX_EINVAL, "stats is NULL");
   if (rows == 0 || cols == 0) return ok();
   const bool vec = c.vec && chunk_cols % vec_elems(c.dtype) == 0;
-  hipError_t err = launch_merge_normalize(c.a, c.dtype, vec, kEpiSoftmax, chunk_cols, nch, stats, nch,
-                                         (hipStream_t)stream);
+  const hipStream_t st = (hipStream_t)stream;
+  if (nch <= kRowMergeMinChunks) {
+    const hipError_t err = launch_merge_normalize(c.a, c.dtype, vec, kEpiSoftmax, chunk_cols, nch, stats, nch, st);
+    if (err != hipSuccess) return hip_fail(err, "merge/normalize launch");
+    return ok();
+  }
+  // many chunks per row: each row's summaries are merged once (8 bytes per
+  // row in a stream-ordered workspace), bitwise as every chunk's workgroup
+  // would merge them, so the summary reads grow linearly with n_chunks
+  void* ws = nullptr;
+  hipError_t err = hipMallocAsync(&ws, (size_t)rows * sizeof(smx_stat), st);
+  if (err != hipSuccess) return hip_fail(err, "hipMallocAsync of the merged summaries");
+  smx_stat* const merged = (smx_stat*)ws;
+  err = launch_row_merge(stats, rows, nch, merged, st);
+  if (err == hipSuccess) err = launch_merge_normalize(c.a, c.dtype, vec, kEpiSoftmax, chunk_cols, nch, merged, 1, st);
+  const hipError_t ferr = hipFreeAsync(ws, st);
   if (err != hipSuccess) return hip_fail(err, "merge/normalize launch");
+  if (ferr != hipSuccess) return hip_fail(ferr, "hipFreeAsync of the merged summaries");
   return ok();
 }
 
@@ -414,14 +434,14 @@ int softmax_weighted_rows(const void* s, const void* v, void* out, int64_t rows,
   if (overlaps(out, ob, s, (uintptr_t)(rows * cols * 2)) || overlaps(out, ob, v, (uintptr_t)(groups * cols * d * 2)))
     return fail(SMX_EINVAL, "out overlaps s or v");
   const hipStream_t st = (hipStream_t)stream;
-  if (!weighted_split(rows_per_group, groups) || cols == 0) {
+  const int64_t chunk = weighted_split(rows_per_group, groups) ? weighted_split_chunk(groups, cols) : 0;
+  if (chunk == 0 || cols == 0) {
     const hipError_t err = launch_pv((const char*)s, (const char*)v, (char*)out, rows, cols, d, rows_per_group,
                                      c.dtype, c.a.mask, st);
     if (err != hipSuccess) return hip_fail(err, "kernel launch");
     return ok();
   }
   // few rows per group: per-chunk states in a stream-ordered workspace, merged
-  const int64_t chunk = weighted_split_chunk(groups, cols);
   const int64_t nch = (cols + chunk - 1) / chunk;
   const size_t ml_bytes = (size_t)(rows * nch) * 2 * sizeof(float);
   const size_t bytes = ml_bytes + (size_t)(rows * nch * d) * sizeof(float);

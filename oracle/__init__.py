@@ -330,12 +330,19 @@ def encode(p: np.ndarray, dtype: str) -> np.ndarray:
     return out
 
 
-def softmax_rows_encode_mt(x: np.ndarray, dtype: str, mask=None, threads: int = 1):
+def softmax_rows_encode_mt(x: np.ndarray, dtype: str, mask=None, threads: int = 1,
+                           out: Optional[np.ndarray] = None):
     """The CPU baseline: three-pass rows over `threads` host threads, written in
-    the element format. Returns (y, seconds)."""
+    the element format (into `out` when given: raw storage of x's shape).
+    Returns (y, seconds)."""
     x = _raw(x, dtype)
     rows, cols = x.shape
-    y = np.empty_like(x)
+    if out is not None:
+        if out.shape != x.shape or out.dtype != x.dtype or not out.flags.c_contiguous:
+            raise ValueError("out must be contiguous raw storage of x's shape")
+        y = out
+    else:
+        y = np.empty_like(x)
     ms, keep = _mask_struct(mask, rows, cols)
     t0 = time.perf_counter()
     rc = lib().oracle_softmax_rows_encode_mt(_ptr(x), _ptr(y), DTYPE_CODE[dtype], rows, cols,

@@ -164,13 +164,16 @@ def test_very_long_rows_split():
 
 def test_row_merge_matches_direct_merge():
     """Beyond 1024 chunks per row the split path merges each row's summaries
-    once before normalizing. Its output is bitwise the one the normalize pass
-    gives when each of its workgroups merges every summary itself (the
-    public softmax_row_stats + softmax_merge_normalize pair), and it meets
-    the oracle; log-softmax, cross-entropy and the backward take the same
-    two-level merge and meet the oracle too. Rows: full, a valid length
-    ending inside a chunk, empty, and NaN in a valid lane."""
-    rows, cols, chunk = 4, 1 << 22, 2048  # 2048 chunks per row
+    once before normalizing, and so does the public softmax_row_stats +
+    softmax_merge_normalize pair (its summary reads then grow linearly with
+    the chunk count): at 4096 chunks per row the pair is bitwise
+    softmax_rows on the split path, and both meet the oracle; at 1024 chunks
+    (every workgroup merging all of its row's summaries) and 1025 (merged
+    once per row first) the pair meets the oracle too. Log-softmax,
+    cross-entropy and the backward take the same two-level merge and meet
+    the oracle. Rows: full, a valid length ending inside a chunk, empty, and
+    NaN in a valid lane."""
+    rows, cols, chunk = 4, 1 << 22, 1024  # 4096 chunks per row
     x = W.random_rows(rows, cols, "f32", seed=91, scale=5.0)
     x[3, 777_777] = np.float32("nan")
     vl = np.array([cols, cols - 1000, 0, cols], dtype=np.int32)
@@ -184,6 +187,12 @@ def test_row_merge_matches_direct_merge():
     torch.cuda.synchronize()
     assert _same_bits(y_two, y_direct)
     check_full(x, "f32", mask, to_host(y_two, "f32"), "row merge softmax")
+    for ch in (cols // 1024, -(-cols // 1025)):  # 1024 and 1025 chunks per row
+        banner(f"public stats + merge, {-(-cols // ch)} chunks per row")
+        st = smx.softmax_row_stats(xd, ch, **kw)
+        y_pub = smx.softmax_merge_normalize(xd, st, ch, **kw)
+        torch.cuda.synchronize()
+        check_full(x, "f32", mask, to_host(y_pub, "f32"), f"public merge {ch}")
     banner("row merge: log-softmax")
     y, lse = run_log(x, "f32", mask, path="split", chunk_cols=chunk)
     check_log_full(x, "f32", mask, y, lse, "row merge log-softmax")
@@ -943,6 +952,25 @@ def test_cross_entropy_confident_and_policy(dtype):
                 check_xent_full(x, dtype, t, mask, loss, dx, what)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_cross_entropy_split_chunks_narrower_than_a_round(dtype):
+    """Split path with chunks far narrower than one register round of the
+    normalize pass: each target's gradient is written by the workgroup of
+    its own chunk (a round reaching into the next chunk must not write it),
+    targets in late chunks included; guard zones around dx stay untouched."""
+    rows, cols, chunk = 6, 5000, 100
+    x_raw = W.random_rows(rows, cols, dtype, seed=31, scale=5.0)
+    t = np.array([0, 150, 199, 4999, 2531, 100], dtype=np.int32)
+    guard = 4096
+    buf = torch.full((rows * cols + 2 * guard,), 77.0, dtype=TORCH_DTYPE[dtype], device="cuda")
+    dx = buf[guard:guard + rows * cols].view(rows, cols)
+    x = to_device(x_raw, dtype)
+    loss, _ = smx.softmax_cross_entropy_rows(x, torch.from_numpy(t).cuda(), dx=dx, path="split", chunk_cols=chunk)
+    torch.cuda.synchronize()
+    assert bool((buf[:guard] == 77.0).all()) and bool((buf[-guard:] == 77.0).all())
+    check_xent_full(x_raw, dtype, t, None, loss.cpu().numpy(), to_host(dx, dtype), f"xent narrow chunks {dtype}")
+
+
 def test_cross_entropy_in_place():
     w = W.long_rows(rows=4, cols=1 << 16)
     t = xent_targets(4, 1 << 16, seed=9)
@@ -1116,6 +1144,22 @@ def test_weighted_rows_few_rows_per_group(dtype):
     vc = np.broadcast_to(c, (2, 512, 64)).copy()
     out = run_weighted(s, vc, dtype)
     assert np.array_equal(out, np.broadcast_to(c, (6, 64))), f"weighted split constant {dtype}"
+
+
+def test_weighted_rows_key_split_past_its_merge_width():
+    """One row per group over 8,388,616 keys: at the key split's usual
+    512-key chunk a row would leave 16,385 states, one more than the merge
+    folds, so the chunk grows (to 1024 keys) and the sums still match the
+    oracle."""
+    rng = np.random.default_rng(515)
+    dtype, groups, cols, d = "bf16", 2, 8_388_616, 32
+    s = W.to_format(3.0 * rng.standard_normal((groups, cols), dtype=np.float32), dtype)
+    v = W.to_format(rng.standard_normal((groups, cols, d), dtype=np.float32), dtype)
+    mask = W.MaskSpec("none")
+    banner(f"weighted key split {groups} x {cols} d={d}")
+    out = run_weighted(s, v, dtype, mask)
+    ref, st, scale = weighted_reference(s, v, dtype, 1, mask)
+    check_weighted(out, dtype, ref, st, scale, "weighted key split past its merge width")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])

@@ -619,3 +619,42 @@ def test_cross_entropy_policy():
     assert np.isnan(loss[2]) and np.isnan(dx[2]).all()  # poisoned
     assert loss[3] == np.inf and dx[3, 3] == -1.0 and abs(dx[3].sum() + 0.0) <= 1e-15  # masked target
     assert loss[4] == np.inf and list(dx[4]) == [0.0, -1.0, 0.0, 0.0]  # empty row
+
+
+# ---------------------------------------------------------------------------
+# The CPU-baseline routine: the same rows, encoded, over host threads
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", W.DTYPES)
+def test_cpu_baseline_routine_equals_rows_then_encode(dtype):
+    """oracle_softmax_rows_encode_mt (what the benchmark's CPU baseline times)
+    must write exactly the bytes of the three-pass rows rounded by
+    oracle_encode, whatever the thread count (including counts that do not
+    divide the rows, one thread per row, and more threads than rows), under
+    every mask kind and with policy rows present. The output buffer starts
+    filled with a byte pattern that is no encoding of any result, so a row
+    the routine skipped, or wrote at another row's offset, cannot match."""
+    rng = np.random.default_rng(78)
+    rows, cols = 37, 203
+    x = W.to_format(12.0 * rng.standard_normal((rows, cols)), dtype)
+    inf = W.POS_INF[dtype].view(np.uint32) if dtype == "f32" else W.POS_INF[dtype]
+    W.set_bits(x, 3, 10, dtype, inf)                   # +inf in a (mostly) valid lane
+    W.set_bits(x, 11, 0, dtype, W.NEG_SNAN[dtype])     # NaN in lane 0 (valid under every mask)
+    x[20] = W.to_format(np.full(cols, -np.inf), dtype)  # every lane -inf
+    valid = rng.integers(0, cols + 1, rows).astype(np.int32)
+    valid[5] = 0
+    keep = (rng.random((rows, cols)) < 0.3).astype(np.uint8)
+    keep[7] = 0
+    keep[3, 10] = keep[11, 0] = 1  # the poisoned lanes stay valid
+    masks = [W.MaskSpec(), W.MaskSpec("valid_len", valid_len=valid),
+             W.MaskSpec("causal", causal_period=13, causal_offset=-2), W.MaskSpec("keep", keep=keep)]
+    for mask in masks:
+        p, cls, st = oracle.softmax_rows(x, dtype, mask)
+        want = oracle.encode(p, dtype).view(np.uint8)
+        assert (st == oracle.ROW_POISON).any() and (st == oracle.ROW_EMPTY).any(), mask.kind
+        for threads in (1, 2, 3, 16, rows, rows + 5):
+            out = np.empty_like(x)
+            out.view(np.uint8)[...] = 0xA5
+            y, dt = oracle.softmax_rows_encode_mt(x, dtype, mask, threads, out=out)
+            assert y is out and dt >= 0.0
+            assert np.array_equal(y.view(np.uint8), want), (mask.kind, threads)
