@@ -25,7 +25,7 @@
  *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL means
  *    the default stream). Results are valid once the stream has synchronized.
  *    The library never synchronizes the host and keeps no device memory
- *    between calls.
+ *    between calls, except the fixed scratch of softmax_rows_noalloc.
  *  - Return value: SMX_OK (0) or an SMX_E* code; smx_last_error() then
  *    returns a message (thread-local, valid until the next call on the same
  *    thread). Invalid arguments are rejected before anything is enqueued.
@@ -121,6 +121,33 @@ typedef enum {
 SMX_API int softmax_rows(const void* x, void* y, int64_t rows, int64_t cols,
                  smx_dtype dtype, const smx_mask* valid_len_or_mask,
                  void* stream);
+
+/* Bytes of device scratch softmax_rows_noalloc holds per device. */
+#define SMX_NOALLOC_SCRATCH_BYTES (4 * 1024 * 1024)
+
+/* softmax_rows_noalloc — softmax_rows_path for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, and
+ * harnesses that forbid allocation. It calls no allocator (no hipMalloc,
+ * hipMallocAsync or hipFree, and none through another library).
+ *  - The split path keeps its chunk summaries in a static device array of
+ *    SMX_NOALLOC_SCRATCH_BYTES bytes that the library holds on each device
+ *    it runs on until the process ends. A split-path call whose summaries
+ *    need more (rows * ceil(cols / chunk) * 8 bytes, plus rows * 8 when a
+ *    row has more than 1024 chunks) is SMX_EINVAL before anything is
+ *    enqueued: pass a larger chunk_cols, or use softmax_rows_path.
+ *  - The wave and LDS paths use no scratch.
+ *  - Every call on one device shares that device's array, which keeps the
+ *    last call's contents (nothing in it needs clearing: each call writes
+ *    every summary before reading it). Calls that overlap in time on one
+ *    device (on two streams, or from two host threads) race on it and must
+ *    be ordered by the caller.
+ *  - The device address of the array is looked up on the first call made
+ *    with that device current; later calls reuse it.
+ * Arguments, paths, results (bitwise those of softmax_rows_path) and errors
+ * otherwise as softmax_rows_path. */
+SMX_API int softmax_rows_noalloc(const void* x, void* y, int64_t rows, int64_t cols,
+                                 smx_dtype dtype, const smx_mask* valid_len_or_mask,
+                                 smx_path path, int64_t chunk_cols, void* stream);
 
 /* softmax_rows_path — softmax_rows with the kernel path forced (AUTO picks
  * as softmax_rows does). chunk_cols applies to SMX_PATH_SPLIT (0 = the

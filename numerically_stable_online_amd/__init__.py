@@ -8,6 +8,7 @@ importing this package raises.
 
 Functions keep the C names:
   softmax_rows(x, ...)              -> y
+  softmax_rows_noalloc(x, out, ...) -> out (allocates no device memory)
   softmax_row_stats(x, chunk_cols)  -> stats [rows, n_chunks, 2] (m, l)
   softmax_merge_normalize(x, stats, chunk_cols) -> y
   log_softmax_rows(x, ...)          -> (y, lse)
@@ -71,6 +72,8 @@ def lib() -> C.CDLL:
         L.softmax_rows.restype = i32
         L.softmax_rows_path.argtypes = [vp, vp, i64, i64, i32, mp, i32, i64, vp]
         L.softmax_rows_path.restype = i32
+        L.softmax_rows_noalloc.argtypes = [vp, vp, i64, i64, i32, mp, i32, i64, vp]
+        L.softmax_rows_noalloc.restype = i32
         L.softmax_select_path.argtypes = [i64, i64, i32]
         L.softmax_select_path.restype = i32
         L.softmax_row_stats.argtypes = [vp, i64, i64, i32, mp, i64, vp, vp]
@@ -213,6 +216,23 @@ def softmax_rows(x: torch.Tensor, out: Optional[torch.Tensor] = None, *, valid_l
                                  PATH[path], int(chunk_cols), _stream_handle(stream, x.device))
     _check(rc)
     return y
+
+
+def softmax_rows_noalloc(x: torch.Tensor, out: torch.Tensor, *, valid_len=None, causal_period=None,
+                         causal_offset: int = 0, keep=None, path: str = "auto", chunk_cols: int = 0,
+                         stream=None) -> torch.Tensor:
+    """softmax_rows into a caller-given out, through the entry point that
+    allocates no device memory (the split path's summaries live in the
+    library's fixed per-device scratch; calls that overlap on one device race)."""
+    rows, cols = _rows_cols(x)
+    if out.shape != x.shape or out.dtype != x.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor of x's shape and dtype")
+    _on(out, x.device, "out")
+    m, keepalive = make_mask(rows, cols, valid_len, causal_period, causal_offset, keep, x.device)
+    rc = lib().softmax_rows_noalloc(x.data_ptr(), out.data_ptr(), rows, cols, _dtype_code(x), _mask_arg(m),
+                                    PATH[path], int(chunk_cols), _stream_handle(stream, x.device))
+    _check(rc)
+    return out
 
 
 def log_softmax_rows(x: torch.Tensor, out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,

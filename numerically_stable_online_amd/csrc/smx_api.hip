@@ -6,6 +6,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "smx_internal.hpp"
 
 namespace smx {
@@ -109,20 +111,40 @@ int64_t default_chunk(int64_t rows, int64_t cols, int dtype, bool vec) {
   return chunk;
 }
 
-int run_split(const Call& c0, int64_t chunk, int epi, hipStream_t stream) {
+// The split path's workspace: the chunk summaries, then (many chunks per row)
+// one merged summary per row, then (cross-entropy) one target logit per row.
+// Every byte of it is written before it is read within one call, so nothing
+// in it has to start at zero.
+struct SplitWs {
+  size_t stat_bytes, merged_bytes, bytes;
+  bool row_merge;
+};
+SplitWs split_ws(int64_t rows, int64_t nch, int epi) {
+  SplitWs w;
+  w.row_merge = nch > kRowMergeMinChunks;
+  w.stat_bytes = (size_t)(rows * nch) * sizeof(smx_stat);
+  w.merged_bytes = w.row_merge ? (size_t)rows * sizeof(smx_stat) : 0;
+  w.bytes = w.stat_bytes + w.merged_bytes + (epi == kEpiXent ? (size_t)rows * sizeof(float) : 0);
+  return w;
+}
+
+// fixed_ws: a caller-provided workspace of at least split_ws(...).bytes (the
+// no-allocation entry point's scratch), or null for a stream-ordered
+// allocation freed on the same stream
+int run_split(const Call& c0, int64_t chunk, int epi, hipStream_t stream, void* fixed_ws) {
   Call c = c0;
   const int64_t e = vec_elems(c.dtype);
   const bool vec = c.vec && chunk % e == 0;
   const int64_t nch = (c.a.cols + chunk - 1) / chunk;
-  // workspace: the chunk summaries, then (many chunks per row) one merged
-  // summary per row, then (cross-entropy) one target logit per row
-  const bool row_merge = nch > kRowMergeMinChunks;
-  const size_t stat_bytes = (size_t)(c.a.rows * nch) * sizeof(smx_stat);
-  const size_t merged_bytes = row_merge ? (size_t)c.a.rows * sizeof(smx_stat) : 0;
-  const size_t bytes = stat_bytes + merged_bytes + (epi == kEpiXent ? (size_t)c.a.rows * sizeof(float) : 0);
-  void* ws = nullptr;
-  hipError_t err = hipMallocAsync(&ws, bytes, stream);
-  if (err != hipSuccess) return hip_fail(err, "hipMallocAsync of the summary workspace");
+  const SplitWs w = split_ws(c.a.rows, nch, epi);
+  const bool row_merge = w.row_merge;
+  const size_t stat_bytes = w.stat_bytes, merged_bytes = w.merged_bytes;
+  void* ws = fixed_ws;
+  hipError_t err = hipSuccess;
+  if (ws == nullptr) {
+    err = hipMallocAsync(&ws, w.bytes, stream);
+    if (err != hipSuccess) return hip_fail(err, "hipMallocAsync of the summary workspace");
+  }
   smx_stat* const stats = (smx_stat*)ws;
   smx_stat* const merged = (smx_stat*)((char*)ws + stat_bytes);
   if (epi == kEpiXent) c.a.xt = (float*)((char*)ws + stat_bytes + merged_bytes);
@@ -132,13 +154,14 @@ int run_split(const Call& c0, int64_t chunk, int epi, hipStream_t stream) {
     err = row_merge ? launch_merge_normalize(c.a, c.dtype, vec, epi, chunk, nch, merged, 1, stream)
                     : launch_merge_normalize(c.a, c.dtype, vec, epi, chunk, nch, stats, nch, stream);
   }
-  const hipError_t ferr = hipFreeAsync(ws, stream);
+  const hipError_t ferr = fixed_ws == nullptr ? hipFreeAsync(ws, stream) : hipSuccess;
   if (err != hipSuccess) return hip_fail(err, "split-path launch");
   if (ferr != hipSuccess) return hip_fail(ferr, "hipFreeAsync of the summary workspace");
   return ok();
 }
 
-int run_rows(const Call& c, smx_path path, int64_t chunk_cols, int epi, hipStream_t stream) {
+int run_rows(const Call& c, smx_path path, int64_t chunk_cols, int epi, hipStream_t stream,
+             void* fixed_ws = nullptr) {
   const int64_t rows = c.a.rows, cols = c.a.cols;
   if (path == SMX_PATH_AUTO) path = choose(rows, cols, c.dtype, c.vec);
   hipError_t err = hipSuccess;
@@ -160,7 +183,7 @@ int run_rows(const Call& c, smx_path path, int64_t chunk_cols, int epi, hipStrea
     case SMX_PATH_SPLIT: {
       if (chunk_cols < 0) return fail(SMX_EINVAL, "chunk_cols must be >= 0");
       const int64_t chunk = chunk_cols > 0 ? chunk_cols : default_chunk(rows, cols, c.dtype, c.vec);
-      return run_split(c, chunk, epi, stream);
+      return run_split(c, chunk, epi, stream, fixed_ws);
     }
     default:
       return fail(SMX_EINVAL, "path %d is not a smx_path", (int)path);
@@ -221,6 +244,40 @@ int64_t weighted_split_chunk(int64_t groups, int64_t cols) {
 }
 
 }  // namespace
+
+// The scratch of softmax_rows_noalloc: the split path's summaries for callers
+// that cannot allocate. Each device holds its own copy for the life of the
+// process. In host code the array's name is only a stand-in; the device
+// address comes from hipGetSymbolAddress on that device.
+static __device__ __align__(256) char scratch[SMX_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+struct ScratchSlot {
+  std::once_flag once;
+  void* ptr = nullptr;
+  hipError_t err = hipSuccess;
+};
+ScratchSlot g_scratch[kMaxDevices];
+
+// The current device's copy of scratch: looked up once per device, on the
+// first call made with that device current, and kept.
+int scratch_on_current_device(void** ptr) {
+  int dev = 0;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(SMX_EHIP, "device %d: softmax_rows_noalloc tracks devices 0 to %d", dev, kMaxDevices - 1);
+  ScratchSlot& s = g_scratch[dev];
+  std::call_once(s.once, [&s] { s.err = hipGetSymbolAddress(&s.ptr, HIP_SYMBOL(scratch)); });
+  if (s.err != hipSuccess) return hip_fail(s.err, "hipGetSymbolAddress of the scratch buffer");
+  *ptr = s.ptr;
+  return SMX_OK;
+}
+
+}  // namespace
 }  // namespace smx
 
 using namespace smx;
@@ -240,6 +297,32 @@ int softmax_rows_path(const void* x, void* y, int64_t rows, int64_t cols, smx_dt
 int softmax_rows(const void* x, void* y, int64_t rows, int64_t cols, smx_dtype dtype, const smx_mask* mask,
                  void* stream) {
   return softmax_rows_path(x, y, rows, cols, dtype, mask, SMX_PATH_AUTO, 0, stream);
+}
+
+int softmax_rows_noalloc(const void* x, void* y, int64_t rows, int64_t cols, smx_dtype dtype, const smx_mask* mask,
+                         smx_path path, int64_t chunk_cols, void* stream) {
+  Call c;
+  if (int rc = check_common(x, y, rows, cols, (int)dtype, mask, true, c)) return rc;
+  if ((int)path < SMX_PATH_AUTO || (int)path > SMX_PATH_SPLIT) return fail(SMX_EINVAL, "path %d is not a smx_path", (int)path);
+  if (chunk_cols < 0) return fail(SMX_EINVAL, "chunk_cols must be >= 0");
+  if (rows == 0 || cols == 0) return ok();
+  const smx_path p = path == SMX_PATH_AUTO ? choose(rows, cols, c.dtype, c.vec) : path;
+  void* ws = nullptr;
+  if (p == SMX_PATH_SPLIT) {
+    // only the split path uses scratch; its size is checked before anything
+    // is enqueued (rows * n_chunks is bounded first so the product cannot
+    // overflow)
+    const int64_t chunk = chunk_cols > 0 ? chunk_cols : default_chunk(rows, cols, c.dtype, c.vec);
+    const int64_t nch = (cols + chunk - 1) / chunk;
+    const int64_t max_summaries = SMX_NOALLOC_SCRATCH_BYTES / (int64_t)sizeof(smx_stat);
+    if (rows > max_summaries / nch || split_ws(rows, nch, kEpiSoftmax).bytes > (size_t)SMX_NOALLOC_SCRATCH_BYTES)
+      return fail(SMX_EINVAL,
+                  "the split path needs %lld x %lld chunk summaries here, more than the %lld bytes of scratch "
+                  "softmax_rows_noalloc holds (use larger chunk_cols, or softmax_rows_path)",
+                  (long long)rows, (long long)nch, (long long)SMX_NOALLOC_SCRATCH_BYTES);
+    if (int rc = scratch_on_current_device(&ws)) return rc;
+  }
+  return run_rows(c, p, chunk_cols, kEpiSoftmax, (hipStream_t)stream, ws);
 }
 
 smx_path softmax_select_path(int64_t rows, int64_t cols, smx_dtype dtype) {

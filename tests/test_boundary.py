@@ -101,6 +101,15 @@ def test_argument_checks_need_no_device(smx):
     assert L.softmax_row_stats(16, 4, 64, 0, None, 16, None, None) == EINVAL
     assert L.softmax_merge_normalize(16, 1 << 20, 4, 64, 0, None, 16, 4096, 3, None) == EINVAL
     assert "n_chunks" in smx.smx_last_error()
+    # the entry point that allocates nothing: a split path whose summaries
+    # exceed its fixed scratch is refused before any device access, as are
+    # the checks it shares with softmax_rows_path
+    assert L.softmax_rows_noalloc(16, 1 << 40, 4096, 8192, 0, None, 3, 16, None) == EINVAL
+    assert "scratch" in smx.smx_last_error()
+    assert L.softmax_rows_noalloc(16, 1 << 40, 1 << 30, 1 << 20, 0, None, 3, 1, None) == EINVAL
+    assert L.softmax_rows_noalloc(16, 1 << 20, 4, 100000, 0, None, 1, 0, None) == EINVAL
+    assert L.softmax_rows_noalloc(16, 1 << 20, 4, 64, 0, None, 9, 0, None) == EINVAL
+    assert L.softmax_rows_noalloc(None, 1 << 20, 4, 64, 0, None, 0, 0, None) == EINVAL
 
 
 def test_stream_copy_argument_checks(smx):
