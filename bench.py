@@ -1,6 +1,6 @@
 """Benchmark: row-softmax effective HBM bandwidth on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads causal,spiked,small,masked,long]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads causal,spiked,small,masked,long,vocab]
 
 One step is one softmax_rows call over one batch of the headline workload,
 the largest of the workloads: bf16 causal attention scores, 256 groups of
@@ -54,11 +54,21 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores
 MALL_BYTES = 256 * 2 ** 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 KERNEL_SOURCES = {
-    "lds": ["k_lds.hip", "smx_device.hpp", "smx_math.hpp"],
+    "lds": ["k_lds.hip", "k_lds_res.hip", "smx_device.hpp", "smx_math.hpp"],
     "wave": ["k_wave.hip", "smx_device.hpp", "smx_math.hpp"],
     "split": ["k_split.hip", "smx_device.hpp", "smx_math.hpp"],
 }
 KERNEL_NAME = {"lds": "k_lds", "wave": "k_wave", "split": "k_merge_normalize+k_stats"}
+LDS_REGISTER_ROW_BYTES = 32768  # longer rows on the LDS path stay in LDS (k_lds_res)
+
+
+def kernel_of(path: str, w) -> str:
+    """The kernel a workload's softmax runs on its path."""
+    from workloads import ITEMSIZE
+
+    if path == "lds" and w.cols * ITEMSIZE[w.dtype] > LDS_REGISTER_ROW_BYTES:
+        return "k_lds_res"
+    return KERNEL_NAME[path]
 
 
 def parse():
@@ -66,10 +76,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workloads", default="causal,spiked,small,masked,long",
+    ap.add_argument("--workloads", default="causal,spiked,small,masked,long,vocab",
                     help="workloads to time (names in workloads.WORKLOADS); the first is the headline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--next-ops", default="spiked,long",
+    ap.add_argument("--next-ops", default="spiked,long,vocab",
                     help="workloads on which the log-softmax, softmax-backward and cross-entropy "
                          "entry points are also timed ('' for none)")
     ap.add_argument("--no-weighted", dest="weighted", action="store_false",
@@ -486,7 +496,8 @@ def main():
                           spread=not args.no_spread)
         gbs = r["bytes"] / (r["ms_per_step"] * 1e-3) / 1e9
         kgbs = r["bytes"] / (r["gpu_ms_per_launch"] * 1e-3) / 1e9
-        entry = {"workload": w.name, "path": r["path"], "algorithmic_bytes": r["bytes"],
+        entry = {"workload": w.name, "path": r["path"], "kernel": kernel_of(r["path"], w),
+                 "algorithmic_bytes": r["bytes"],
                  "step_ms": round(r["ms_per_step"], 5), "gpu_ms_per_launch": round(r["gpu_ms_per_launch"], 5),
                  "single_launch_ms_mean": round(r["launch_ms_mean"], 5),
                  "launch_ms_p10": round(r["launch_ms_p10"], 5), "launch_ms_p90": round(r["launch_ms_p90"], 5),
@@ -545,7 +556,7 @@ def main():
         "config": {"workload": w.name, "rows": w.rows, "cols": w.cols, "mask": w.mask.kind,
                    "path": r["path"], "seed": w.seed, "algorithmic_bytes_per_step": r["bytes"],
                    "buffer_copies": r["copies"]},
-        "roofline": {"bound": "hbm", "kernel": KERNEL_NAME[r["path"]], "achieved": round(kgbs, 1),
+        "roofline": {"bound": "hbm", "kernel": kernel_of(r["path"], w), "achieved": round(kgbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(kgbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel_source_sha": sha},
         "per_workload": per,

@@ -106,7 +106,9 @@ typedef struct {
 typedef enum {
   SMX_PATH_AUTO = 0,  /* chosen from the row size and the row count        */
   SMX_PATH_WAVE = 1,  /* one wave64 per row, the row held in registers     */
-  SMX_PATH_LDS = 2,   /* one workgroup per row, the row staged in LDS      */
+  SMX_PATH_LDS = 2,   /* one workgroup per row, the row staged in LDS and
+                         read from HBM once: up to 32 KiB held in registers,
+                         up to 152 KiB kept in LDS for all three passes    */
   SMX_PATH_SPLIT = 3  /* chunk summaries, then merge + normalize (2 reads) */
 } smx_path;
 
@@ -114,7 +116,12 @@ typedef enum {
  *   x, y  : device [rows, cols] row-major, element type dtype.
  *   valid_len_or_mask : host pointer to a mask descriptor, or NULL.
  *   stream: hipStream_t.
- * Long rows go through the split path, which takes its summary workspace
+ * Rows of at most 4 KiB take one wave each. Rows up to 152 KiB with 16-byte
+ * aligned x and y and cols * element size a multiple of 16 are read once on
+ * the LDS path ("Stable softmax: keep the normalizer consistent as tiles
+ * arrive", paragraph on fused rows: a row that fits on chip is read once).
+ * Longer rows, and unaligned ones the wave path cannot hold, go through the
+ * split path (the row read twice), which takes its summary workspace
  * (rows * ceil(cols / chunk) * 8 bytes, plus 8 bytes per row when a row has
  * more than 1024 chunks and its summaries are merged once per row first)
  * with a stream-ordered allocation and frees it on the same stream. */

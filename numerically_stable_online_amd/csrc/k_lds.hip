@@ -249,7 +249,8 @@ __global__ __launch_bounds__(NT) void k_lds(RowArgs a, int64_t row0) {
 }
 
 // rows up to 8 packs per thread of a 256-thread workgroup: 32 KiB of LDS,
-// 32 (f32) or 64 (16-bit) register-resident values per thread
+// 32 (f32) or 64 (16-bit) register-resident values per thread (longer rows
+// take k_lds_res, which keeps them in LDS)
 constexpr int64_t kMaxRowBytes = 256 * 8 * 16;
 
 // rows per launch: the grid's work-items stay far below 2^32
@@ -300,9 +301,11 @@ hipError_t launch_epi(const RowArgs& a, int dtype, hipStream_t s) {
 
 }  // namespace
 
-int64_t lds_max_cols(int dtype) { return kMaxRowBytes / elem_size(dtype); }
+int64_t lds_max_cols(int dtype) { return lds_res_max_cols(dtype); }
 
 hipError_t launch_lds(const RowArgs& a, int dtype, int epi, hipStream_t s) {
+  // rows past the register budget stay in LDS for all three passes
+  if (a.cols * elem_size(dtype) > kMaxRowBytes) return launch_lds_res(a, dtype, epi, s);
   if (epi == kEpiSoftmax) return launch_epi<kEpiSoftmax>(a, dtype, s);
   if (epi == kEpiLogSoftmax) return launch_epi<kEpiLogSoftmax>(a, dtype, s);
   return launch_epi<kEpiXent>(a, dtype, s);

@@ -89,14 +89,19 @@ int check_common(const void* x, const void* y, int64_t rows, int64_t cols, int d
   return SMX_OK;
 }
 
-// rows at least this many to fill the chip one workgroup per row
-constexpr int64_t kLdsMinRows = 1024;
+// Rows of at most 4 KiB take a wave each; aligned rows up to the LDS budget
+// (152 KiB) are read once on the LDS path whatever their number (measured
+// faster than the split path from 64 rows up, and the split path's two
+// launches and stream-ordered workspace cost some 24 us on small inputs);
+// unaligned rows the wave path still holds, when there are enough of them to
+// fill the chip, stay there; everything else is split.
+constexpr int64_t kWaveMinRows = 1024;
 
 smx_path choose(int64_t rows, int64_t cols, int dtype, bool vec) {
   const int64_t bytes = cols * elem_size(dtype);
   if (cols <= wave_max_cols(dtype, vec) && bytes <= 4096) return SMX_PATH_WAVE;
-  if (vec && cols <= lds_max_cols(dtype) && rows >= kLdsMinRows) return SMX_PATH_LDS;
-  if (cols <= wave_max_cols(dtype, vec) && rows >= kLdsMinRows) return SMX_PATH_WAVE;
+  if (vec && cols <= lds_max_cols(dtype)) return SMX_PATH_LDS;
+  if (cols <= wave_max_cols(dtype, vec) && rows >= kWaveMinRows) return SMX_PATH_WAVE;
   return SMX_PATH_SPLIT;
 }
 

@@ -56,9 +56,14 @@ inline int vec_elems(int dtype) { return 16 / elem_size(dtype); }
 int64_t wave_max_cols(int dtype, bool vec);
 hipError_t launch_wave(const RowArgs& a, int dtype, bool vec, int epi, hipStream_t stream);
 
-// --- workgroup-per-row, LDS-staged kernel (k_lds.hip) ---
+// --- workgroup-per-row, LDS-staged kernels ---
+// The LDS path: rows up to 32 KiB staged in LDS and held in registers
+// (k_lds.hip), longer ones up to lds_max_cols resident in LDS (k_lds_res.hip).
 int64_t lds_max_cols(int dtype);
 hipError_t launch_lds(const RowArgs& a, int dtype, int epi, hipStream_t stream);
+// rows too long for the registers: three passes over the row in LDS
+int64_t lds_res_max_cols(int dtype);
+hipError_t launch_lds_res(const RowArgs& a, int dtype, int epi, hipStream_t stream);
 
 // --- split path (k_split.hip) ---
 // Elements one workgroup holds per round of a chunk.

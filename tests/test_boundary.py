@@ -208,6 +208,15 @@ def test_path_choice_and_default_chunk(smx):
     assert smx.softmax_select_path(32768, 512, "f16") == "wave"
     assert smx.softmax_select_path(64, 1 << 20, "f32") == "split"
     assert smx.softmax_select_path(524288, 2048, "bf16") == "wave"
+    # aligned rows past 4 KiB are read once on the LDS path up to 152 KiB,
+    # however few; unaligned ones (rows not a multiple of 16 bytes) split
+    assert smx.softmax_select_path(4096, 32768, "bf16") == "lds"
+    assert smx.softmax_select_path(4096, 77824, "bf16") == "lds"
+    assert smx.softmax_select_path(4096, 38912, "f32") == "lds"
+    assert smx.softmax_select_path(4096, 77832, "bf16") == "split"
+    assert smx.softmax_select_path(100, 32768, "bf16") == "lds"
+    assert smx.softmax_select_path(3, 8192, "f32") == "lds"
+    assert smx.softmax_select_path(3, 100001, "f16") == "split"
     c = smx.softmax_default_chunk_cols(64, 1 << 20, "f32")
     assert c > 0 and c % 4 == 0 and 64 * (-(-(1 << 20) // c)) >= 2048
     for rows, cols, dt in ((1, 10, "bf16"), (3, 100000, "f16"), (1000, 5000, "f32")):

@@ -343,7 +343,7 @@ def _paths(dtype, cols, misalign):
     wave_max = 64 * 8 * (4 if dtype == "f32" else 8) if vec else 64 * 32
     if cols <= wave_max:
         paths.append("wave")
-    if vec and cols <= 256 * 8 * (4 if dtype == "f32" else 8):
+    if vec and cols * (4 if dtype == "f32" else 2) <= 152 * 1024:  # held in registers up to 32 KiB, then in LDS
         paths.append("lds")
     return paths
 
@@ -385,6 +385,93 @@ def test_odd_shapes_masks_paths(dtype):
                     what = f"{dtype} cols={cols} mask={mask.kind} misalign={misalign} path={path} chunk={chunk}"
                     y = run_rows(x, dtype, mask, path=path, chunk_cols=chunk, misalign=misalign)
                     check(y, dtype, p, cls, st, what)
+
+
+# ---------------------------------------------------------------------------
+# Rows above the register budget (32 KiB) up to 152 KiB: resident in LDS
+# ---------------------------------------------------------------------------
+
+RES_COLS = {"f32": [8196, 16384, 25132, 38912], "f16": [16392, 32768, 50264, 77824],
+            "bf16": [16392, 32768, 50264, 65536, 77824]}
+RES_MAX = {"f32": 38912, "f16": 77824, "bf16": 77824}
+
+
+def _res_case(rng, dtype, rows, cols, mask_kind):
+    """Seeded rows with policy rows (+inf in a valid lane, NaN in a lane
+    that is masked or, without a mask, valid; all -inf) under a mask."""
+    x = W.random_rows(rows, cols, dtype, seed=int(rng.integers(1 << 30)), scale=6.0)
+    inf = W.POS_INF[dtype].view(np.uint32) if dtype == "f32" else W.POS_INF[dtype]
+    W.set_bits(x, 2, 5, dtype, inf)
+    W.set_bits(x, 3, cols - 1, dtype, W.NEG_SNAN[dtype])
+    x[4] = W.to_format(np.full(cols, -np.inf), dtype)
+    if mask_kind == "valid_len":
+        vl = rng.integers(0, cols + 1, rows).astype(np.int32)
+        vl[:6] = [cols, cols - 3, cols, cols - 1, cols, 0]
+        return x, W.MaskSpec("valid_len", valid_len=vl)
+    if mask_kind == "causal":
+        return x, W.MaskSpec("causal", causal_period=rows, causal_offset=cols // 2 - rows // 2)
+    if mask_kind == "keep":
+        keep = (rng.random((rows, cols)) < 0.6).astype(np.uint8)
+        keep[2, 5] = 1
+        return x, W.MaskSpec("keep", keep=keep)
+    return x, W.MaskSpec()
+
+
+@pytest.mark.parametrize("dtype", W.DTYPES)
+def test_lds_resident_rows(dtype):
+    """Rows past the register budget stay in LDS for all three passes: every
+    dtype from just past 32 KiB to the 152 KiB maximum (ragged last pieces),
+    every mask kind, the policy rows, and the log-softmax and cross-entropy
+    epilogues, each against the oracle."""
+    rng = np.random.default_rng(610 + W.DTYPES.index(dtype))
+    kinds = ["none", "valid_len", "causal", "keep"]
+    for i, cols in enumerate(RES_COLS[dtype]):
+        kind = kinds[i % 4]
+        x, mask = _res_case(rng, dtype, 37, cols, kind)
+        what = f"lds-resident {dtype} 37x{cols} {kind}"
+        banner(what)
+        y = run_rows(x, dtype, mask, path="lds")
+        check_full(x, dtype, mask, y, what)
+        yl, lse = run_log(x, dtype, mask, path="lds")
+        check_log_full(x, dtype, mask, yl, lse, what + " log-softmax")
+        t = xent_targets(37, cols, seed=cols)
+        t[7] = -1  # ignored
+        t[8] = 3
+        x8 = x.copy()
+        x8[8] = W.to_format(np.where(np.arange(cols) == 3, 40.0, 1.0), dtype)  # a confident target
+        loss, dx = run_xent(x8, dtype, t, mask, path="lds")
+        check_xent_full(x8, dtype, t, mask, loss, dx, what + " cross-entropy")
+    # one past the maximum is refused on the forced path and goes split on auto
+    assert smx.softmax_select_path(4096, RES_MAX[dtype], dtype) == "lds"
+    assert smx.softmax_select_path(4096, RES_MAX[dtype] + 16 // W.ITEMSIZE[dtype], dtype) == "split"
+    xx = torch.zeros((2, RES_MAX[dtype] + 16 // W.ITEMSIZE[dtype]), dtype=TORCH_DTYPE[dtype], device="cuda")
+    with pytest.raises(smx.SmxError):
+        smx.softmax_rows(xx, path="lds")
+
+
+@pytest.mark.parametrize("dtype", W.DTYPES)
+def test_lds_resident_many_rows_per_workgroup(dtype):
+    """Workgroups stay resident and take several rows each, loading the next
+    row while they normalize the current one: valid lengths that differ from
+    row to row (empty rows, one lane, full rows) change how many pieces each
+    wave loads and waits for between consecutive rows. The automatic path
+    takes these rows, at the largest width and at a width two rows of which
+    share a CU."""
+    rng = np.random.default_rng(620 + W.DTYPES.index(dtype))
+    for cols, rows in ((RES_MAX[dtype], 1100), (RES_MAX[dtype] // 2, 1500)):
+        x = W.random_rows(rows, cols, dtype, seed=int(rng.integers(1 << 30)), scale=5.0)
+        vl = rng.integers(0, cols + 1, rows).astype(np.int32)
+        vl[rng.random(rows) < 0.1] = 0
+        vl[rng.random(rows) < 0.1] = 1
+        vl[rng.random(rows) < 0.2] = cols
+        mask = W.MaskSpec("valid_len", valid_len=vl)
+        assert smx.softmax_select_path(rows, cols, dtype) == "lds"
+        what = f"lds-resident {dtype} {rows}x{cols} valid lengths"
+        banner(what)
+        y = run_rows(x, dtype, mask)
+        check_full(x, dtype, mask, y, what)
+        y2 = run_rows(x, dtype, mask)
+        assert np.array_equal(y.view(np.uint8), y2.view(np.uint8)), "not deterministic"
 
 
 @pytest.mark.parametrize("dtype", W.DTYPES)

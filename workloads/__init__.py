@@ -20,8 +20,11 @@ pages talk about; no public dataset or suite is involved:
 * ``causal_scores`` bf16, 256 groups x 2048 rows x 2048 cols, scores q.k^T/sqrt(128)
   of N(0,1) q, k with head dimension 128, causal (row i of a group keeps
   columns 0..i), with five injected special rows per group.
+* ``vocab_rows`` bf16, 4096 x 32768, logits 4*N(0,1): output-head rows over
+  a vocabulary ("Softmax numerics architecture", memory-traffic account:
+  the softmax and loss of the output head).
 
-Every generator takes a seed (defaults 1 to 5, in the order above) and optional
+Every generator takes a seed (defaults 1 to 6, in the order above) and optional
 smaller shapes, so a test can draw the same distribution at a size the
 oracle finishes in seconds.
 """
@@ -241,9 +244,18 @@ def causal_values(seed: int = 5, groups: int = 256, n: int = 2048, head_dim: int
     return v
 
 
-# by short name; the first is the benchmark's headline
+def vocab_rows(seed: int = 6, rows: int = 4096, cols: int = 32768) -> Workload:
+    """Output-head rows: one row of logits per token over a vocabulary of
+    32768 classes, bf16, logits 4*N(0,1). Rows of 64 KiB: longer than the
+    registers of one workgroup hold, short enough to stay on chip."""
+    rng = _rng(seed)
+    x = 4.0 * rng.standard_normal((rows, cols), dtype=np.float32)
+    return Workload(f"bf16_{rows}x{cols}_vocab", "bf16", to_format(x, "bf16"), MaskSpec(), seed)
+
+
+# by short name, in the benchmark's order (its headline is the largest)
 WORKLOADS = {"spiked": spiked_rows, "small": small_rows, "masked": masked_rows, "long": long_rows,
-             "causal": causal_scores}
+             "causal": causal_scores, "vocab": vocab_rows}
 
 
 def random_rows(rows: int, cols: int, dtype: str, seed: int, scale: float = 4.0,
