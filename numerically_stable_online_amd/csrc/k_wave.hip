@@ -18,7 +18,8 @@ namespace smx {
 namespace {
 
 // MK: the mask class, fixed at compile time: kMaskNone (the whole row),
-// kMaskValidLen (a valid prefix: valid lengths or causal) or kMaskKeep.
+// kMaskValidLen (valid lengths), kMaskCausal (computed valid lengths) or
+// kMaskKeep, so a wave's prologue is straight-line code.
 template <int DT, int E, int VPT, int RPW, int MK, int EPI>
 __global__ __launch_bounds__(kThreads) void k_wave(RowArgs a, int64_t rbase) {
   constexpr bool KEEP = MK == kMaskKeep;
@@ -40,12 +41,16 @@ __global__ __launch_bounds__(kThreads) void k_wave(RowArgs a, int64_t rbase) {
   int64_t tgt[RPW];
   int slot[RPW];
   float xo[RPW];
+  valid_prefixes<MK, RPW>(a.mask, row0, a.rows, cols, prefix);
+  if constexpr (EPI == kEpiXent) {
+    row_targets<RPW>(a.target, row0, a.rows, cols, tgt);
+  } else {
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) tgt[r] = -1;
+  }
 #pragma unroll
   for (int r = 0; r < RPW; ++r) {
-    const int64_t row = row0 + r;
-    prefix[r] = row < a.rows ? (MK == kMaskValidLen ? (int)valid_prefix(a.mask, row, cols) : icols) : 0;
     mx[r] = -kInf;
-    tgt[r] = (EPI == kEpiXent && row < a.rows) ? row_target(a.target, row, cols) : -1;
     slot[r] = target_slot<64, E>(tgt[r], lane);
     xo[r] = -kInf;
   }
@@ -262,8 +267,10 @@ hipError_t launch_vpt(const RowArgs& a, hipStream_t stream) {
       hipLaunchKernelGGL((k_wave<DT, E, VPT, RPW, kMaskKeep, EPI>), grid, dim3(kThreads), 0, stream, a, rbase);
     } else if (a.mask.kind == kMaskNone) {
       hipLaunchKernelGGL((k_wave<DT, E, VPT, RPW, kMaskNone, EPI>), grid, dim3(kThreads), 0, stream, a, rbase);
-    } else {
+    } else if (a.mask.kind == kMaskValidLen) {
       hipLaunchKernelGGL((k_wave<DT, E, VPT, RPW, kMaskValidLen, EPI>), grid, dim3(kThreads), 0, stream, a, rbase);
+    } else {
+      hipLaunchKernelGGL((k_wave<DT, E, VPT, RPW, kMaskCausal, EPI>), grid, dim3(kThreads), 0, stream, a, rbase);
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

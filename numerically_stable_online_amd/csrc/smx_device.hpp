@@ -182,19 +182,72 @@ __device__ __forceinline__ uint64_t load_keep(const uint8_t* p) {
 
 __device__ __forceinline__ bool keep_lane(uint64_t k, int e) { return ((k >> (8 * e)) & 0xFFu) != 0; }
 
+// The causal valid length of row r, (r mod period) + 1 + offset, unclamped:
+// r mod period takes a short 32-bit sequence when both fit, else the 64-bit one.
+__device__ __forceinline__ int64_t causal_len(const MaskArgs& mk, int64_t r) {
+  const int64_t q = (((uint64_t)r | (uint64_t)mk.period) >> 32) != 0 ? r % mk.period
+                                                                     : (int64_t)((uint32_t)r % (uint32_t)mk.period);
+  return q + 1 + mk.offset;
+}
+
 // Valid-prefix length of row r (the whole row for NONE and KEEP_BYTES).
 __device__ __forceinline__ int64_t valid_prefix(const MaskArgs& mk, int64_t r, int64_t cols) {
   int64_t v = cols;
   if (mk.kind == kMaskValidLen) {
     v = mk.valid_len[r];
   } else if (mk.kind == kMaskCausal) {
-    // r % period: a short 32-bit sequence when both fit, else the 64-bit one
-    const int64_t q = (((uint64_t)r | (uint64_t)mk.period) >> 32) != 0
-                          ? r % mk.period
-                          : (int64_t)((uint32_t)r % (uint32_t)mk.period);
-    v = q + 1 + mk.offset;
+    v = causal_len(mk, r);
   }
   return v < 0 ? 0 : (v > cols ? cols : v);
+}
+
+// N consecutive int32 values p[0 .. N) loaded together, every one before any
+// is used: off one base address with constant offsets (so the scalar loads
+// share their address registers and go out back to back, or merge), except
+// where fewer than N remain (n < N, the last rows), which clamps.
+template <int N>
+__device__ __forceinline__ void load_run(const int32_t* p, int64_t n, int64_t (&v)[N]) {
+  if (n >= N) {
+#pragma unroll
+    for (int r = 0; r < N; ++r) v[r] = p[r];
+  } else {
+#pragma unroll
+    for (int r = 0; r < N; ++r) v[r] = p[r < n ? r : n - 1];
+  }
+}
+
+// Valid-prefix lengths of the N consecutive rows r0 .. r0 + N - 1 (0 for
+// rows at or past `rows`; r0 < rows) under a mask of compile-time class MK:
+// kMaskValidLen loads the valid lengths of all N rows before using any, so
+// their latencies overlap instead of queuing one after another in front of
+// the rows' loads; kMaskCausal computes them; any other class is the whole
+// row.
+template <int MK, int N>
+__device__ __forceinline__ void valid_prefixes(const MaskArgs& mk, int64_t r0, int64_t rows, int64_t cols,
+                                               int (&out)[N]) {
+  int64_t v[N];
+  if constexpr (MK == kMaskValidLen) {
+    load_run<N>(mk.valid_len + r0, rows - r0, v);
+  } else if constexpr (MK == kMaskCausal) {
+#pragma unroll
+    for (int r = 0; r < N; ++r) v[r] = causal_len(mk, r0 + r);
+  } else {
+#pragma unroll
+    for (int r = 0; r < N; ++r) v[r] = cols;
+  }
+#pragma unroll
+  for (int r = 0; r < N; ++r) out[r] = r0 + r < rows ? (int)(v[r] < 0 ? 0 : (v[r] > cols ? cols : v[r])) : 0;
+}
+
+// The cross-entropy targets of the N consecutive rows r0 .. (as row_target;
+// -1 for rows at or past `rows`), loaded together like valid_prefixes.
+template <int N>
+__device__ __forceinline__ void row_targets(const int32_t* target, int64_t r0, int64_t rows, int64_t cols,
+                                            int64_t (&out)[N]) {
+  int64_t t[N];
+  load_run<N>(target + r0, rows - r0, t);
+#pragma unroll
+  for (int r = 0; r < N; ++r) out[r] = (r0 + r < rows && t[r] >= 0 && t[r] < cols) ? t[r] : -1;
 }
 
 // ---------------------------------------------------------------------------
