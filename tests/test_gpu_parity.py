@@ -1304,8 +1304,12 @@ def test_weighted_rows_causal_full():
     """The attention workload at full size: 256 groups of 2048 x 2048
     bf16 causal scores (with their injected policy rows) and per group 2048
     value vectors of width 128. Every policy row is checked in every group;
-    numeric rows are checked against the oracle on a sample (the first, the
-    last and 6 random rows of every 8th group)."""
+    every row of four whole groups is checked against the oracle (the first
+    and last groups and two in between: the kernel hands the 16 row tiles of
+    a group to one XCD, so workgroup b takes tile (b mod 8) * 512 + b / 8
+    and these groups land on different XCDs and workgroup ranges), and a
+    sample of the others (the first, the last and 6 random rows of every
+    8th group)."""
     banner("weighted causal generate")
     w = W.causal_scores()
     v = W.causal_values()
@@ -1319,9 +1323,14 @@ def test_weighted_rows_causal_full():
             assert (sub == 0x7FC0).all(), name
         elif name == "all_neg_inf":
             assert (sub == 0).all(), name
+    worst = 0
+    for g in (0, 37, 130, 255):
+        banner(f"weighted causal: every row of group {g}")
+        ref, st, scale = weighted_reference(w.x, v, "bf16", n, w.mask, g * n, (g + 1) * n)
+        res = check_weighted(out[g * n:(g + 1) * n], "bf16", ref, st, scale, f"weighted causal group {g}")
+        worst = max(worst, res.get("max_ulp", 0))
     banner("weighted causal sampled rows")
     rng = np.random.default_rng(520)
-    worst = 0
     for g in range(0, 256, 8):
         picks = sorted({g * n, g * n + n - 1, *(g * n + rng.choice(n, 6, replace=False))})
         for r in picks:

@@ -433,16 +433,37 @@ def test_empty_shapes():
 VALUE_SET = (-np.inf, -30.0, -1.0, 0.0, 0.5, 3.0, 88.0, 1000.0)
 
 
+# The oracle's summaries and merges are pure functions of their inputs, and
+# the brute force below evaluates the same segments and the same merges over
+# and over (rows are drawn from a set of eight values), so both are cached:
+# each distinct call reaches the oracle once, and the exhaustive tiers fit
+# the default run. Keys are the exact float bit patterns (NaN included).
+_SEG_CACHE = {}
+_MERGE_CACHE = {}
+
+
 def _segment_stats(row, lo, hi):
-    seg = np.ascontiguousarray(np.array([row[lo:hi]], dtype=np.float32))
-    m, l = oracle.chunk_stats(seg, "f32", hi - lo)
-    return m[0, 0], l[0, 0]
+    key = tuple(row[lo:hi])
+    r = _SEG_CACHE.get(key)
+    if r is None:
+        seg = np.ascontiguousarray(np.array([row[lo:hi]], dtype=np.float32))
+        m, l = oracle.chunk_stats(seg, "f32", hi - lo)
+        r = _SEG_CACHE[key] = (m[0, 0], l[0, 0])
+    return r
+
+
+def _merge(ma, la, mb, lb):
+    key = np.array([ma, la, mb, lb], dtype=np.float64).tobytes()
+    r = _MERGE_CACHE.get(key)
+    if r is None:
+        r = _MERGE_CACHE[key] = oracle.merge(ma, la, mb, lb)
+    return r
 
 
 def _fold(stats):
     m, l = -np.inf, 0.0
     for sm, sl in stats:
-        m, l = oracle.merge(m, l, sm, sl)
+        m, l = _merge(m, l, sm, sl)
     return m, l
 
 
@@ -454,7 +475,7 @@ def _tree_shapes(items):
     for k in range(1, len(items)):
         for a in _tree_shapes(items[:k]):
             for b in _tree_shapes(items[k:]):
-                yield oracle.merge(*a, *b)
+                yield _merge(*a, *b)
 
 
 def _brute_force_rows(n, rows):
@@ -493,19 +514,18 @@ def test_brute_force_every_split_and_merge_order():
     assert checked > 100000
 
 
-@pytest.mark.slow
 def test_brute_force_rows_of_five_exhaustive():
-    """The slow tier: every row of five values from the set."""
+    """Every row of five values from the set (32768 rows, every contiguous
+    split, every merge order and bracketing: over a million folds)."""
     assert _brute_force_rows(5, itertools.product(VALUE_SET, repeat=5)) > 1000000
 
 
 @pytest.mark.slow
-def test_brute_force_rows_of_six_sampled():
-    """The slow tier at length six: 3000 seeded rows of the set (the full
-    8^6 rows would take the better part of an hour here)."""
-    rng = np.random.default_rng(66)
-    rows = [tuple(VALUE_SET[i] for i in rng.integers(0, len(VALUE_SET), 6)) for _ in range(3000)]
-    assert _brute_force_rows(6, rows) > 100000
+def test_brute_force_rows_of_six_exhaustive():
+    """The slow tier (--runslow): every row of six values from the set
+    (262144 rows, every contiguous split, every merge order of up to four
+    chunks and every bracketing)."""
+    assert _brute_force_rows(6, itertools.product(VALUE_SET, repeat=6)) > 10000000
 
 
 def test_split_path_oracle_equals_three_pass():
