@@ -9,11 +9,11 @@
 // ("Kernel visualization: online softmax", overview: the three quantities of
 // the safe softmax, each a pass over the row, here over on-chip copies).
 //
-// Every wave owns the 1 KiB pieces k * 8 + w of the row (w its index, k =
-// 0, 1, ...): it loads them, and lane i of the wave only ever touches the 16
-// bytes at offset 16 i of each of its pieces. So no wave waits on another's
-// loads: each waits (vmcnt) for its own pieces one at a time, and only the two
-// row reductions need barriers. The loads are issued as instructions the
+// Every wave of the NW owns the 1 KiB pieces k * NW + w of the row (w its
+// index, k = 0, 1, ...): it loads them, and lane i of the wave only ever
+// touches the 16 bytes at offset 16 i of each of its pieces. So no wave waits
+// on another's loads: each waits (vmcnt) for its own pieces one at a time,
+// and only the two row reductions need barriers. The loads are issued as instructions the
 // compiler does not track, so it inserts no wait for them; the kernel waits
 // itself.
 //
@@ -26,11 +26,19 @@
 namespace smx {
 namespace {
 
-constexpr int kPiece = 64 * 16;           // bytes of one wave's direct load
-constexpr int kResThreads = 512;          // eight waves
-constexpr int kResWaves = kResThreads / 64;
-constexpr int kResMaxPieces = 152;        // LDS pieces per row: 152 KiB
-constexpr int kResMaxPerWave = kResMaxPieces / kResWaves;  // 19
+constexpr int kPiece = 64 * 16;    // bytes of one wave's direct load
+constexpr int kResMaxPieces = 152;  // LDS pieces per row: 152 KiB
+// Workgroups of 8 waves (up to 19 pieces each), or of 16 for 16-bit rows of
+// 64 to 144 pieces (at most nine per wave: the LDS of one workgroup with its
+// 1 KiB of scratch stays within the CU's 160 KiB). Measured against 8 waves
+// in one process: 128 KiB bf16 rows 5.2 % faster, 98 KiB f16 1.4 %, 64 KiB
+// bf16 2.2 %, but 64 KiB fp32 rows 5.8 % slower and 33 KiB bf16 rows 3.5 %
+// slower (fewer pieces per wave, the same reductions over twice the waves).
+constexpr int kWideWaves = 16;
+constexpr int kWideMinPieces = 64;
+constexpr int kWideMaxPieces = 144;
+constexpr int kNarrowWaves = 8;
+constexpr int kResMaxPerWave = kResMaxPieces / kNarrowWaves;  // 19, the most any wave holds
 
 // One wave's direct 16-byte-per-lane global -> LDS load: lane i's 16 bytes
 // land at LDS byte address lds + 16 i (lds is the same in every lane; it
@@ -109,36 +117,40 @@ __device__ __forceinline__ float tree_max(const float* a) {
 // One array per reduction of a row, so that no reduction writes what another
 // may still be reading; the row's last barrier separates one row's uses from
 // the next row's.
+template <int NW>
 struct ResScratch {
-  float mx[kResWaves];
-  float hi[kResWaves];
-  float lo[kResWaves];
+  float mx[NW];
+  float hi[NW];
+  float lo[NW];
   float xt;  // cross-entropy: the target's logit, from the lane that holds it
 };
 
-// Workgroup reductions over the eight waves; every thread combines the wave
+// Workgroup reductions over the NW waves; every thread combines the wave
 // results in the same order, so all of them hold the same bits.
-__device__ __forceinline__ float res_max(float v, ResScratch& s) {
+template <int NW>
+__device__ __forceinline__ float res_max(float v, ResScratch<NW>& s) {
   v = wave_max(v);
   if ((threadIdx.x & 63) == 0) s.mx[threadIdx.x >> 6] = v;
   lds_barrier();
   float r = s.mx[0];
 #pragma unroll
-  for (int i = 1; i < kResWaves; ++i) r = vmax(r, s.mx[i]);
+  for (int i = 1; i < NW; ++i) r = vmax(r, s.mx[i]);
   return uniform(r);
 }
 
-__device__ __forceinline__ float res_sum(float v, ResScratch& s) {
+template <int NW>
+__device__ __forceinline__ float res_sum(float v, ResScratch<NW>& s) {
   v = wave_sum(v);
   if ((threadIdx.x & 63) == 0) s.hi[threadIdx.x >> 6] = v;
   lds_barrier();
   float r = s.hi[0];
 #pragma unroll
-  for (int i = 1; i < kResWaves; ++i) r = r + s.hi[i];
+  for (int i = 1; i < NW; ++i) r = r + s.hi[i];
   return uniform(r);
 }
 
-__device__ __forceinline__ void res_pair(float& hi, float& lo, ResScratch& s) {
+template <int NW>
+__device__ __forceinline__ void res_pair(float& hi, float& lo, ResScratch<NW>& s) {
   wave_pair_reduce(hi, lo);
   if ((threadIdx.x & 63) == 0) {
     s.hi[threadIdx.x >> 6] = hi;
@@ -147,22 +159,21 @@ __device__ __forceinline__ void res_pair(float& hi, float& lo, ResScratch& s) {
   lds_barrier();
   float rh = s.hi[0], rl = s.lo[0];
 #pragma unroll
-  for (int i = 1; i < kResWaves; ++i) pair_add(rh, rl, s.hi[i], s.lo[i]);
+  for (int i = 1; i < NW; ++i) pair_add(rh, rl, s.hi[i], s.lo[i]);
   hi = uniform(rh);
   lo = uniform(rl);
 }
 
 // MK: kMaskNone, kMaskValidLen (valid lengths or causal: a valid prefix) or
 // kMaskKeep (the keep bytes are read from memory in each pass).
-template <int DT, int MK, int EPI>
-__global__ __launch_bounds__(kResThreads) void k_lds_res(RowArgs a) {
+template <int DT, int MK, int EPI, int NW>
+__global__ __launch_bounds__(NW * 64) void k_lds_res(RowArgs a) {
   constexpr bool KEEP = MK == kMaskKeep;
   constexpr int S = Fmt<DT>::S;
   constexpr int E = 16 / S;
   constexpr bool ACC = DT == kF32;
-  constexpr int NW = kResWaves;
   extern __shared__ __attribute__((aligned(1024))) char row_lds[];
-  __shared__ ResScratch red;
+  __shared__ ResScratch<NW> red;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -506,14 +517,12 @@ constexpr int kMaxDevices = 64;
 // (capped by the rows): the CU count per device and the instance's resident
 // workgroups per CU for each LDS size are looked up once and kept (0 = not
 // yet known); the instance is also allowed the LDS it asks for once.
-template <int DT, int MK, int EPI>
-hipError_t launch_mk(const RowArgs& a, hipStream_t s) {
-  constexpr int S = Fmt<DT>::S;
+template <int DT, int MK, int EPI, int NW>
+hipError_t launch_nw(const RowArgs& a, int pieces, hipStream_t s) {
   static int cu_count[kMaxDevices];
   static int per_cu[kMaxDevices][kResMaxPieces + 1];
   static int lds_allowed[kMaxDevices];
-  auto kernel = k_lds_res<DT, MK, EPI>;
-  const int pieces = (int)((a.cols * S + kPiece - 1) / kPiece);
+  auto kernel = k_lds_res<DT, MK, EPI, NW>;
   const size_t lds = (size_t)pieces * kPiece;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -533,15 +542,24 @@ hipError_t launch_mk(const RowArgs& a, hipStream_t s) {
   }
   int occ = __atomic_load_n(&per_cu[dev][pieces], __ATOMIC_RELAXED);
   if (occ == 0) {
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, kResThreads, lds);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, NW * 64, lds);
     if (e != hipSuccess) return e;
     if (occ <= 0) return hipErrorInvalidConfiguration;
     __atomic_store_n(&per_cu[dev][pieces], occ, __ATOMIC_RELAXED);
   }
   const int64_t resident = (int64_t)cus * occ;
   const unsigned grid = (unsigned)(a.rows < resident ? a.rows : resident);
-  hipLaunchKernelGGL(kernel, dim3(grid), dim3(kResThreads), lds, s, a);
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(NW * 64), lds, s, a);
   return hipGetLastError();
+}
+
+template <int DT, int MK, int EPI>
+hipError_t launch_mk(const RowArgs& a, hipStream_t s) {
+  constexpr int S = Fmt<DT>::S;
+  const int pieces = (int)((a.cols * S + kPiece - 1) / kPiece);
+  if (DT != kF32 && pieces >= kWideMinPieces && pieces <= kWideMaxPieces)
+    return launch_nw<DT, MK, EPI, kWideWaves>(a, pieces, s);
+  return launch_nw<DT, MK, EPI, kNarrowWaves>(a, pieces, s);
 }
 
 template <int DT, int EPI>
