@@ -34,8 +34,14 @@ constexpr int kResMaxPieces = 152;  // LDS pieces per row: 152 KiB
 // in one process: 128 KiB bf16 rows 5.2 % faster, 98 KiB f16 1.4 %, 64 KiB
 // bf16 2.2 %, but 64 KiB fp32 rows 5.8 % slower and 33 KiB bf16 rows 3.5 %
 // slower (fewer pieces per wave, the same reductions over twice the waves).
+// The cross-entropy takes 16 waves only from 80 pieces, where a CU holds
+// one workgroup whatever its width: at 64 pieces (two workgroups per CU) it
+// measured 108.7 us with 16 waves against 98.6 us with 8 on 4096 rows of
+// 32768 bf16 logits, while from 80 to 144 pieces 16 waves were 3 to 6 %
+// faster.
 constexpr int kWideWaves = 16;
 constexpr int kWideMinPieces = 64;
+constexpr int kWideMinPiecesXent = 80;
 constexpr int kWideMaxPieces = 144;
 constexpr int kNarrowWaves = 8;
 constexpr int kResMaxPerWave = kResMaxPieces / kNarrowWaves;  // 19, the most any wave holds
@@ -185,7 +191,19 @@ __global__ __launch_bounds__(NW * 64) void k_lds_res(RowArgs a) {
 
   // A row's valid prefix, and the pieces of it this wave loads: pieces past
   // the prefix are never fetched (their outputs are policy zeros).
-  auto prefix_of = [&](int64_t r) -> int { return MK == kMaskValidLen ? (int)valid_prefix(a.mask, r, cols) : icols; };
+  auto prefix_of = [&](int64_t r) -> int {
+    if constexpr (MK == kMaskValidLen) {  // valid lengths and causal masks
+      const int64_t v = a.mask.kind == kMaskCausal ? causal_len(a.mask, r) : load_readonly(a.mask.valid_len, r);
+      return (int)(v < 0 ? 0 : (v > cols ? cols : v));
+    } else {
+      return icols;
+    }
+  };
+  // cross-entropy: the row's target lane, -1 for an ignored row
+  auto target_of = [&](int64_t r) -> int64_t {
+    const int64_t v = load_readonly(a.target, r);
+    return v >= 0 && v < cols ? v : -1;
+  };
   auto loaded_of = [&](int prefix) {
     const int npv = ((prefix + E - 1) / E + 63) >> 6;
     return npv > wid ? (npv - wid + NW - 1) / NW : 0;
@@ -202,6 +220,9 @@ __global__ __launch_bounds__(NW * 64) void k_lds_res(RowArgs a) {
   if (row >= a.rows) return;
   int prefix = prefix_of(row);
   int nld = loaded_of(prefix);
+  // cross-entropy: the row's target lane (-1: an ignored row), read one row
+  // ahead like the prefix, so its load is not waited for at the row's start
+  int64_t t = EPI == kEpiXent ? target_of(row) : -1;
   {
     const char* xr = a.x + row * cols * S;
     for (int k = 0; k < nld; ++k) dma_piece(src_of(xr, k, prefix), uniform(lds0 + (k * NW + wid) * kPiece));
@@ -212,15 +233,14 @@ __global__ __launch_bounds__(NW * 64) void k_lds_res(RowArgs a) {
     const bool more = nrow < a.rows;
     const int prefix_n = more ? prefix_of(nrow) : 0;
     const int nld_n = more ? loaded_of(prefix_n) : 0;
+    const int64_t t_n = EPI == kEpiXent && more ? target_of(nrow) : -1;
     const char* const xn = a.x + (more ? nrow : row) * cols * S;
     char* const yr = a.y + row * cols * S;
     const uint8_t* const kr = KEEP ? a.mask.keep + row * cols : nullptr;
 
-    // cross-entropy: the target lane t (-1: an ignored row) and the one
-    // thread holding it: element t is slot te of pack t / E, which is lane
-    // (t / E) % 64 of piece (t / E) / 64, owned by wave piece % 8 as its
-    // piece number tk = piece / 8
-    const int64_t t = EPI == kEpiXent ? row_target(a.target, row, cols) : -1;
+    // cross-entropy: the one thread holding the target lane t: element t is
+    // slot te of pack t / E, which is lane (t / E) % 64 of piece (t / E) / 64,
+    // owned by wave piece % NW as its piece number tk = piece / NW
     int tk = -1, te = 0;
     if (EPI == kEpiXent && t >= 0) {
       const int q = (int)t / E, pc = q >> 6;
@@ -505,6 +525,7 @@ __global__ __launch_bounds__(NW * 64) void k_lds_res(RowArgs a) {
     }
     prefix = prefix_n;
     nld = nld_n;
+    t = t_n;
     // the scratch is written again only after this barrier (every thread
     // has read this row's reductions)
     lds_barrier();
@@ -557,7 +578,8 @@ template <int DT, int MK, int EPI>
 hipError_t launch_mk(const RowArgs& a, hipStream_t s) {
   constexpr int S = Fmt<DT>::S;
   const int pieces = (int)((a.cols * S + kPiece - 1) / kPiece);
-  if (DT != kF32 && pieces >= kWideMinPieces && pieces <= kWideMaxPieces)
+  constexpr int kMin = EPI == kEpiXent ? kWideMinPiecesXent : kWideMinPieces;
+  if (DT != kF32 && pieces >= kMin && pieces <= kWideMaxPieces)
     return launch_nw<DT, MK, EPI, kWideWaves>(a, pieces, s);
   return launch_nw<DT, MK, EPI, kNarrowWaves>(a, pieces, s);
 }

@@ -201,6 +201,17 @@ __device__ __forceinline__ int64_t valid_prefix(const MaskArgs& mk, int64_t r, i
   return v < 0 ? 0 : (v > cols ? cols : v);
 }
 
+// p[i] of an int32 array that no thread of the kernel writes (a row's valid
+// length or target), read through the constant address space. With a
+// uniform index that is a scalar load, waited for by itself; a plain load
+// placed after the kernel's own global stores (the next row of a persistent
+// loop) may not go through the scalar cache, so it becomes a vector load and
+// its wait, vmcnt(0), would also drain every store and every direct LDS load
+// in flight.
+__device__ __forceinline__ int64_t load_readonly(const int32_t* p, int64_t i) {
+  return ((const __attribute__((address_space(4))) int32_t*)p)[i];
+}
+
 // N consecutive int32 values p[0 .. N) loaded together, every one before any
 // is used: off one base address with constant offsets (so the scalar loads
 // share their address registers and go out back to back, or merge), except

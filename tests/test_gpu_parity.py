@@ -111,6 +111,18 @@ def test_masked_rows_full(path):
     banner(f"masked {path}: {r}")
 
 
+@pytest.mark.parametrize("path", ["auto", "split"])
+def test_vocab_rows_full(path):
+    """The vocabulary rows (4096 x 32768 bf16, 64 KiB each) at full size:
+    resident in LDS on the automatic path, and through the split path."""
+    w = W.vocab_rows()
+    assert smx.softmax_select_path(w.rows, w.cols, w.dtype) == "lds"
+    banner(f"vocab {path}")
+    y = run_rows(w.x, "bf16", w.mask, path=path)
+    r = check_full(w.x, "bf16", w.mask, y, f"vocab/{path}")
+    banner(f"vocab {path}: {r}")
+
+
 @pytest.mark.parametrize("chunk", [0, 4096, 100000])
 def test_long_rows_full(chunk):
     w = W.long_rows()
@@ -835,7 +847,7 @@ def check_log_full(x_raw, dtype, mask, y, lse, what, r0=0, r1=None):
 
 
 @pytest.mark.parametrize("cfg,path", [("small", "auto"), ("small", "wave"), ("small", "lds"), ("small", "split"), ("spiked", "auto"),
-                                      ("spiked", "split"), ("masked", "auto"), ("masked", "split"), ("long", "auto")])
+                                      ("spiked", "split"), ("masked", "auto"), ("masked", "split"), ("long", "auto"), ("vocab", "auto")])
 def test_log_softmax_workloads(cfg, path):
     w = W.WORKLOADS[cfg]()
     banner(f"log {cfg} {path}")
@@ -926,7 +938,7 @@ def check_bwd_full(p_raw, g_raw, dtype, dx, what):
 
 
 @pytest.mark.parametrize("cfg,path", [("small", "auto"), ("small", "wave"), ("small", "lds"), ("small", "split"), ("spiked", "auto"),
-                                      ("spiked", "split"), ("masked", "auto"), ("long", "auto")])
+                                      ("spiked", "split"), ("masked", "auto"), ("long", "auto"), ("vocab", "auto")])
 def test_backward_workloads(cfg, path):
     w = W.WORKLOADS[cfg]()
     p_raw, g_raw = bwd_inputs(w.x, w.dtype, w.mask, seed=100 + w.seed)
@@ -1001,7 +1013,7 @@ def check_xent_full(x_raw, dtype, target, mask, loss, dx, what):
 
 
 @pytest.mark.parametrize("cfg,path", [("small", "auto"), ("small", "wave"), ("small", "lds"), ("small", "split"), ("spiked", "auto"),
-                                      ("spiked", "split"), ("masked", "auto"), ("masked", "split"), ("long", "auto")])
+                                      ("spiked", "split"), ("masked", "auto"), ("masked", "split"), ("long", "auto"), ("vocab", "auto")])
 def test_cross_entropy_workloads(cfg, path):
     w = W.WORKLOADS[cfg]()
     t = xent_targets(w.rows, w.cols, seed=300 + w.seed)
