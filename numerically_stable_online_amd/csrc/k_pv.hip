@@ -223,12 +223,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     tr_off[i] = vr * D * S + v_pos<D>(vr, d0 / 8) * 16 + (d0 % 8) * S;
   }
 
-  for (int64_t b = blockIdx.x; b < total; b += gridDim.x) {
-    // XCD-aware order: the eight XCDs take workgroups round-robin, so
-    // consecutive logical tiles (the tiles of one group, which share V) are
-    // given to one XCD and its L2; within a group the longest tiles (the
-    // last rows of a causal group) come first
-    const int64_t lb = (total % 8 == 0) ? (b % 8) * per_xcd + b / 8 : b;
+  // The workgroups stay resident and take tiles round by round. XCD-aware
+  // order: the eight XCDs take workgroups round-robin, so each XCD is given
+  // a contiguous eighth of the logical tiles (whole groups, which share V,
+  // stay in its L2); within a group the longest tiles (the last rows of a
+  // causal group) come first, and the XCD's workgroups walk its tiles in a
+  // snake, reversing direction every round, so that a workgroup that took a
+  // long tile of a group takes a short one next (causal tiles of one group
+  // differ in length by up to 16 times).
+  const bool xcd = total % 8 == 0 && gridDim.x % 8 == 0;
+  const int64_t per = gridDim.x / 8;  // workgroups per XCD (when xcd)
+  const int64_t u = blockIdx.x / 8;
+  const int64_t rounds = xcd ? (per_xcd + per - 1) / per : (total - blockIdx.x + gridDim.x - 1) / gridDim.x;
+  for (int64_t k = 0; k < rounds; ++k) {
+    int64_t lb = blockIdx.x + k * gridDim.x;
+    if (xcd) {
+      const int64_t p = k * per + ((k & 1) ? per - 1 - u : u);
+      if (p >= per_xcd) continue;  // uniform across the workgroup
+      lb = (blockIdx.x % 8) * per_xcd + p;
+    }
     const int64_t g = lb / tiles_per_group;
     const int64_t tile = tiles_per_group - 1 - lb % tiles_per_group;
     const int64_t row0 = g * rpg + tile * kPvRows;
@@ -443,16 +456,38 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   }
 }
 
+constexpr int kMaxDevices = 64;
+
+// As many workgroups as the device holds at once (the occupancy the runtime
+// reports for the kernel, times the CU count), at most one per tile.
+template <int DT, int D, bool KEEP>
+hipError_t launch_keep(const PvArgs& a, int64_t tiles, hipStream_t s) {
+  static int resident[kMaxDevices];
+  auto kernel = k_pv<DT, D, KEEP>;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  int res = __atomic_load_n(&resident[dev], __ATOMIC_RELAXED);
+  if (res == 0) {
+    int occ = 0, cus = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, kThreads, 0);
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    res = (occ > 0 ? occ : 1) * cus;
+    __atomic_store_n(&resident[dev], res, __ATOMIC_RELAXED);
+  }
+  const unsigned grid = (unsigned)(tiles < res ? tiles : res);
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
 template <int DT, int D>
 hipError_t launch_d(const PvArgs& a, hipStream_t s) {
   const int64_t tiles = (a.rows / a.rows_per_group) * ((a.rows_per_group + kPvRows - 1) / kPvRows);
-  const unsigned grid = (unsigned)(tiles < (1 << 20) ? tiles : (1 << 20));
-  if (a.mask.kind == kMaskKeep) {
-    hipLaunchKernelGGL((k_pv<DT, D, true>), dim3(grid), dim3(kThreads), 0, s, a);
-  } else {
-    hipLaunchKernelGGL((k_pv<DT, D, false>), dim3(grid), dim3(kThreads), 0, s, a);
-  }
-  return hipGetLastError();
+  if (a.mask.kind == kMaskKeep) return launch_keep<DT, D, true>(a, tiles, s);
+  return launch_keep<DT, D, false>(a, tiles, s);
 }
 
 template <int DT>
