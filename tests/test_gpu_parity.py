@@ -312,10 +312,13 @@ def test_row_slices_past_2_20_workgroups():
 def test_stream_copy_is_exact():
     """The bandwidth reference copy moves every byte: sizes from one 16-byte
     pack through ragged multiples to the headline footprint, on the default
-    and on a separate stream."""
+    and on a separate stream; from 1 GiB it copies 16 KiB per workgroup in
+    the XCDs' contiguous order, with the grid padded to a multiple of 8 (the
+    second large size leaves a ragged last chunk and padding workgroups)."""
     g = torch.Generator(device="cuda")
     g.manual_seed(11)
-    for nbytes in (16, 48, 4096 + 16, 1 << 20, (1 << 26) + 4080, 8192 * 4096 * 2):
+    for nbytes in (16, 48, 4096 + 16, 1 << 20, (1 << 26) + 4080, 8192 * 4096 * 2, 1 << 30,
+                   (1 << 30) + 3 * 16384 + 48):
         banner(f"stream copy {nbytes} B")
         x = torch.randint(-2 ** 31, 2 ** 31 - 1, (nbytes // 4,), dtype=torch.int32, device="cuda", generator=g)
         y = torch.full_like(x, 0x5A5A5A5A)
