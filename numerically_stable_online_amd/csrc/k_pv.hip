@@ -7,8 +7,9 @@
 // weighted-value numerator and the reference summary; "Softmax numerics
 // architecture", tiled attention: the output is o / l at the end).
 //
-// A workgroup of four waves owns 128 rows of one group; each wave owns 32 of
-// them. Blocks of 64 columns of the scores and of V travel HBM -> LDS by
+// A tile is 128 rows of one group; a workgroup of four waves takes one tile
+// at a time (each wave 32 of its rows), and the workgroups stay resident,
+// taking tiles round by round. Blocks of 64 columns of the scores and of V travel HBM -> LDS by
 // direct loads into a ring (scores three stages deep, issued two blocks
 // ahead; V two stages, one block ahead); score chunks wholly past a row's
 // valid prefix are loaded from a -inf chunk instead of from HBM. Per block:
