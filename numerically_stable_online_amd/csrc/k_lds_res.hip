@@ -110,16 +110,6 @@ struct Kind {
   static constexpr int value = K;
 };
 
-// Maximum of N register values as a balanced tree (NaN-propagating).
-template <int N>
-__device__ __forceinline__ float tree_max(const float* a) {
-  if constexpr (N == 1) {
-    return a[0];
-  } else {
-    return vmax(tree_max<N / 2>(a), tree_max<N - N / 2>(a + N / 2));
-  }
-}
-
 // One array per reduction of a row, so that no reduction writes what another
 // may still be reading; the row's last barrier separates one row's uses from
 // the next row's.

@@ -72,7 +72,19 @@ __global__ __launch_bounds__(kThreads) void k_stats(RowArgs a, int64_t chunk, in
     // nontemporal ones: part of x then stays in the Infinity Cache for the
     // normalize pass's reread (nontemporal loads here made the two passes
     // 12-14 % slower end to end)
+    // a round wholly inside the valid prefix needs no per-element test
+    // (keep masks and the cross-entropy's target lane always do); the test
+    // is uniform across the workgroup, so the two forms are scalar branches
+    auto full_round = [&](int64_t base) { return !KEEP && !XENT && base + kRound <= lim; };
     auto fetch = [&](int64_t base, Pack<DT, E>(&p)[VPT], uint64_t(&kb)[VPT]) {
+      if (full_round(base)) {
+#pragma unroll
+        for (int k = 0; k < VPT; ++k) {
+          p[k].load(xr + (base + (int64_t)(k * kThreads + tid) * E) * S);
+          kb[k] = ~0ull;
+        }
+        return;
+      }
 #pragma unroll
       for (int k = 0; k < VPT; ++k) {
         const int64_t j0 = base + (int64_t)(k * kThreads + tid) * E;
@@ -93,26 +105,36 @@ __global__ __launch_bounds__(kThreads) void k_stats(RowArgs a, int64_t chunk, in
       const int slot = XENT ? target_slot<kThreads, E>(t >= base && t - base < kRound ? t - base : -1, tid) : -1;
       float v[VPT * E];
       float mr = -kInf;
+      if (full_round(base)) {
 #pragma unroll
-      for (int k = 0; k < VPT; ++k) {
-        const int64_t left = lim - (base + (int64_t)(k * kThreads + tid) * E);
-        const int rem = left <= 0 ? 0 : (left >= E ? E : (int)left);
+        for (int k = 0; k < VPT; ++k) {
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-          const bool ok = e < rem && (!KEEP || keep_lane(kb[k], e)) && (!XENT || k * E + e != slot);
-          v[k * E + e] = ok ? p[k].get(e) : -kInf;
+          for (int e = 0; e < E; ++e) v[k * E + e] = p[k].get(e);
         }
+        mr = tree_max<VPT * E>(v);
+      } else {
 #pragma unroll
-        for (int e = 0; e < E; ++e) mr = vmax(mr, v[k * E + e]);
+        for (int k = 0; k < VPT; ++k) {
+          const int64_t left = lim - (base + (int64_t)(k * kThreads + tid) * E);
+          const int rem = left <= 0 ? 0 : (left >= E ? E : (int)left);
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            const bool ok = e < rem && (!KEEP || keep_lane(kb[k], e)) && (!XENT || k * E + e != slot);
+            v[k * E + e] = ok ? p[k].get(e) : -kInf;
+          }
+#pragma unroll
+          for (int e = 0; e < E; ++e) mr = vmax(mr, v[k * E + e]);
+        }
       }
       const float m_new = vmax(m_t, mr);
       if (m_new != -kInf) {
         // correct the running sum, then add this round against m_new; the
         // round's terms are summed as a tree in registers
+        const float lo = m_new - 126.0f;
 #pragma unroll
         for (int i = 0; i < VPT * E; ++i) {
           if constexpr (ACC) {
-            v[i] = exp_acc_sum(v[i], m_new);
+            v[i] = exp_acc_sum_clamped(vmax(v[i], lo), m_new);  // NaN stays NaN: such a chunk is poisoned
           } else {
             v[i] = __builtin_amdgcn_exp2f((v[i] - m_new) * kLog2e);
           }
@@ -256,6 +278,32 @@ __global__ __launch_bounds__(kThreads) void k_merge_normalize(RowArgs a, int64_t
                            : -1;
       Pack<DT, E> in[VPT];
       uint64_t kb[VPT];
+      // a round wholly inside the valid prefix: every pack is loaded and
+      // stored, no lane is masked (uniform across the workgroup)
+      if (!KEEP && base + kRound <= lim) {
+#pragma unroll
+        for (int k = 0; k < VPT; ++k) in[k].template load<true>(xr + (base + (int64_t)(k * kThreads + tid) * E) * S);
+#pragma unroll
+        for (int k = 0; k < VPT; ++k) {
+          const int64_t j0 = base + (int64_t)(k * kThreads + tid) * E;
+          float o[E];
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            if constexpr (EPI == kEpiLogSoftmax) {
+              o[e] = minus_lse(in[k].get(e), lse);
+            } else {
+              o[e] = exp_b64<ACC>(in[k].get(e), m) * inv;
+            }
+          }
+          Pack<DT, E> out;
+          out.put_values(o);
+          out.template store<true>(yr + j0 * S);
+        }
+        if constexpr (EPI == kEpiXent) {
+          if (slot >= 0) store_one<DT>(yr + t * S, at_t);
+        }
+        continue;
+      }
 #pragma unroll
       for (int k = 0; k < VPT; ++k) {
         const int64_t j0 = base + (int64_t)(k * kThreads + tid) * E;

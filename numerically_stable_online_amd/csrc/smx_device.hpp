@@ -307,6 +307,23 @@ __device__ __forceinline__ float exp_acc_sum(float x, float m) {
   return dh >= -120.0f ? r : 0.0f;
 }
 
+// exp_acc_sum for a value already clamped to at least m - 126: no lane is
+// -inf (masked lanes arrive as m - 126), so no NaN arises, and every
+// exponential below exp(-120) is exactly 0 either way (2^-173 and below
+// underflow), so no select is needed.
+__device__ __forceinline__ float exp_acc_sum_clamped(float x, float m) {
+  constexpr float kLog2eLo = 1.925963033500011e-08f;
+  constexpr float kLn2 = 0.693147182464599609375f;
+  float dh, dl;
+  two_diff(x, m, dh, dl);
+  const float th = dh * kLog2e;
+  float tl = __builtin_fmaf(dh, kLog2e, -th);
+  tl = __builtin_fmaf(dh, kLog2eLo, tl);
+  tl = __builtin_fmaf(dl, kLog2e, tl);
+  const float e = __builtin_amdgcn_exp2f(th);
+  return __builtin_fmaf(e, tl * kLn2, e);
+}
+
 // 16-bit I/O: the hardware base-2 exponential, v_exp_f32. Its argument
 // carries a relative error of about 2^-23 |x - m|, far below half an ulp of
 // bf16 or fp16 wherever the result is not rounded to zero.
@@ -458,6 +475,16 @@ __device__ __forceinline__ float lane_read(float v, int lane) {
 // any operand makes the result NaN, so a row's maximum is NaN exactly when a
 // valid lane holds NaN, and +inf exactly when one holds +inf and none NaN.
 __device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
+// Maximum of N register values as a balanced tree (NaN-propagating).
+template <int N>
+__device__ __forceinline__ float tree_max(const float* a) {
+  if constexpr (N == 1) {
+    return a[0];
+  } else {
+    return vmax(tree_max<N / 2>(a), tree_max<N - N / 2>(a + N / 2));
+  }
+}
 
 __device__ __forceinline__ float wave_max(float v) {
   v = vmax(v, dpp<kDppXor1>(v));
