@@ -169,7 +169,7 @@ __global__ __launch_bounds__(NW * 64) void k_lds_res(RowArgs a) {
   constexpr int E = 16 / S;
   constexpr bool ACC = DT == kF32;
   extern __shared__ __attribute__((aligned(1024))) char row_lds[];
-  __shared__ ResScratch<NW> red;
+  __shared__ ResScratch<NW> red2[2];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -218,6 +218,7 @@ __global__ __launch_bounds__(NW * 64) void k_lds_res(RowArgs a) {
     for (int k = 0; k < nld; ++k) dma_piece(src_of(xr, k, prefix), uniform(lds0 + (k * NW + wid) * kPiece));
   }
 
+  int par = 0;
   for (; row < a.rows; row += gridDim.x) {
     const int64_t nrow = row + gridDim.x;
     const bool more = nrow < a.rows;
@@ -368,6 +369,8 @@ __global__ __launch_bounds__(NW * 64) void k_lds_res(RowArgs a) {
         fold_pack(va);
       }
     }
+    // the row's reduction scratch: two copies, alternating from row to row
+    ResScratch<NW>& red = red2[par];
     if (EPI == kEpiXent && tk >= 0) red.xt = xt_own;
     float mx = res_max(m_l, red);
     float xt = -kInf;
@@ -516,9 +519,10 @@ __global__ __launch_bounds__(NW * 64) void k_lds_res(RowArgs a) {
     prefix = prefix_n;
     nld = nld_n;
     t = t_n;
-    // the scratch is written again only after this barrier (every thread
-    // has read this row's reductions)
-    lds_barrier();
+    // the next row uses the other copy of the scratch; this row's copy is
+    // written again two rows on, after the next row's first barrier, which
+    // every thread reaches only once it has read this row's reductions
+    par ^= 1;
   }
 }
 
