@@ -111,8 +111,8 @@ struct Kind {
 };
 
 // One array per reduction of a row, so that no reduction writes what another
-// may still be reading; the row's last barrier separates one row's uses from
-// the next row's.
+// may still be reading; consecutive rows use two copies in turn (a row's
+// copy is written again only two rows on).
 template <int NW>
 struct ResScratch {
   float mx[NW];
