@@ -70,8 +70,9 @@ template <int DT>
 constexpr float kSlack = DT == kF16 ? 2.0f : 8.0f;
 template <int DT>
 constexpr float kLog2WeightScale = DT == kF16 ? 12.0f : 0.0f;
-// rows whose reference exceeds this in magnitude take exp(x - mr) with an
-// explicit subtraction; below it, 2^(x log2e + c) with one constant per row
+// below this reference magnitude a row's weights are 2^(x log2e + c) with
+// one rounded constant c per row; once a row of a wave reaches it, the wave
+// subtracts the reference explicitly for the rest of its tile
 constexpr float kBiasedMax = 32768.0f;
 
 // s_waitcnt immediate that waits until at most n vector-memory operations of
@@ -294,7 +295,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       }
     };
 
+    // m: the running maximum; l: the running sum; (ch, cl): the exponent
+    // constant (as an unevaluated sum) that l and the accumulators carry
     float m = -kInf, l = 0.0f;
+    uint64_t wide_rows = 0;  // lanes whose reference reached 2^15 this tile (the wave's form)
     f32x16 acc[NT];
 #pragma unroll
     for (int i = 0; i < NT; ++i) acc[i] = f32x16{};
@@ -388,34 +392,64 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       load_scores(blk, x);
       // The reference moves to the block's maximum when that exceeds it by
       // more than the slack (or is NaN / +inf, which poisons the row, or
-      // the row was empty so far); the old state then takes exp(m - m'),
-      // exactly 1 when nothing moves.
+      // the row was empty so far).
       float bm = -kInf;
 #pragma unroll
       for (int i = 0; i < 32; ++i) bm = vmax(bm, x[i]);
       bm = vmax(bm, __shfl_xor(bm, 32));  // the other half of the row
       const float m_new = (bm <= m + kSlack<DT>) ? m : vmax(m, bm);
-      const bool moved = m_new != m && m > -kInf;  // an empty state holds zeros
+      // exp(x - m) as 2^(x log2e + c), c = -m log2e plus the log2 of the
+      // fp16 weight scale, rounded once (the folded form). A row with no
+      // finite reference uses 0, so masked lanes (-inf) give 0 without
+      // forming -inf - -inf. Once a row of the wave has a large reference
+      // (|m| >= 2^15, rare) the wave subtracts the reference explicitly
+      // instead, for the rest of the tile (the explicit form): x - m is exact
+      // wherever the weight is not negligible, so the constant is then
+      // exactly the scale's log2 minus m log2e.
+      //
+      // The state (l and the accumulators) carries the constant its weights
+      // were formed with. When the reference moves, the state takes 2^(c' -
+      // c), the difference of the two constants as they were formed: in the
+      // folded form that is the difference of the two rounded constants, so
+      // earlier and later terms keep one common factor, which cancels in o /
+      // l. When the wave turns to the explicit form, the state first takes
+      // the rounding error of its folded constant, 2^(exact - rounded), the
+      // exact constant held as an unevaluated sum (the product split by a
+      // fused multiply-add, the difference by a two-sum). Either factor is
+      // exactly 1 when nothing changes; an empty state holds zeros and is
+      // left alone.
+      const float mu = __builtin_fabsf(m_new) < kInf ? m_new : 0.0f;
+      const bool was_wide = wide_rows != 0;
+      wide_rows |= __ballot(!(__builtin_fabsf(mu) < kBiasedMax));
+      const bool wide = wide_rows != 0;
+      float c = kLog2WeightScale<DT> - mu * kLog2e;
+      if (wide) {
+        if (!was_wide) {
+          const float mo = __builtin_fabsf(m) < kInf ? m : 0.0f;
+          const float mp = mo * kLog2e;
+          const float e = __builtin_fmaf(mo, kLog2e, -mp);  // mo log2e = mp + e
+          const float h = kLog2WeightScale<DT> - mp;         // the folded constant
+          const float bb = h - kLog2WeightScale<DT>;         // two-sum of the scale and -mp
+          const float lo = ((kLog2WeightScale<DT> - (h - bb)) + (-mp - bb)) - e;
+          const float alpha = m > -kInf ? __builtin_amdgcn_exp2f(lo) : 1.0f;  // exact = h + lo
+          l *= alpha;
+#pragma unroll
+          for (int i = 0; i < NT; ++i) acc[i] *= alpha;
+        }
+#pragma unroll
+        for (int i = 0; i < 32; ++i) x[i] -= mu;
+        c = kLog2WeightScale<DT>;
+      }
+      const bool moved = m_new != m && m > -kInf;
       if (__ballot(moved) != 0) {
-        const float alpha = moved ? __builtin_amdgcn_exp2f((m - m_new) * kLog2e) : 1.0f;
+        const float mo = __builtin_fabsf(m) < kInf ? m : 0.0f;
+        const float d = wide ? (mo - mu) * kLog2e : c - (kLog2WeightScale<DT> - mo * kLog2e);
+        const float alpha = moved ? __builtin_amdgcn_exp2f(d) : 1.0f;
         l *= alpha;
 #pragma unroll
         for (int i = 0; i < NT; ++i) acc[i] *= alpha;
       }
       m = m_new;
-      // exp(x - m) as 2^(x log2e + c), c = -m log2e plus the log2 of the
-      // fp16 weight scale: the rounding of c scales the row's weights and
-      // its l alike and cancels in o / l. A row with no finite reference
-      // uses 0, so masked lanes (-inf) give 0 without forming -inf - -inf; a
-      // wave holding a row with a large reference (|m| >= 2^15, rare)
-      // subtracts it explicitly instead.
-      const float mu = __builtin_fabsf(m) < kInf ? m : 0.0f;
-      float c = kLog2WeightScale<DT> - mu * kLog2e;
-      if (__ballot(!(__builtin_fabsf(mu) < kBiasedMax)) != 0) {
-#pragma unroll
-        for (int i = 0; i < 32; ++i) x[i] -= mu;
-        c = kLog2WeightScale<DT>;
-      }
 
       // the products of k-step t run while the weights of k-step t + 1 form
       const int vst = blk & 1;

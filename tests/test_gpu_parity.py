@@ -1315,6 +1315,59 @@ def test_weighted_rows_reference_paths(dtype):
         banner(f"{what}: {res}")
 
 
+def _step16(v: float, dtype: str, up: bool) -> float:
+    """The neighbour of v (a value of the 16-bit format) above it (up) or below it."""
+    if dtype == "f16":
+        return float(np.nextafter(np.float16(v), np.float16(np.inf if up else -np.inf)))
+    bits = int(np.array([v], dtype=np.float32).view(np.uint32)[0]) >> 16
+    bits += 1 if (v >= 0) == up else -1
+    return float(np.array([bits << 16], dtype=np.uint32).view(np.float32)[0])
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_weighted_rows_reference_moves_at_large_maxima(dtype):
+    """Rows whose maximum lies between 2^8 and 2^13 in magnitude (below the
+    explicit-subtraction threshold) and moves past the slack once, in the
+    last block, after as many columns at the old maximum as make the terms
+    before and after the move weigh the same; the values are +1 before the
+    move and -1 at it, so the output is near 0 and any disagreement between
+    the rescaling of the earlier terms and the constants their weights were
+    formed with shows in full (a relative mismatch e gives an error of about
+    e / 2 against a sum of |weight x value| of 1). Rows of 256 columns in
+    fp16; bf16's coarser spacing makes every move there at least 10, so its
+    rows are long (165,000 columns)."""
+    rpg, groups, d = 16, 2, 64
+    cols = 256 if dtype == "f16" else 165_000
+    slack = 2.0 if dtype == "f16" else 8.0
+    rows = rpg * groups
+    bases = ([600.0, 1000.0, 1500.0, 2500.0, 3000.0, 5000.0, 6000.0, 7000.0] if dtype == "f16"
+             else [300.0, 400.0, 500.0, 600.0, 700.0, 800.0, 900.0, 1000.0])
+    top_col = cols - 6
+    x = np.empty((rows, cols))
+    for r in range(rows):
+        b0 = bases[r % len(bases)] * (1.0 if (r // len(bases)) % 2 == 0 else -1.0)
+        base = float(oracle.decode(W.to_format(np.array([b0]), dtype), dtype)[0])
+        top = base
+        while top <= base + slack:
+            top = _step16(top, dtype, up=True)
+        n_old = int(round(np.exp(top - base)))
+        assert 1 <= n_old < top_col - 64  # the move lands in a later block than every earlier term
+        x[r] = float(oracle.decode(W.to_format(np.array([base - 100.0]), dtype), dtype)[0])  # weight ~e^-100
+        x[r, :n_old] = base
+        x[r, top_col] = top
+    s = W.to_format(x, dtype)
+    vrow = np.full(cols, 0.25)
+    vrow[: top_col - 64] = 1.0
+    vrow[top_col] = -1.0
+    v = W.to_format(np.broadcast_to(vrow[None, :, None], (groups, cols, d)).copy(), dtype)
+    what = f"weighted reference moves at large maxima {dtype} cols={cols}"
+    banner(what)
+    out = run_weighted(s, v, dtype, W.MaskSpec("none"))
+    ref, st, scale = weighted_reference(s, v, dtype, rpg, None)
+    res = check_weighted(out, dtype, ref, st, scale, what)
+    banner(f"{what}: {res}")
+
+
 def test_weighted_rows_causal_full():
     """The attention workload at full size: 256 groups of 2048 x 2048
     bf16 causal scores (with their injected policy rows) and per group 2048
