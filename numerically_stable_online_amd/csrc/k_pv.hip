@@ -132,6 +132,17 @@ __device__ __forceinline__ int v_pos(int row, int chunk) {
   }
 }
 
+// The value of lane i ^ 32 beside lane i's own: v_permlane32_swap exchanges
+// the upper 32 lanes of its first operand with the lower 32 of its second,
+// so with both holding v, the first becomes (v[0..31], v[0..31]) and the
+// second (v[32..63], v[32..63]); one VALU instruction instead of an LDS
+// permute. The wait states cover a VALU write of either operand just before.
+__device__ __forceinline__ void halves(float v, float& lo_half, float& hi_half) {
+  lo_half = v;
+  hi_half = v;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(lo_half), "+v"(hi_half));
+}
+
 // Two fp32 weights as 16-bit hi + lo pairs (p = hi + lo to about 16 bits),
 // packed two to a word: one packed conversion for the high parts, the exact
 // residuals, one packed conversion for the low parts.
@@ -396,7 +407,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       float bm = -kInf;
 #pragma unroll
       for (int i = 0; i < 32; ++i) bm = vmax(bm, x[i]);
-      bm = vmax(bm, __shfl_xor(bm, 32));  // the other half of the row
+      {
+        float a0, a1;
+        halves(bm, a0, a1);  // the two halves of the row
+        bm = vmax(a0, a1);
+      }
       const float m_new = (bm <= m + kSlack<DT>) ? m : vmax(m, bm);
       // exp(x - m) as 2^(x log2e + c), c = -m log2e plus the log2 of the
       // fp16 weight scale, rounded once (the folded form). A row with no
