@@ -306,9 +306,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       }
     };
 
-    // m: the running maximum; l: the running sum; (ch, cl): the exponent
-    // constant (as an unevaluated sum) that l and the accumulators carry
-    float m = -kInf, l = 0.0f;
+    float m = -kInf, l = 0.0f;  // the running maximum (the reference) and sum
     uint64_t wide_rows = 0;  // lanes whose reference reached 2^15 this tile (the wave's form)
     f32x16 acc[NT];
 #pragma unroll
