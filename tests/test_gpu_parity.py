@@ -1368,6 +1368,35 @@ def test_weighted_rows_reference_moves_at_large_maxima(dtype):
     banner(f"{what}: {res}")
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_weighted_rows_switch_to_explicit_form(dtype):
+    """A wave turns to the explicit subtraction in the middle of its tile:
+    one row in every 32 (one per wave) jumps past 2^15 (to 40000) at column
+    256, while the other rows hold one value throughout (20272 in fp16,
+    21248 in bf16: values whose exponent constant, rounded once, is off from
+    the exact one by nearly 2^-10, the most in that range). Their state is
+    carried over to the explicit form at the switch; with values +1 before
+    column 256 and -1 from it on, the two halves of the row cancel, so an
+    error in that conversion (a relative 6.6e-4 if it were left out) shows
+    in full against the oracle. Rows whose reference starts at -40000 and
+    climbs to 0 (the explicit form throughout) ride along."""
+    rpg, groups, cols, d, cut = 128, 2, 512, 64, 256
+    rows = rpg * groups
+    x = np.full((rows, cols), 20272.0 if dtype == "f16" else 21248.0)
+    x[7::32, cut:] = 40000.0
+    x[19::64, : cut - 128] = -40000.0
+    x[19::64, cut - 128 :] = 0.0
+    s = W.to_format(x, dtype)
+    vrow = np.where(np.arange(cols) < cut, 1.0, -1.0)
+    v = W.to_format(np.broadcast_to(vrow[None, :, None], (groups, cols, d)).copy(), dtype)
+    what = f"weighted switch to the explicit form {dtype}"
+    banner(what)
+    out = run_weighted(s, v, dtype, W.MaskSpec("none"))
+    ref, st, scale = weighted_reference(s, v, dtype, rpg, None)
+    res = check_weighted(out, dtype, ref, st, scale, what)
+    banner(f"{what}: {res}")
+
+
 def test_weighted_rows_causal_full():
     """The attention workload at full size: 256 groups of 2048 x 2048
     bf16 causal scores (with their injected policy rows) and per group 2048
