@@ -192,3 +192,24 @@ def test_policy_rows():
     p = np.exp(np.array([3.0, 1.0]) - 3.0) / np.exp(np.array([3.0, 1.0]) - 3.0).sum()
     assert np.allclose(out[3], p[0] * v[3, 0] + p[1] * v[3, 2], rtol=1e-15)
     assert np.array_equal(out[4], v[4, 0].astype(np.float64))
+
+
+@pytest.mark.parametrize("offset", [16384.0, -16384.0, 2.0 ** 20])
+def test_shift_invariance_at_large_references(offset):
+    # A common shift of a row's scores cancels in o / l ("Online stable
+    # softmax", deriving the update: any common shift cancels). Scores on a
+    # grid of 2^-3 within [-8, 8] stay exact in float32 after adding the
+    # offset, so the shifted rows must give the same sums to double rounding,
+    # with references far past the range where a float exponent would
+    # overflow.
+    rng = np.random.default_rng(43)
+    rows, cols, d, rpg = 6, 90, 7, 3
+    s = (np.round(rng.uniform(-8, 8, (rows, cols)) * 8) / 8).astype(np.float32)
+    shifted = (s.astype(np.float64) + offset).astype(np.float32)
+    assert np.array_equal(shifted.astype(np.float64) - offset, s.astype(np.float64))  # the shift is exact
+    v = rng.standard_normal((rows // rpg, cols, d)).astype(np.float32)
+    mask = W.MaskSpec("causal", causal_period=rpg, causal_offset=80)
+    o1, st1 = oracle.softmax_weighted_rows(s, v, "f32", rpg, mask)
+    o2, st2 = oracle.softmax_weighted_rows(shifted, v, "f32", rpg, mask)
+    assert np.array_equal(st1, st2)
+    assert np.allclose(o2, o1, rtol=1e-14, atol=1e-15)
