@@ -1368,6 +1368,23 @@ def test_weighted_rows_reference_moves_at_large_maxima(dtype):
     banner(f"{what}: {res}")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_weighted_rows_few_columns(dtype):
+    """The matrix-core path on rows of one 16-byte chunk up to one chunk past
+    a block (columns are a multiple of 8): 8, 16, 56, 64 and 72 columns (the
+    value rows past the end re-read the last one with weight 0), 16 and 129
+    rows per group, with the policy rows, and causal and valid-length
+    masks."""
+    rng = np.random.default_rng(560)
+    for cols in (8, 16, 56, 64, 72):
+        for rpg, mask_kind in ((16, "none"), (129, "causal"), (16, "valid_len")):
+            s, v, mask = _weighted_case(rng, dtype, rpg, 3, cols, 32, mask_kind)
+            what = f"weighted few columns {dtype} cols={cols} rpg={rpg} {mask_kind}"
+            out = run_weighted(s, v, dtype, mask)
+            ref, st, scale = weighted_reference(s, v, dtype, rpg, mask)
+            check_weighted(out, dtype, ref, st, scale, what)
+
+
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 def test_weighted_rows_switch_to_explicit_form(dtype):
     """A wave turns to the explicit subtraction in the middle of its tile:
