@@ -151,7 +151,8 @@ def check_log(y_raw, dtype, logp, lse_ref, lse_got, cls, st, x_float, what=""):
     assert (bits[zero] == NEG_INF_BITS[dtype]).all(), f"{what}: masked lanes must be -inf"
     assert (bits[nan] == NAN_BITS[dtype]).all(), f"{what}: NaN rows must be the canonical NaN"
     lse_b = np.broadcast_to(np.where(st == oracle.ROW_OK, lse_ref, 0.0)[:, None], logp.shape)
-    scale = np.maximum(1.0, np.maximum(np.abs(x_float.astype(np.float64)), np.abs(lse_b)))
+    with np.errstate(invalid="ignore"):  # NaN lanes of policy rows; only numeric lanes use the scale
+        scale = np.maximum(1.0, np.maximum(np.abs(x_float.astype(np.float64)), np.abs(lse_b)))
     y = y_raw.astype(np.float64) if dtype == "f32" else \
         (y_raw.view(np.float16).astype(np.float64) if dtype == "f16"
          else (y_raw.astype(np.uint32) << 16).view(np.float32).astype(np.float64))
