@@ -1385,6 +1385,29 @@ def test_weighted_rows_few_columns(dtype):
             check_weighted(out, dtype, ref, st, scale, what)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_weighted_rows_output_8_byte_aligned(dtype):
+    """An output 8 bytes off a 16-byte boundary (the least alignment the
+    call takes) is written by the kernel's 8-byte stores instead of its
+    16-byte ones: bitwise the same values as an aligned output, for every
+    value width, with the policy rows."""
+    rng = np.random.default_rng(570)
+    for d in (32, 64, 128):
+        s, v, mask = _weighted_case(rng, dtype, 130, 2, 200, d, "causal")
+        sd = to_device(s, dtype)
+        vd = to_device(v.reshape(-1, d), dtype).view(v.shape)
+        aligned = smx.softmax_weighted_rows(sd, vd, **mask_kwargs(mask))
+        buf = torch.full((s.shape[0] * d + 4,), 3.0, dtype=TORCH_DTYPE[dtype], device="cuda")
+        off = buf[4:].view(s.shape[0], d)
+        assert off.data_ptr() % 16 == 8
+        smx.softmax_weighted_rows(sd, vd, off, **mask_kwargs(mask))
+        torch.cuda.synchronize()
+        assert torch.equal(off.view(torch.int16), aligned.view(torch.int16)), f"d={d}"
+        assert (buf[:4] == 3.0).all(), "no write before the output"
+        ref, st, scale = weighted_reference(s, v, dtype, 130, mask)
+        check_weighted(to_host(off, dtype), dtype, ref, st, scale, f"weighted 8-byte-aligned out {dtype} d={d}")
+
+
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 def test_weighted_rows_switch_to_explicit_form(dtype):
     """A wave turns to the explicit subtraction in the middle of its tile:
