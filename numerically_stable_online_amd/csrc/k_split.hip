@@ -130,11 +130,11 @@ __global__ __launch_bounds__(kThreads) void k_stats(RowArgs a, int64_t chunk, in
       if (m_new != -kInf) {
         // correct the running sum, then add this round against m_new; the
         // round's terms are summed as a tree in registers
-        const float lo = m_new - 126.0f;
+        const double m64 = (double)m_new;
 #pragma unroll
         for (int i = 0; i < VPT * E; ++i) {
           if constexpr (ACC) {
-            v[i] = exp_acc_sum_clamped(vmax(v[i], lo), m_new);  // NaN stays NaN: such a chunk is poisoned
+            v[i] = exp_acc_sum(v[i], m64);  // a NaN lane adds 0 here; m_new carries it into the poison flag
           } else {
             v[i] = __builtin_amdgcn_exp2f((v[i] - m_new) * kLog2e);
           }

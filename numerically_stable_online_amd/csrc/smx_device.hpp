@@ -266,63 +266,26 @@ __device__ __forceinline__ void row_targets(const int32_t* target, int64_t r0, i
 // ---------------------------------------------------------------------------
 
 // fp32 I/O: exp(x - m) * 2^64 from the hardware base-2 exponential
-// (v_exp_f32, measured within 0.79 ulp on gfx950 for normal results) with a
-// compensated argument: x - m is carried exactly as dh + dl, t = (x - m) log2 e
-// as th + tl (th = fl(dh log2e), tl the exact product error plus the low-order
-// terms), and e = 2^th (1 + tl ln 2) with one fused multiply-add. Arguments
-// below -64 are raised by 64 before the exponential and results above are
-// scaled by 2^64 afterwards, so the value is a normal fp32 number down to
-// exp(-131) (v_exp_f32 itself flushes subnormal results). Masked lanes
-// (x = -inf) and d < -120 give exactly 0.
-__device__ __forceinline__ float exp_acc_b64(float x, float m) {
-  constexpr float kLog2eLo = 1.925963033500011e-08f;  // log2 e - kLog2e
-  constexpr float kLn2 = 0.693147182464599609375f;
-  float dh, dl;
-  two_diff(x, m, dh, dl);
-  const float th = dh * kLog2e;
-  float tl = __builtin_fmaf(dh, kLog2e, -th);
-  tl = __builtin_fmaf(dh, kLog2eLo, tl);
-  tl = __builtin_fmaf(dl, kLog2e, tl);
-  const bool deep = th < -64.0f;
-  const float e = __builtin_amdgcn_exp2f(deep ? th + 64.0f : th);
-  const float eb = deep ? e : e * 18446744073709551616.0f;  // * 2^64
-  const float r = __builtin_fmaf(eb, tl * kLn2, eb);
-  return dh >= -120.0f ? r : 0.0f;
-}
+// (v_exp_f32, measured within 0.79 ulp on gfx950 for normal results) with
+// the difference x - m taken exactly in fp64 and the rest of the argument
+// carried past the exponential as a factor 1 + r (exp_dd_b64 in
+// smx_math.hpp). The 2^64 scale rides in the exponential's argument, so the
+// value is a normal fp32 number down to exp(-131) (v_exp_f32 itself flushes
+// subnormal results). Masked lanes (x = -inf) and d < -120 give exactly 0.
+// fp64 adds, fused multiply-adds and conversions issue at the fp32 rate on
+// CDNA4: twelve instructions, where the same accuracy in fp32 alone (an
+// exact two-difference and a three-term product error) took nineteen.
+struct HwExp2 {
+  __device__ float operator()(float t) const { return __builtin_amdgcn_exp2f(t); }
+};
+__device__ __forceinline__ float exp_acc_b64(float x, float m) { return exp_dd_b64(x, (double)m, HwExp2{}); }
 
-// The same exponential unscaled, for sums only: results below 2^-126 flush
-// to zero, which changes a sum that holds a term equal to 1 by less than
-// 2^-126 relative.
-__device__ __forceinline__ float exp_acc_sum(float x, float m) {
-  constexpr float kLog2eLo = 1.925963033500011e-08f;
-  constexpr float kLn2 = 0.693147182464599609375f;
-  float dh, dl;
-  two_diff(x, m, dh, dl);
-  const float th = dh * kLog2e;
-  float tl = __builtin_fmaf(dh, kLog2e, -th);
-  tl = __builtin_fmaf(dh, kLog2eLo, tl);
-  tl = __builtin_fmaf(dl, kLog2e, tl);
-  const float e = __builtin_amdgcn_exp2f(th);
-  const float r = __builtin_fmaf(e, tl * kLn2, e);
-  return dh >= -120.0f ? r : 0.0f;
-}
-
-// exp_acc_sum for a value already clamped to at least m - 126: no lane is
-// -inf (masked lanes arrive as m - 126), so no NaN arises, and every
-// exponential below exp(-120) is exactly 0 either way (2^-173 and below
-// underflow), so no select is needed.
-__device__ __forceinline__ float exp_acc_sum_clamped(float x, float m) {
-  constexpr float kLog2eLo = 1.925963033500011e-08f;
-  constexpr float kLn2 = 0.693147182464599609375f;
-  float dh, dl;
-  two_diff(x, m, dh, dl);
-  const float th = dh * kLog2e;
-  float tl = __builtin_fmaf(dh, kLog2e, -th);
-  tl = __builtin_fmaf(dh, kLog2eLo, tl);
-  tl = __builtin_fmaf(dl, kLog2e, tl);
-  const float e = __builtin_amdgcn_exp2f(th);
-  return __builtin_fmaf(e, tl * kLn2, e);
-}
+// The same exponential unscaled, for sums only (exp_dd_sum in smx_math.hpp):
+// results below 2^-126 flush to zero, which changes a sum that holds a term
+// equal to 1 by less than 2^-126 relative; x - m is clamped at -160 in fp64,
+// so -inf lanes give 0 and a NaN lane gives 0 (the caller's maximum carries
+// NaN into the row's poison flag). Ten instructions. m64 is (double)m.
+__device__ __forceinline__ float exp_acc_sum(float x, double m64) { return exp_dd_sum(x, m64, HwExp2{}); }
 
 // 16-bit I/O: the hardware base-2 exponential, v_exp_f32. Its argument
 // carries a relative error of about 2^-23 |x - m|, far below half an ulp of

@@ -1,9 +1,10 @@
 // smx_math.hpp — scalar arithmetic shared by the row-softmax kernels.
 //
-// Everything here is plain IEEE fp32 arithmetic (add, multiply, fused
-// multiply-add, round-to-integer, scale by a power of two), so the same code
-// compiles for gfx950 and, for testing, for the host CPU, where it gives the
-// same bits.
+// Everything here is plain IEEE fp32 and fp64 arithmetic (add, multiply,
+// fused multiply-add, conversion, round-to-integer, scale by a power of
+// two), so the same code compiles for gfx950 and, for testing, for the host
+// CPU, where it gives the same bits (the hardware base-2 exponential, which
+// the exp_dd forms take as an argument, aside).
 #pragma once
 
 #include <stdint.h>
@@ -87,6 +88,49 @@ SMX_HD float exp_diff(float a, float b) {
   two_diff(a, b, hi, lo);
   if (!(hi >= -120.0f)) return 0.0f;
   return exp_biased64(hi, lo) * 5.42101086242752217e-20f;  // * 2^-64
+}
+
+// exp(x - m) for fp32 x <= m, with the difference taken in fp64, where it is
+// exact (two fp32 values need at most 53 bits unless m is tiny and x far
+// below it, and then it is rounded to 2^-53 relative, far below what the
+// result keeps). An fp32 value t near (x - m) log2 e (any nearby value serves)
+// is the point the base-2 exponential is taken at, and the rest of the
+// argument, r = (x - m) - t ln 2, is formed in fp64 from the exact product
+// and rounded once. |r| < 2^-15, so 2^t (1 + r) misses e^(x - m) by under
+// 2^-31 relative: the result carries the base-2 exponential's own error and
+// one rounding. The same splitting as the Cody-Waite step above, with fp64
+// instead of a two-constant ln 2 and a two-difference; exp2 is the hardware
+// base-2 exponential on the GPU (a correctly rounded stand-in on the host).
+constexpr double kLn2d = 0.6931471805599453094;      // ln 2 to double precision
+constexpr float kLog2eF = 1.44269502162933349609375f;  // fl(log2 e)
+
+// For sums: exp(x - m), unscaled. x - m is clamped at -160 in fp64 (masked
+// lanes, -inf, and values that far below the maximum give exactly 0, since
+// 2^(-160 log2 e) flushes), where the clamp is exact even when |m| is so
+// large that m - 160 would round back to m in fp32. A NaN x gives 0: the
+// caller's maximum carries NaN into the row's poison flag.
+template <class Exp2>
+SMX_HD float exp_dd_sum(float x, double m64, Exp2 exp2) {
+  const double d = __builtin_fmax((double)x - m64, -160.0);
+  const float t = (float)d * kLog2eF;
+  const float r = (float)__builtin_fma((double)t, -kLn2d, d);
+  const float e = exp2(t);
+  return __builtin_fmaf(e, r, e);
+}
+
+// exp(x - m) * 2^64, a normal fp32 number down to x - m = -120 (as
+// exp_biased64), and exactly 0 below that, for -inf and for NaN. The base-2
+// argument carries the bias: tb is near (x - m) log2 e + 64, rounded once,
+// and r = (x - m) + 64 ln 2 - tb ln 2, so 2^tb (1 + r) = e^(x - m) 2^64
+// exactly up to r's truncation.
+template <class Exp2>
+SMX_HD float exp_dd_b64(float x, double m64, Exp2 exp2) {
+  const double d = (double)x - m64;
+  const float tb = __builtin_fmaf((float)d, kLog2eF, 64.0f);
+  const float r = (float)__builtin_fma((double)tb, -kLn2d, d + 64.0 * kLn2d);
+  const float e = exp2(tb);
+  const float v = __builtin_fmaf(e, r, e);
+  return d >= -120.0 ? v : 0.0f;
 }
 
 // Nearest-even rounding of a finite, non-negative fp32 value to bfloat16,

@@ -2,7 +2,10 @@
 // against libm's double-precision exp. Prints one line of results.
 //   check_smx_math <stride>
 // walks every stride-th fp32 value d in [-120, 0] with dl = 0, plus a seeded
-// set of (dh, dl) pairs formed as exact differences of two fp32 values.
+// set of (dh, dl) pairs formed as exact differences of two fp32 values; then
+// the fp64-difference forms (exp_dd_b64, exp_dd_sum) on the same walk and on
+// seeded pairs (x, m) of every magnitude, with a correctly rounded base-2
+// exponential standing in for the hardware one, and their special cases.
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
@@ -62,7 +65,57 @@ int main(int argc, char** argv) {
     uint32_t want = dist_a < dist_b ? a : (dist_b < dist_a ? b : ((a & 1) ? b : a));
     if (smx::bf16_rne(f) != want) ++bad_bf16;
   }
-  std::printf("n=%ld max_ulp=%.4f at d=%.9g max_ulp_pair=%.4f bad_identity=%d bad_bf16=%d\n", n, worst,
-              worst_d, worst2, bad_identity, bad_bf16);
+  // exp_dd_b64 / exp_dd_sum: every stride-th d in [-120, 0] against m = 0,
+  // and seeded (x, m) pairs whose magnitudes run from 2^-30 to 2^100, x
+  // within 120 below m; errors in ulps of the correctly rounded value
+  struct Exp2Ref {
+    float operator()(float t) const { return (float)std::exp2((double)t); }
+  };
+  double worst_dd = 0.0, worst_dd_sum = 0.0;
+  for (uint64_t b = lo_bits; b <= hi_bits; b += stride) {
+    float d = smx::u2f((uint32_t)b);
+    double ref = std::exp((double)d);
+    worst_dd = std::fmax(worst_dd, ulp_err(smx::exp_dd_b64(d, 0.0, Exp2Ref{}), std::ldexp(ref, 64)));
+    if (d >= -87.0f) worst_dd_sum = std::fmax(worst_dd_sum, ulp_err(smx::exp_dd_sum(d, 0.0, Exp2Ref{}), ref));
+  }
+  for (int i = 0; i < 2000000; ++i) {
+    s = s * 1103515245u + 12345u;
+    const int ex = (int)((s >> 8) % 131) - 30;
+    s = s * 1103515245u + 12345u;
+    float m = std::ldexp((float)((s >> 8) & 0xFFFFFF) / 16777216.0f + 0.5f, ex);
+    if (s & 1) m = -m;
+    s = s * 1103515245u + 12345u;
+    float x = m - (float)((s >> 8) % 1000000) * 1.2e-4f;  // fp32-rounded: x - m need not be that step
+    if (!(x <= m)) continue;
+    double d = (double)x - (double)m;  // exact for these magnitudes
+    if (d < -120.0) continue;
+    double ref = std::exp(d);
+    worst_dd = std::fmax(worst_dd, ulp_err(smx::exp_dd_b64(x, (double)m, Exp2Ref{}), std::ldexp(ref, 64)));
+    if (d >= -87.0) worst_dd_sum = std::fmax(worst_dd_sum, ulp_err(smx::exp_dd_sum(x, (double)m, Exp2Ref{}), ref));
+  }
+  // special cases: the maximum itself gives exactly 1 (2^64 scaled), at any
+  // magnitude; lanes far below it (also where m - 160 rounds to m in fp32),
+  // -inf and NaN give exactly 0
+  int bad_dd = 0;
+  const float big = 4294967296.0f;  // 2^32: m - 160 rounds back to m in fp32
+  const float ms[] = {0.0f, 1.5f, -3.0f, big, -big, 1e30f, -3e38f, 3e38f};
+  for (float m : ms) {
+    bad_dd += smx::exp_dd_sum(m, (double)m, Exp2Ref{}) != 1.0f;
+    bad_dd += smx::exp_dd_b64(m, (double)m, Exp2Ref{}) != 18446744073709551616.0f;
+    bad_dd += smx::exp_dd_sum(-INFINITY, (double)m, Exp2Ref{}) != 0.0f;
+    bad_dd += smx::exp_dd_b64(-INFINITY, (double)m, Exp2Ref{}) != 0.0f;
+    bad_dd += smx::exp_dd_sum(NAN, (double)m, Exp2Ref{}) != 0.0f;
+    bad_dd += smx::exp_dd_b64(NAN, (double)m, Exp2Ref{}) != 0.0f;
+    const float below = std::nextafter(m, -INFINITY);  // one fp32 step below m
+    const double gap = (double)below - (double)m;
+    if (gap < -160.0) {
+      bad_dd += smx::exp_dd_sum(below, (double)m, Exp2Ref{}) != 0.0f;
+      bad_dd += smx::exp_dd_b64(below, (double)m, Exp2Ref{}) != 0.0f;
+    }
+  }
+  bad_dd += smx::exp_dd_sum(big - 512.0f, (double)big, Exp2Ref{}) != 0.0f;
+  std::printf("n=%ld max_ulp=%.4f at d=%.9g max_ulp_pair=%.4f bad_identity=%d bad_bf16=%d max_ulp_dd=%.4f "
+              "max_ulp_dd_sum=%.4f bad_dd=%d\n",
+              n, worst, worst_d, worst2, bad_identity, bad_bf16, worst_dd, worst_dd_sum, bad_dd);
   return 0;
 }

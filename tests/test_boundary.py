@@ -228,7 +228,11 @@ def test_kernel_arithmetic_on_host(tmp_path):
     """The kernels' scalar arithmetic built for the CPU: the fp32 exponential
     is within one ulp of libm's double exp over [-120, 0] (every 8th float,
     and exact differences x - m with a low part), merge identities are exact,
-    and bf16 rounding is nearest-even."""
+    and bf16 rounding is nearest-even. The fp64-difference exponentials, with
+    a correctly rounded base-2 exponential standing in for the hardware one,
+    are within one ulp (plus 2^-31 relative) over the same walk and over pairs (x, m) of every
+    magnitude, give 1 at the maximum and 0 for -inf, NaN and lanes far below
+    it, also where m - 160 rounds back to m in fp32 (|m| >= 2^31)."""
     exe = tmp_path / "check_smx_math"
     subprocess.run(["g++", "-std=c++20", "-O2", "-ffp-contract=off",
                     f"-I{ROOT}/numerically_stable_online_amd/csrc",
@@ -237,6 +241,12 @@ def test_kernel_arithmetic_on_host(tmp_path):
     vals = dict(kv.split("=") for kv in out.split() if "=" in kv)
     assert float(vals["max_ulp"]) < 1.0 and float(vals["max_ulp_pair"]) < 1.0, out
     assert vals["bad_identity"] == "0" and vals["bad_bf16"] == "0", out
+    # the fp64-difference forms: a correctly rounded base-2 exponential (half
+    # an ulp) and the final rounding (half an ulp) bound them by one ulp plus
+    # r's truncation (2^-31 relative) here; the walk reaches 0.9998. The
+    # hardware exponential's 0.79 ulp makes the bound about 1.3 on the GPU
+    assert float(vals["max_ulp_dd"]) < 1.01 and float(vals["max_ulp_dd_sum"]) < 1.01, out
+    assert vals["bad_dd"] == "0", out
 
 
 def test_m0_feeds_only_its_direct_loads(tmp_path):

@@ -384,6 +384,29 @@ def test_large_maxima_switch_the_exponential(dtype):
         check(y, dtype, p, cls, st, f"{dtype} large maxima path={path}")
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_maxima_beyond_2_31(dtype):
+    """Rows whose maximum is 2^31 or more in magnitude, where m - 160 rounds
+    back to m in fp32: lanes one or more format steps below the maximum lie
+    thousands below it and must give exactly 0 (not 1), and the lanes equal
+    to the maximum share the row, on every path, the split path with several
+    chunks per row."""
+    rng = np.random.default_rng(91)
+    rows, cols = 8, 1024
+    big = [2.0 ** 31, 2.0 ** 32, -2.0 ** 32, 1e30, -1e30, 3e38, 2.0 ** 40, -2.0 ** 31]
+    step = 2.0 ** -21 if dtype == "f32" else 2.0 ** -6  # at least one step of the format
+    a = np.empty((rows, cols))
+    for r, b in enumerate(big):
+        k = rng.integers(0, 4, cols)
+        a[r] = b * (1.0 - step * k) if b > 0 else b * (1.0 + step * k)
+    x = W.to_format(a, dtype)
+    p, cls, st = oracle.softmax_rows(x, dtype, W.MaskSpec())
+    for path in ("wave", "lds", "split"):
+        banner(f"{dtype} maxima beyond 2^31 path={path}")
+        y = run_rows(x, dtype, W.MaskSpec(), path=path, chunk_cols=256 if path == "split" else 0)
+        check(y, dtype, p, cls, st, f"{dtype} maxima beyond 2^31 path={path}")
+
+
 @pytest.mark.parametrize("dtype", W.DTYPES)
 def test_odd_shapes_masks_paths(dtype):
     rng = np.random.default_rng(100)
