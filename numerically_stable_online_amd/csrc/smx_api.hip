@@ -106,13 +106,15 @@ smx_path choose(int64_t rows, int64_t cols, int dtype, bool vec) {
 }
 
 int64_t default_chunk(int64_t rows, int64_t cols, int dtype, bool vec) {
-  // 64 KiB chunks (several register rounds per workgroup, so the stats pass
-  // overlaps its loads with its arithmetic), halved while the grid has fewer
-  // than 2048 workgroups (8 per CU), never below 64 packs
+  // 32 KiB chunks (two register rounds per thread of the stats pass, both in
+  // flight from the start), halved while the grid has fewer than 1024
+  // workgroups (4 per CU), never below 64 packs. Measured on the split path
+  // against 64 KiB chunks and a floor of 2048 workgroups: 1 to 4 % faster on
+  // every large fp32 and 16-bit shape, 5 % on a few long fp32 rows.
   const int64_t e = vec ? vec_elems(dtype) : 1;
-  int64_t chunk = 65536 / elem_size(dtype);
+  int64_t chunk = 32768 / elem_size(dtype);
   const int64_t floor_chunk = 64 * e;
-  while (chunk > floor_chunk && rows * ((cols + chunk - 1) / chunk) < 2048) chunk /= 2;
+  while (chunk > floor_chunk && rows * ((cols + chunk - 1) / chunk) < 1024) chunk /= 2;
   return chunk;
 }
 

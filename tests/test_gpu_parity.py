@@ -160,14 +160,14 @@ def test_causal_scores_full():
 
 def test_very_long_rows_split():
     """Two fp32 rows of 2^26 lanes (256 MiB each): the automatic path is the
-    split one with 64 KiB chunks, so each row's merge folds 4096 chunk
-    summaries (16 per thread of the merging workgroup); the second row's
+    split one with 32 KiB chunks, so each row's merge folds 8192 chunk
+    summaries (32 per thread of the merging workgroup); the second row's
     valid length ends inside a chunk."""
     cols = 1 << 26
     x = W.random_rows(2, cols, "f32", seed=77, scale=4.0)
     mask = W.MaskSpec("valid_len", valid_len=np.array([cols, cols - 12345], dtype=np.int32))
     assert smx.softmax_select_path(2, cols, "f32") == "split"
-    assert smx.softmax_default_chunk_cols(2, cols, "f32") == 16384
+    assert smx.softmax_default_chunk_cols(2, cols, "f32") == 8192
     banner("two rows of 2^26 lanes, split path")
     y = run_rows(x, "f32", mask)
     r = check_full(x, "f32", mask, y, "very long rows")
