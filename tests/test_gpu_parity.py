@@ -384,13 +384,9 @@ def test_large_maxima_switch_the_exponential(dtype):
         check(y, dtype, p, cls, st, f"{dtype} large maxima path={path}")
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_maxima_beyond_2_31(dtype):
-    """Rows whose maximum is 2^31 or more in magnitude, where m - 160 rounds
-    back to m in fp32: lanes one or more format steps below the maximum lie
-    thousands below it and must give exactly 0 (not 1), and the lanes equal
-    to the maximum share the row, on every path, the split path with several
-    chunks per row."""
+def _beyond_2_31_rows(dtype):
+    """Eight rows whose maxima are 2^31 to 3e38 in magnitude, each lane 0 to
+    3 steps of the format below its row's maximum."""
     rng = np.random.default_rng(91)
     rows, cols = 8, 1024
     big = [2.0 ** 31, 2.0 ** 32, -2.0 ** 32, 1e30, -1e30, 3e38, 2.0 ** 40, -2.0 ** 31]
@@ -399,12 +395,37 @@ def test_maxima_beyond_2_31(dtype):
     for r, b in enumerate(big):
         k = rng.integers(0, 4, cols)
         a[r] = b * (1.0 - step * k) if b > 0 else b * (1.0 + step * k)
-    x = W.to_format(a, dtype)
-    p, cls, st = oracle.softmax_rows(x, dtype, W.MaskSpec())
+    return W.to_format(a, dtype)
+
+
+@pytest.mark.parametrize("op", ["softmax", "log", "xent"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_maxima_beyond_2_31(dtype, op):
+    """Rows whose maximum is 2^31 or more in magnitude, where m - 160 rounds
+    back to m in fp32: lanes one or more format steps below the maximum lie
+    thousands below it and must give exactly 0 (not 1), and the lanes equal
+    to the maximum share the row; the log-softmax's LSE is m + log(count) and
+    the cross-entropy's loss m - x_t + log(count). Every path, the split path
+    with several chunks per row (its stats pass serves all three)."""
+    x = _beyond_2_31_rows(dtype)
+    rows, cols = x.shape
+    mask = W.MaskSpec()
+    if op == "softmax":
+        p, cls, st = oracle.softmax_rows(x, dtype, mask)
+    t = W.class_targets(rows, cols, seed=92)
     for path in ("wave", "lds", "split"):
-        banner(f"{dtype} maxima beyond 2^31 path={path}")
-        y = run_rows(x, dtype, W.MaskSpec(), path=path, chunk_cols=256 if path == "split" else 0)
-        check(y, dtype, p, cls, st, f"{dtype} maxima beyond 2^31 path={path}")
+        chunk = 256 if path == "split" else 0
+        what = f"{dtype} {op} maxima beyond 2^31 path={path}"
+        banner(what)
+        if op == "softmax":
+            y = run_rows(x, dtype, mask, path=path, chunk_cols=chunk)
+            check(y, dtype, p, cls, st, what)
+        elif op == "log":
+            y, lse = run_log(x, dtype, mask, path=path, chunk_cols=chunk)
+            check_log_full(x, dtype, mask, y, lse, what)
+        else:
+            loss, dx = run_xent(x, dtype, t, mask, path=path, chunk_cols=chunk)
+            check_xent_full(x, dtype, t, mask, loss, dx, what)
 
 
 @pytest.mark.parametrize("dtype", W.DTYPES)
