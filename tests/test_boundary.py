@@ -218,7 +218,13 @@ def test_path_choice_and_default_chunk(smx):
     assert smx.softmax_select_path(3, 8192, "f32") == "lds"
     assert smx.softmax_select_path(3, 100001, "f16") == "split"
     c = smx.softmax_default_chunk_cols(64, 1 << 20, "f32")
-    assert c > 0 and c % 4 == 0 and 64 * (-(-(1 << 20) // c)) >= 2048
+    assert c > 0 and c % 4 == 0 and 64 * (-(-(1 << 20) // c)) >= 1024
+    # 32 KiB chunks while the grid keeps at least 1024 workgroups, halved below
+    assert smx.softmax_default_chunk_cols(64, 1 << 20, "f32") == 8192
+    assert smx.softmax_default_chunk_cols(16, 1 << 22, "bf16") == 16384
+    assert smx.softmax_default_chunk_cols(4, 1 << 20, "f32") == 4096   # 1024 workgroups
+    assert smx.softmax_default_chunk_cols(4, 1 << 20, "bf16") == 4096
+    assert smx.softmax_default_chunk_cols(1, 100000, "f16") == 512     # floor: 64 packs of 8
     for rows, cols, dt in ((1, 10, "bf16"), (3, 100000, "f16"), (1000, 5000, "f32")):
         c = smx.softmax_default_chunk_cols(rows, cols, dt)
         assert c >= 64 and c % (4 if dt == "f32" else 8) == 0
