@@ -384,6 +384,29 @@ def test_large_maxima_switch_the_exponential(dtype):
         check(y, dtype, p, cls, st, f"{dtype} large maxima path={path}")
 
 
+@pytest.mark.parametrize("dtype", W.DTYPES)
+def test_ragged_long_rows_default_chunks(dtype):
+    """Rows past the LDS budget that are not a whole number of the default
+    chunk, through the automatic path (the split path at its default chunk
+    width, so the last chunk of each row is partial): 16-byte multiples and
+    odd lengths (no 128-bit accesses), each under every mask kind, with a
+    +inf row and a NaN lane."""
+    rng = np.random.default_rng(95)
+    rows = 9 if dtype == "f32" else 17  # enough chunks for the full default width
+    for cols in (1000032, 1000007):
+        x = W.random_rows(rows, cols, dtype, seed=cols, scale=5.0)
+        inf = W.POS_INF[dtype].view(np.uint32) if dtype == "f32" else W.POS_INF[dtype]
+        W.set_bits(x, 1, cols // 2, dtype, inf)
+        W.set_bits(x, 3, cols - 1, dtype, W.NEG_SNAN[dtype])
+        assert smx.softmax_select_path(rows, cols, dtype) == "split"
+        assert smx.softmax_default_chunk_cols(rows, cols, dtype) == 32768 // W.ITEMSIZE[dtype]
+        for mask in _masks(rows, cols, rng):
+            what = f"{dtype} ragged long rows cols={cols} mask={mask.kind} chunk={smx.softmax_default_chunk_cols(rows, cols, dtype)}"
+            banner(what)
+            y = run_rows(x, dtype, mask)
+            check_full(x, dtype, mask, y, what)
+
+
 def _beyond_2_31_rows(dtype):
     """Eight rows whose maxima are 2^31 to 3e38 in magnitude, each lane 0 to
     3 steps of the format below its row's maximum."""
