@@ -192,7 +192,10 @@ __global__ __launch_bounds__(NT) void k_lds(RowArgs a, int64_t row0) {
       for (int k = 0; k < VPT; ++k)
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-          const float te = exp_hw_b64(v[k][e], mx);
+          // the sum of the cross-entropy and of the log-softmax feeds an fp32
+          // result (the loss, the log-sum-exp): the accurate exponential; the
+          // softmax's 16-bit outputs (rows with |m| >= 2^15) need only this one
+          const float te = EPI == kEpiSoftmax ? exp_hw_b64(v[k][e], mx) : exp_acc_b64(v[k][e], mx);
           if constexpr (EPI != kEpiLogSoftmax) v[k][e] = te;
           s += te;
         }
@@ -200,7 +203,7 @@ __global__ __launch_bounds__(NT) void k_lds(RowArgs a, int64_t row0) {
     total = block_sum<NW>(s, red);
     if constexpr (EPI == kEpiXent) {
       others = total;
-      total = others + exp_hw_b64(xt, mx);
+      total = others + exp_acc_b64(xt, mx);
     }
   }
 

@@ -328,7 +328,8 @@ __global__ __launch_bounds__(NW * 64) void k_lds_res(RowArgs a) {
           l_l = m_l == -kInf ? 0.0f : l_l * __builtin_amdgcn_exp2f(cn - c_l);
           c_l = cn;
         } else {
-          l_l = m_l == -kInf ? 0.0f : l_l * __builtin_amdgcn_exp2f((m_l - mn) * kLog2e);
+          // (the cross-entropy's fp32 loss takes the accurate factor)
+          l_l = m_l == -kInf ? 0.0f : l_l * exp_diff(m_l, mn);
         }
         m_l = mn;
       }
@@ -341,7 +342,7 @@ __global__ __launch_bounds__(NW * 64) void k_lds_res(RowArgs a) {
         } else if constexpr (FOLD) {
           e[q] = exp_hw_bias(v[q], c_l);
         } else {
-          e[q] = exp_hw_b64(v[q], mref);
+          e[q] = exp_acc_b64(v[q], mref);  // the loss or the log-sum-exp: an fp32 result
         }
       }
       if constexpr (ACC) {
@@ -418,12 +419,12 @@ __global__ __launch_bounds__(NW * 64) void k_lds_res(RowArgs a) {
         if constexpr (FOLD) {
           f = m_l == mx ? 1.0f : (m_l == -kInf ? 0.0f : __builtin_amdgcn_exp2f(c_row - c_l));
         } else {
-          f = m_l == mx ? 1.0f : (m_l == -kInf ? 0.0f : __builtin_amdgcn_exp2f((m_l - mx) * kLog2e));
+          f = m_l == mx ? 1.0f : (m_l == -kInf ? 0.0f : exp_diff(m_l, mx));
         }
         total = res_sum(l_l * f, red);
         if constexpr (EPI == kEpiXent) {
           others = total;
-          total = others + exp_hw_b64(xt, mx);
+          total = others + exp_acc_b64(xt, mx);
         }
       }
     }
@@ -496,7 +497,8 @@ __global__ __launch_bounds__(NW * 64) void k_lds_res(RowArgs a) {
     };
     if (fill) {
       Pack<DT, E> f;
-      f.fill(poisoned ? Fmt<DT>::kNaN : ((EPI == kEpiLogSoftmax && !ignored) ? Fmt<DT>::kNegInf : 0u));
+      // an ignored row's gradient is +0.0 even when the row holds NaN or +inf
+      f.fill(ignored ? 0u : (poisoned ? Fmt<DT>::kNaN : (EPI == kEpiLogSoftmax ? Fmt<DT>::kNegInf : 0u)));
       for (int k = 0; k < pw; ++k) {
         put(k, f);
         refill(k, none);

@@ -136,7 +136,8 @@ __global__ __launch_bounds__(kThreads) void k_stats(RowArgs a, int64_t chunk, in
           if constexpr (ACC) {
             v[i] = exp_acc_sum(v[i], m64);  // a NaN lane adds 0 here; m_new carries it into the poison flag
           } else {
-            v[i] = __builtin_amdgcn_exp2f((v[i] - m_new) * kLog2e);
+            // the cross-entropy's sum feeds its fp32 loss: the accurate exponential
+            v[i] = XENT ? exp_acc_sum(v[i], m64) : __builtin_amdgcn_exp2f((v[i] - m_new) * kLog2e);
           }
         }
         l_t = l_t * exp_diff(m_t, m_new) + tree_sum<VPT * E>(v);

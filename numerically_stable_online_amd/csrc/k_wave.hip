@@ -198,7 +198,10 @@ __global__ __launch_bounds__(kThreads) void k_wave(RowArgs a, int64_t rbase, int
         for (int k = 0; k < VPT; ++k)
 #pragma unroll
           for (int e = 0; e < E; ++e) {
-            const float te = exp_hw_b64(v[r][k][e], m);
+            // the sum of the cross-entropy and of the log-softmax feeds an fp32
+            // result (the loss, the log-sum-exp): the accurate exponential; the
+            // softmax's 16-bit outputs (rows with |m| >= 2^15) need only this one
+            const float te = EPI == kEpiSoftmax ? exp_hw_b64(v[r][k][e], m) : exp_acc_b64(v[r][k][e], m);
             if constexpr (EPI != kEpiLogSoftmax) v[r][k][e] = te;
             s += te;
           }
@@ -206,7 +209,7 @@ __global__ __launch_bounds__(kThreads) void k_wave(RowArgs a, int64_t rbase, int
       total = wave_sum(s);
       if constexpr (EPI == kEpiXent) {
         others = total;
-        total = others + exp_hw_b64(xt, m);
+        total = others + exp_acc_b64(xt, m);
       }
     }
 

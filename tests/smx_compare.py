@@ -237,9 +237,12 @@ def check_bwd(dx_raw, dtype, ref, p_f64, g_f64, what=""):
 # Cross-entropy with logits (loss_r = LSE - x_t, dx = p - onehot(t))
 # ---------------------------------------------------------------------------
 #
-# loss (fp32): |loss - r| <= 1e-6 * max(|r|, a), with a = 0 when the target
-#   holds the row maximum (the log1p form keeps full relative precision) and
-#   a = 1 otherwise (the fp32 resolution of m - x_t + log l);
+# loss (fp32): |loss - r| <= 1e-6 * max(|r|, a, 2^-126), with a = 0 when the
+#   target holds the row maximum (the log1p form keeps full relative
+#   precision) and a = 1 otherwise (the fp32 resolution of m - x_t + log l);
+#   the 2^-126 floor is the fp32 output's, as for dx: a loss below the
+#   smallest normal fp32 number is held to about 8 subnormal steps, and one
+#   below the smallest subnormal rounds to 0, which is then its value;
 # dx: the softmax bars (f32 relative 1e-6 with the 2^-126 floor, f16/bf16
 #   1 ulp), the target lane included (its value -(others / l) is accurate);
 # policy: ignored rows loss 0 and dx +0.0; poisoned rows NaN; an empty row or
@@ -267,7 +270,7 @@ def check_xent(loss_got, dx_raw, dtype, loss_ref, dx_ref, x_float, target, what=
         rowmax = np.nanmax(np.where(np.isfinite(x_float[rows_i]), x_float[rows_i], -np.inf), axis=1)
         a = np.where(xt == rowmax, 0.0, 1.0)
         err = np.abs(loss_got[rows_i].astype(np.float64) - lr[rows_i])
-        bound = XENT_TOL * np.maximum(np.abs(lr[rows_i]), a)
+        bound = XENT_TOL * np.maximum(np.maximum(np.abs(lr[rows_i]), a), FLT_MIN)
         bad = err > bound
         if bad.any():
             i = rows_i[np.argmax(bad)]

@@ -944,6 +944,30 @@ def test_log_softmax_causal_scores():
     assert (y[empty] == 0xFF80).all() and (lse[empty] == -np.inf).all()
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_log_softmax_lse_precision_16bit(dtype):
+    """A row of one maximum and 1000 equal lanes a little below it, shifted so
+    that the log-sum-exp is near 0 (where its bar, 1e-6 absolute, is
+    tightest): every lane's exponential then carries the same rounding, so
+    nothing averages out, and an exponential good only to 16-bit precision
+    (2.6e-6) misses the fp32 log-sum-exp by 1.3e-6. The difference chosen is
+    one whose exponent argument, biased by 64, rounds furthest. Every path,
+    the rows repeated with more columns."""
+    x0, x1 = (-6.125, -6.9375) if dtype == "bf16" else (-6.671875, -6.91015625)
+    for cols in (1001, 4096, 40000):
+        rows = 4
+        a = np.full((rows, cols), -np.inf)
+        a[:, :1001] = x1
+        a[:, 0] = x0
+        a[1] = np.roll(a[1], 500)  # the maximum elsewhere in the row
+        x = W.to_format(a, dtype)
+        for path in _paths(dtype, cols, False):
+            what = f"lse precision {dtype} cols={cols} {path}"
+            banner(what)
+            y, lse = run_log(x, dtype, None, path=path, chunk_cols=300 if path == "split" else 0)
+            check_log_full(x, dtype, None, y, lse, what)
+
+
 @pytest.mark.parametrize("dtype", W.DTYPES)
 def test_log_softmax_odd_shapes_and_policy(dtype):
     rng = np.random.default_rng(200)
@@ -1119,6 +1143,54 @@ def test_cross_entropy_confident_and_policy(dtype):
                 loss, dx = run_xent(x, dtype, t, mask, path=path, chunk_cols=300 if path == "split" else 0,
                                     misalign=misalign)
                 check_xent_full(x, dtype, t, mask, loss, dx, what)
+
+
+@pytest.mark.parametrize("dtype", W.DTYPES)
+def test_cross_entropy_ignored_rows_holding_inf_or_nan(dtype):
+    """An ignored row (target outside [0, cols)) has loss 0 and gradient +0.0
+    even when a valid lane holds +inf or NaN: the ignore wins over the
+    poison. Rows of every length class (wave, LDS, LDS-resident, split),
+    aligned and not, next to a poisoned row that is not ignored."""
+    rng = np.random.default_rng(303)
+    inf = W.POS_INF[dtype].view(np.uint32) if dtype == "f32" else W.POS_INF[dtype]
+    for cols in (7, 1000, 4096, 20000, 40000):
+        rows = 6
+        x = W.random_rows(rows, cols, dtype, seed=cols + 1, scale=4.0)
+        t = rng.integers(0, cols, rows).astype(np.int32)
+        W.set_bits(x, 0, cols // 2, dtype, inf)
+        t[0] = -1  # ignored, +inf in a valid lane
+        W.set_bits(x, 1, cols - 1, dtype, W.QNAN[dtype])
+        t[1] = cols  # ignored, NaN in a valid lane
+        W.set_bits(x, 2, 0, dtype, inf)  # poisoned, not ignored
+        for misalign in (False, True):
+            for path in _paths(dtype, cols, misalign):
+                what = f"xent ignored+poisoned {dtype} cols={cols} {path} misalign={misalign}"
+                banner(what)
+                loss, dx = run_xent(x, dtype, t, None, path=path, chunk_cols=300 if path == "split" else 0,
+                                    misalign=misalign)
+                check_xent_full(x, dtype, t, None, loss, dx, what)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_cross_entropy_loss_precision_16bit(dtype):
+    """16-bit logits whose target is the row's maximum: the loss is then
+    log1p of the other lanes' share, held to 1e-6 relative (the fp32 loss's
+    own bar, with no absolute floor), so the exponentials that sum those
+    lanes must carry fp32 precision even though the inputs and the gradient
+    are 16-bit. Short rows at large and small logit scales (where a few
+    lanes a few units below the maximum make the whole loss) and longer ones,
+    on every path that holds them."""
+    rng = np.random.default_rng(304)
+    cases = [(2, 4.0), (5, 0.5), (17, 4.0), (17, 30.0), (64, 8.0), (1000, 4.0), (20000, 4.0)]
+    for cols, scale in cases:
+        rows = 2048 if cols <= 64 else 64
+        x = W.random_rows(rows, cols, dtype, seed=int(rng.integers(1 << 30)), scale=scale)
+        t = np.argmax(W.to_float(x, dtype), axis=1).astype(np.int32)
+        for path in _paths(dtype, cols, False):
+            what = f"xent 16-bit loss {dtype} cols={cols} scale={scale} {path}"
+            banner(what)
+            loss, dx = run_xent(x, dtype, t, None, path=path, chunk_cols=300 if path == "split" else 0)
+            check_xent_full(x, dtype, t, None, loss, dx, what)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
