@@ -193,14 +193,18 @@ __global__ __launch_bounds__(NT) void k_lds(RowArgs a, int64_t row0) {
 #pragma unroll
         for (int e = 0; e < E; ++e) {
           // the sum of the cross-entropy and of the log-softmax feeds an fp32
-          // result (the loss, the log-sum-exp): the accurate exponential; the
-          // softmax's 16-bit outputs (rows with |m| >= 2^15) need only this one
-          const float te = EPI == kEpiSoftmax ? exp_hw_b64(v[k][e], mx) : exp_acc_b64(v[k][e], mx);
+          // result (the loss, the log-sum-exp): the accurate exponential, unscaled
+          // where it feeds the sum alone (log-softmax; the total is scaled after);
+          // the softmax's 16-bit outputs (rows with |m| >= 2^15) need only the first
+          const float te = EPI == kEpiSoftmax      ? exp_hw_b64(v[k][e], mx)
+                           : EPI == kEpiLogSoftmax ? exp_acc_sum(v[k][e], (double)mx)
+                                                   : exp_acc_b64(v[k][e], mx);
           if constexpr (EPI != kEpiLogSoftmax) v[k][e] = te;
           s += te;
         }
     }
     total = block_sum<NW>(s, red);
+    if constexpr (EPI == kEpiLogSoftmax) total *= 18446744073709551616.0f;  // into the 2^64 scale (exact)
     if constexpr (EPI == kEpiXent) {
       others = total;
       total = others + exp_acc_b64(xt, mx);

@@ -310,8 +310,11 @@ __global__ __launch_bounds__(NW * 64) void k_lds_res(RowArgs a) {
     // kept against its own reference: fp32 its maximum (compensated
     // exponentials, a Kahan sum); 16-bit softmax the folded constant
     // c_l = 64 - m_l log2 e, so its terms are exp2(x log2 e + c_l); 16-bit
-    // log-softmax and cross-entropy exp(x - m_l) 2^64. The maximum propagates
-    // NaN, so its reduction also gives the row's policy.
+    // log-softmax and cross-entropy exp(x - m_l) unscaled, with x - m_l in
+    // fp64 (their loss and log-sum-exp are fp32 results; the normalize pass
+    // takes its own exponentials, so these serve the sum alone), scaled by
+    // 2^64 when the lanes merge. The maximum propagates NaN, so its
+    // reduction also gives the row's policy.
     constexpr bool FOLD = !ACC && EPI == kEpiSoftmax;
     float m_l = -kInf, c_l = 0.0f, l_l = 0.0f;
     KahanSum ks;
@@ -337,12 +340,10 @@ __global__ __launch_bounds__(NW * 64) void k_lds_res(RowArgs a) {
       const float mref = m_l == -kInf ? 0.0f : m_l;  // an all-masked lane adds exact zeros
 #pragma unroll
       for (int q = 0; q < E; ++q) {
-        if constexpr (ACC) {
-          e[q] = exp_acc_sum(v[q], mref);
-        } else if constexpr (FOLD) {
+        if constexpr (FOLD) {
           e[q] = exp_hw_bias(v[q], c_l);
         } else {
-          e[q] = exp_acc_b64(v[q], mref);  // the loss or the log-sum-exp: an fp32 result
+          e[q] = exp_acc_sum(v[q], (double)mref);
         }
       }
       if constexpr (ACC) {
@@ -392,11 +393,12 @@ __global__ __launch_bounds__(NW * 64) void k_lds_res(RowArgs a) {
     float total = 0.0f, others = 0.0f;
     if (!fill) {
       if constexpr (ACC) {
-        const float f = exp_diff(m_l, mx);
+        // the factor in the 2^64 scale: a lane far below the maximum keeps
+        // its relative precision, which the cross-entropy's loss of a
+        // confident row is made of
+        const float f = exp_diff_b64(m_l, mx);
         float hi = ks.hi() * f, lo = ks.lo() * f;
         res_pair(hi, lo, red);
-        hi *= 18446744073709551616.0f;  // * 2^64 (exact)
-        lo *= 18446744073709551616.0f;
         if constexpr (EPI == kEpiXent) {
           others = hi + lo;
           pair_add(hi, lo, exp_acc_b64(xt, mx), 0.0f);
@@ -419,7 +421,7 @@ __global__ __launch_bounds__(NW * 64) void k_lds_res(RowArgs a) {
         if constexpr (FOLD) {
           f = m_l == mx ? 1.0f : (m_l == -kInf ? 0.0f : __builtin_amdgcn_exp2f(c_row - c_l));
         } else {
-          f = m_l == mx ? 1.0f : (m_l == -kInf ? 0.0f : exp_diff(m_l, mx));
+          f = exp_diff_b64(m_l, mx);  // the unscaled lane sum into the 2^64 scale, as above
         }
         total = res_sum(l_l * f, red);
         if constexpr (EPI == kEpiXent) {

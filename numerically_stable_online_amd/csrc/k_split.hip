@@ -233,14 +233,20 @@ __global__ __launch_bounds__(kThreads) void k_merge_normalize(RowArgs a, int64_t
       }
       continue;
     }
-    // cross-entropy: the summaries leave out the target lane; fold it back in
-    float others = 0.0f, xt = -kInf;
+    // cross-entropy: the summaries leave out the target lane; fold it back
+    // in, in the 2^64 scale (o64, l64), so that the others keep their
+    // relative precision when they lie far below the target (the loss of a
+    // confident row is made of them); others and l are the same unscaled,
+    // each rounded once
+    float others = 0.0f, xt = -kInf, o64 = 0.0f, l64 = 1.0f;
     if constexpr (EPI == kEpiXent) {
       if (!poisoned) {
         xt = xt_in;
         const float mm = fmaxf(m, xt);
-        others = l * exp_diff(m, mm);
-        l = others + exp_diff(xt, mm);
+        o64 = l * exp_diff_b64(m, mm);
+        l64 = o64 + exp_diff_b64(xt, mm);
+        others = o64 * 5.42101086242752217e-20f;  // * 2^-64
+        l = l64 * 5.42101086242752217e-20f;       // >= 1: exact
         m = mm;
       }
       if (c == 0 && tid == 0) {
@@ -268,7 +274,7 @@ __global__ __launch_bounds__(kThreads) void k_merge_normalize(RowArgs a, int64_t
     // softmax / cross-entropy: the reciprocal 2^-64 / L; log-softmax: M + log L as hi + lo
     const float inv = EPI != kEpiLogSoftmax ? 1.0f / (l * 18446744073709551616.0f) : 0.0f;
     const Lse lse = EPI != kEpiLogSoftmax ? Lse{0.0f, 0.0f} : make_lse(m, l);
-    const float at_t = (0.0f - others) / l;  // cross-entropy target lane: -(others / L)
+    const float at_t = (0.0f - o64) / l64;  // cross-entropy target lane: -(others / L)
 
     for (int64_t base = j_lo; base < j_hi; base += kRound) {
       // cross-entropy: the target's place in this round's registers (-1: not

@@ -199,14 +199,18 @@ __global__ __launch_bounds__(kThreads) void k_wave(RowArgs a, int64_t rbase, int
 #pragma unroll
           for (int e = 0; e < E; ++e) {
             // the sum of the cross-entropy and of the log-softmax feeds an fp32
-            // result (the loss, the log-sum-exp): the accurate exponential; the
-            // softmax's 16-bit outputs (rows with |m| >= 2^15) need only this one
-            const float te = EPI == kEpiSoftmax ? exp_hw_b64(v[r][k][e], m) : exp_acc_b64(v[r][k][e], m);
+            // result (the loss, the log-sum-exp): the accurate exponential, unscaled
+            // where it feeds the sum alone (log-softmax; the total is scaled after);
+            // the softmax's 16-bit outputs (rows with |m| >= 2^15) need only the first
+            const float te = EPI == kEpiSoftmax      ? exp_hw_b64(v[r][k][e], m)
+                             : EPI == kEpiLogSoftmax ? exp_acc_sum(v[r][k][e], (double)m)
+                                                     : exp_acc_b64(v[r][k][e], m);
             if constexpr (EPI != kEpiLogSoftmax) v[r][k][e] = te;
             s += te;
           }
       }
       total = wave_sum(s);
+      if constexpr (EPI == kEpiLogSoftmax) total *= 18446744073709551616.0f;  // into the 2^64 scale (exact)
       if constexpr (EPI == kEpiXent) {
         others = total;
         total = others + exp_acc_b64(xt, m);

@@ -90,6 +90,19 @@ SMX_HD float exp_diff(float a, float b) {
   return exp_biased64(hi, lo) * 5.42101086242752217e-20f;  // * 2^-64
 }
 
+// The same factor in the 2^64 scale: exp(a - b) 2^64 for a <= b, exactly
+// 2^64 when a == b and 0 below a - b = -120. A merge that multiplies a sum
+// by it keeps the sum's relative precision down to a - b = -120, where the
+// unscaled factor is subnormal below -87 and carries only the subnormal
+// spacing's absolute precision; the loss of a confident cross-entropy row
+// is made of exactly such far-below terms.
+SMX_HD float exp_diff_b64(float a, float b) {
+  if (a == b) return 18446744073709551616.0f;
+  float hi, lo;
+  two_diff(a, b, hi, lo);
+  return exp_biased64(hi, lo);  // 0 below -120, for -inf and for NaN
+}
+
 // exp(x - m) for fp32 x <= m, with the difference taken in fp64, where it is
 // exact (two fp32 values need at most 53 bits unless m is tiny and x far
 // below it, and then it is rounded to 2^-53 relative, far below what the

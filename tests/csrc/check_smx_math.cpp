@@ -51,9 +51,34 @@ int main(int argc, char** argv) {
     double u = ulp_err(smx::exp_biased64(hi, lo), ref);
     if (u > worst2) worst2 = u;
   }
-  // factor of a merge
+  // factor of a merge, unscaled and in the 2^64 scale
+  const float two64 = 18446744073709551616.0f;
   int bad_identity = (smx::exp_diff(-INFINITY, -INFINITY) != 1.0f) + (smx::exp_diff(3.0f, 3.0f) != 1.0f) +
-                     (smx::exp_diff(-INFINITY, 2.0f) != 0.0f);
+                     (smx::exp_diff(-INFINITY, 2.0f) != 0.0f) +
+                     (smx::exp_diff_b64(-INFINITY, -INFINITY) != two64) +
+                     (smx::exp_diff_b64(3e38f, 3e38f) != two64) + (smx::exp_diff_b64(-INFINITY, 2.0f) != 0.0f) +
+                     (smx::exp_diff_b64(-121.0f, 0.0f) != 0.0f) + (smx::exp_diff_b64(NAN, 0.0f) != 0.0f);
+  // the scaled factor over pairs (a, b) of every magnitude whose difference
+  // lies in [-120, 0], most of them below -87 (where the unscaled one is
+  // subnormal): within an ulp of exp(a - b) 2^64, and equal to 2^64 times
+  // the unscaled one wherever that is a normal number
+  double worst_b64 = 0.0;
+  int bad_scale = 0;
+  for (int i = 0; i < 1000000; ++i) {
+    s = s * 1103515245u + 12345u;
+    const int ex = (int)((s >> 8) % 40) - 10;
+    s = s * 1103515245u + 12345u;
+    float b = std::ldexp((float)((s >> 8) & 0xFFFFFF) / 16777216.0f + 0.5f, ex);
+    if (s & 1) b = -b;
+    s = s * 1103515245u + 12345u;
+    float a = b - (float)((s >> 8) % 1000000) * 1.2e-4f;
+    const double d = (double)a - (double)b;  // exact for these magnitudes
+    if (!(d >= -120.0) || !(a <= b)) continue;
+    const float got = smx::exp_diff_b64(a, b);
+    worst_b64 = std::fmax(worst_b64, ulp_err(got, std::ldexp(std::exp(d), 64)));
+    const float un = smx::exp_diff(a, b);
+    if (un >= 1.1754943508222875e-38f && (double)un != std::ldexp((double)got, -64)) ++bad_scale;
+  }
   // bf16 rounding against a brute-force reference on a few patterns
   int bad_bf16 = 0;
   for (uint32_t u = 0; u < 0x7F800000u; u += 4093u) {
@@ -115,7 +140,7 @@ int main(int argc, char** argv) {
   }
   bad_dd += smx::exp_dd_sum(big - 512.0f, (double)big, Exp2Ref{}) != 0.0f;
   std::printf("n=%ld max_ulp=%.4f at d=%.9g max_ulp_pair=%.4f bad_identity=%d bad_bf16=%d max_ulp_dd=%.4f "
-              "max_ulp_dd_sum=%.4f bad_dd=%d\n",
-              n, worst, worst_d, worst2, bad_identity, bad_bf16, worst_dd, worst_dd_sum, bad_dd);
+              "max_ulp_dd_sum=%.4f bad_dd=%d max_ulp_diff_b64=%.4f bad_scale=%d\n",
+              n, worst, worst_d, worst2, bad_identity, bad_bf16, worst_dd, worst_dd_sum, bad_dd, worst_b64, bad_scale);
   return 0;
 }

@@ -253,6 +253,9 @@ def test_kernel_arithmetic_on_host(tmp_path):
     # hardware exponential's 0.79 ulp makes the bound about 1.3 on the GPU
     assert float(vals["max_ulp_dd"]) < 1.01 and float(vals["max_ulp_dd_sum"]) < 1.01, out
     assert vals["bad_dd"] == "0", out
+    # the merge factor in the 2^64 scale: as exact as the exponential it
+    # wraps, also where the unscaled factor would be subnormal
+    assert float(vals["max_ulp_diff_b64"]) < 1.0 and vals["bad_scale"] == "0", out
 
 
 def test_m0_feeds_only_its_direct_loads(tmp_path):

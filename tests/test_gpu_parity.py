@@ -1194,6 +1194,32 @@ def test_cross_entropy_loss_precision_16bit(dtype):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_cross_entropy_confident_rows_far_below(dtype):
+    """Rows whose target holds the maximum (0) and whose other logits all lie
+    95 to 115 below it (every other row: all exactly 100 below): the loss,
+    log1p of the others' share, is made of terms whose unscaled merge factors
+    e^(m - x_t) are subnormal fp32 numbers. A merge that applies such a
+    factor before the 2^64 scale keeps only the subnormal spacing's absolute
+    precision (a subnormal factor times a long row's sum, or one subnormal
+    rounding per lane, all in one direction on equal lanes). The loss must
+    still meet its 1e-6 bar (with the 2^-126 floor of the fp32 output), at
+    widths that reach the wave, LDS, LDS-resident and split kernels."""
+    rng = np.random.default_rng(317)
+    for cols in (1000, 4096, 16384, 40000, 262144):
+        rows = max(2, min(64, (1 << 22) // cols))
+        vals = rng.uniform(-115.0, -95.0, size=(rows, cols))
+        vals[::2] = -100.0
+        t = rng.integers(0, cols, rows).astype(np.int32)
+        vals[np.arange(rows), t] = 0.0
+        x = oracle.encode(vals, dtype)
+        for path in _paths(dtype, cols, False):
+            what = f"xent confident far-below {dtype} cols={cols} {path}"
+            banner(what)
+            loss, dx = run_xent(x, dtype, t, None, path=path)
+            check_xent_full(x, dtype, t, None, loss, dx, what)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_cross_entropy_split_chunks_narrower_than_a_round(dtype):
     """Split path with chunks far narrower than one register round of the
     normalize pass: each target's gradient is written by the workgroup of
