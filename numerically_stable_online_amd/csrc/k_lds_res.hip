@@ -305,39 +305,46 @@ __global__ __launch_bounds__(NW * 64) void k_lds_res(RowArgs a) {
     // pass 1: each lane's running maximum and sum of exponentials over its
     // packs, as the packs land (two at a time, each pair waited for): the
     // online recurrence of "Online stable softmax" ("Derive the update for
-    // two blocks"), per lane. When a pack raises the lane's maximum, the
-    // lane's sum first takes the factor exp(m_old - m_new). The lane's sum is
-    // kept against its own reference: fp32 its maximum (compensated
-    // exponentials, a Kahan sum); 16-bit softmax the folded constant
-    // c_l = 64 - m_l log2 e, so its terms are exp2(x log2 e + c_l); 16-bit
-    // log-softmax and cross-entropy exp(x - m_l) unscaled, with x - m_l in
-    // fp64 (their loss and log-sum-exp are fp32 results; the normalize pass
-    // takes its own exponentials, so these serve the sum alone), scaled by
-    // 2^64 when the lanes merge. The maximum propagates NaN, so its
-    // reduction also gives the row's policy.
+    // two blocks"), per lane. When the lane's reference moves up, the lane's
+    // sum first takes the factor exp(ref_old - ref_new). The lane's sum is
+    // kept against its own reference: 16-bit softmax the folded constant
+    // c_l = 64 - m_l log2 e, so its terms are exp2(x log2 e + c_l); fp32
+    // (compensated exponentials, a Kahan sum) and 16-bit log-softmax and
+    // cross-entropy a reference r_l that moves only when the lane maximum
+    // passes it by more than kRefSlack, so terms exp(x - r_l) stay below
+    // e^16 and the accurate rescale factor (about 25 instructions, paid by
+    // the whole wave whenever any lane takes it) is taken a few times per
+    // row instead of on nearly every pack. Those terms are unscaled, with
+    // x - r_l in fp64 (the loss and log-sum-exp are fp32 results; the
+    // normalize pass takes its own exponentials, so these serve the sum
+    // alone), and enter the 2^64 scale when the lanes merge. The maximum
+    // propagates NaN, so its reduction also gives the row's policy.
     constexpr bool FOLD = !ACC && EPI == kEpiSoftmax;
-    float m_l = -kInf, c_l = 0.0f, l_l = 0.0f;
+    constexpr float kRefSlack = 8.0f;
+    float m_l = -kInf, r_l = -kInf, c_l = 0.0f, l_l = 0.0f;
     KahanSum ks;
     float xt_own = -kInf;
     auto fold_pack = [&](const float (&v)[E]) {
       const float mn = vmax(m_l, tree_max<E>(v));
-      if (mn != m_l) {  // a new lane maximum (or NaN, whose row is poisoned)
-        if constexpr (ACC) {
-          const float f = exp_diff(m_l, mn);  // 0 when m_l is -inf
-          ks.s *= f;
-          ks.c *= f;
-        } else if constexpr (FOLD) {
+      if constexpr (FOLD) {
+        if (mn != m_l) {  // a new lane maximum (or NaN, whose row is poisoned)
           const float cn = row_exp_bias(mn);
           l_l = m_l == -kInf ? 0.0f : l_l * __builtin_amdgcn_exp2f(cn - c_l);
           c_l = cn;
-        } else {
-          // (the cross-entropy's fp32 loss takes the accurate factor)
-          l_l = m_l == -kInf ? 0.0f : l_l * exp_diff(m_l, mn);
         }
-        m_l = mn;
+      } else if (!(mn <= r_l + kRefSlack)) {  // also taken for NaN
+        const float f = exp_diff(r_l, mn);    // 0 when r_l is -inf
+        if constexpr (ACC) {
+          ks.s *= f;
+          ks.c *= f;
+        } else {
+          l_l = r_l == -kInf ? 0.0f : l_l * f;
+        }
+        r_l = mn;
       }
+      m_l = mn;
       float e[E];
-      const float mref = m_l == -kInf ? 0.0f : m_l;  // an all-masked lane adds exact zeros
+      const float mref = r_l == -kInf ? 0.0f : r_l;  // an all-masked lane adds exact zeros
 #pragma unroll
       for (int q = 0; q < E; ++q) {
         if constexpr (FOLD) {
@@ -396,7 +403,7 @@ __global__ __launch_bounds__(NW * 64) void k_lds_res(RowArgs a) {
         // the factor in the 2^64 scale: a lane far below the maximum keeps
         // its relative precision, which the cross-entropy's loss of a
         // confident row is made of
-        const float f = exp_diff_b64(m_l, mx);
+        const float f = exp_diff_b64(r_l, mx);
         float hi = ks.hi() * f, lo = ks.lo() * f;
         res_pair(hi, lo, red);
         if constexpr (EPI == kEpiXent) {
@@ -421,7 +428,7 @@ __global__ __launch_bounds__(NW * 64) void k_lds_res(RowArgs a) {
         if constexpr (FOLD) {
           f = m_l == mx ? 1.0f : (m_l == -kInf ? 0.0f : __builtin_amdgcn_exp2f(c_row - c_l));
         } else {
-          f = exp_diff_b64(m_l, mx);  // the unscaled lane sum into the 2^64 scale, as above
+          f = exp_diff_b64(r_l, mx);  // the unscaled lane sum into the 2^64 scale, as above
         }
         total = res_sum(l_l * f, red);
         if constexpr (EPI == kEpiXent) {
