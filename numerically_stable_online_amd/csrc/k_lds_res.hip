@@ -317,7 +317,8 @@ __global__ __launch_bounds__(NW * 64) void k_lds_res(RowArgs a) {
     // row instead of on nearly every pack. Those terms are unscaled, with
     // x - r_l in fp64 (the loss and log-sum-exp are fp32 results; the
     // normalize pass takes its own exponentials, so these serve the sum
-    // alone), and enter the 2^64 scale when the lanes merge. The maximum
+    // alone), and enter the 2^64 scale when the lanes merge (after one last
+    // rescale to the lane's own maximum). The maximum
     // propagates NaN, so its reduction also gives the row's policy.
     constexpr bool FOLD = !ACC && EPI == kEpiSoftmax;
     constexpr float kRefSlack = 8.0f;
@@ -378,6 +379,19 @@ __global__ __launch_bounds__(NW * 64) void k_lds_res(RowArgs a) {
         fold_pack(va);
       }
     }
+    // each lane's sum brought to its own maximum (its reference lies at most
+    // 16 below it), once per row: the merge factor below then drops only
+    // lanes more than 120 below the row maximum, whose terms no fp32 result
+    // can hold, and not lanes whose reference alone lies that far below
+    if constexpr (!FOLD) {
+      const float g = exp_diff(r_l, m_l);  // 1 when equal (also -inf, -inf)
+      if constexpr (ACC) {
+        ks.s *= g;
+        ks.c *= g;
+      } else {
+        l_l *= g;
+      }
+    }
     // the row's reduction scratch: two copies, alternating from row to row
     ResScratch<NW>& red = red2[par];
     if (EPI == kEpiXent && tk >= 0) red.xt = xt_own;
@@ -403,7 +417,7 @@ __global__ __launch_bounds__(NW * 64) void k_lds_res(RowArgs a) {
         // the factor in the 2^64 scale: a lane far below the maximum keeps
         // its relative precision, which the cross-entropy's loss of a
         // confident row is made of
-        const float f = exp_diff_b64(r_l, mx);
+        const float f = exp_diff_b64(m_l, mx);
         float hi = ks.hi() * f, lo = ks.lo() * f;
         res_pair(hi, lo, red);
         if constexpr (EPI == kEpiXent) {
@@ -428,7 +442,7 @@ __global__ __launch_bounds__(NW * 64) void k_lds_res(RowArgs a) {
         if constexpr (FOLD) {
           f = m_l == mx ? 1.0f : (m_l == -kInf ? 0.0f : __builtin_amdgcn_exp2f(c_row - c_l));
         } else {
-          f = exp_diff_b64(r_l, mx);  // the unscaled lane sum into the 2^64 scale, as above
+          f = exp_diff_b64(m_l, mx);  // the unscaled lane sum into the 2^64 scale, as above
         }
         total = res_sum(l_l * f, red);
         if constexpr (EPI == kEpiXent) {
