@@ -313,8 +313,8 @@ __global__ __launch_bounds__(NW * 64) void k_lds_res(RowArgs a) {
     // cross-entropy a reference r_l that moves only when the lane maximum
     // passes it by more than kRefSlack, so terms exp(x - r_l) stay below
     // e^16 and the accurate rescale factor (about 25 instructions, paid by
-    // the whole wave whenever any lane takes it) is taken a few times per
-    // row instead of on nearly every pack. Those terms are unscaled, with
+    // the whole wave whenever any lane takes it) is taken less often than
+    // the maximum rises. Those terms are unscaled, with
     // x - r_l in fp64 (the loss and log-sum-exp are fp32 results; the
     // normalize pass takes its own exponentials, so these serve the sum
     // alone), and enter the 2^64 scale when the lanes merge (after one last
