@@ -1219,6 +1219,31 @@ def test_cross_entropy_confident_rows_far_below(dtype):
             check_xent_full(x, dtype, t, None, loss, dx, what)
 
 
+def test_cross_entropy_lane_reference_below_the_cutoff():
+    """LDS-resident rows keep each lane's sum against a reference that moves
+    only when the lane maximum passes it by more than 8, and bring the sum to
+    the lane's maximum once per row before the merge, whose factor drops
+    lanes more than 120 below the row maximum. Here every lane's first packs
+    lie at -120.0625 (below that cutoff) and its later ones at -112.0625
+    (within 8 of the first, so the reference never moves), with the target
+    at the row maximum 0: the loss, about 1.5e-44, is made of the later
+    packs and exceeds its absolute floor (1e-6 of 2^-126), so a merge that
+    took the factor from the reference would return 0 and fail. f16 rows of
+    77,824 logits (152 KiB, the LDS-resident kernel's largest)."""
+    rows, cols = 8, 77824
+    vals = np.full((rows, cols), -112.0625)
+    vals[:, :8192] = -120.0625  # the first 16 KiB: every lane's first packs
+    t = np.array([0, 1, 4095, 8191, 100, 3, 7, 2], dtype=np.int32)
+    vals[np.arange(rows), t] = 0.0
+    x = oracle.encode(vals, "f16")
+    for path in ("auto", "lds"):
+        what = f"xent lane reference below the cutoff f16 {path}"
+        banner(what)
+        loss, dx = run_xent(x, "f16", t, None, path=path)
+        check_xent_full(x, "f16", t, None, loss, dx, what)
+        assert (loss > 0).all(), f"{what}: {loss}"
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_cross_entropy_split_chunks_narrower_than_a_round(dtype):
     """Split path with chunks far narrower than one register round of the
